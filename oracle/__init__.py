@@ -1,0 +1,146 @@
+"""ctypes binding of the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the library. It shares
+no code with the HIP path. See oracle.c for what is computed and which
+passages of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+WFMT = {"w4": 0, "w8": 1}
+AFMT = {"f32": 0, "bf16": 1, "i8": 2}
+SFMT = {"f32": 0, "bf16": 1}
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP over output columns)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+           "-Wall", "-Wextra", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load(path: str = _LIB):
+    global _lib
+    if path == _LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        build(out=path)
+    lib = ctypes.CDLL(path)
+    vp, i64p = ctypes.c_void_p, ctypes.c_void_p
+    c_int = ctypes.c_int
+    lib.oracle_check.argtypes = [c_int] * 8
+    lib.oracle_dequant.argtypes = [c_int] * 6 + [vp, vp, vp, i64p, c_int, vp]
+    lib.oracle_qgemm.argtypes = [c_int] * 8 + [vp] * 5 + [i64p, c_int, i64p, c_int, vp, vp]
+    lib.oracle_int_partials.argtypes = [c_int] * 6 + [vp, vp, vp, i64p, c_int, i64p, c_int, vp]
+    lib.oracle_num_threads.argtypes = []
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _idx(a):
+    if a is None:
+        return None, 0
+    a = np.ascontiguousarray(a, dtype=np.int64)
+    return a, len(a)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _weights(W, wfmt):
+    return _c(W, np.uint32 if wfmt == "w4" else np.int8)
+
+
+def _scales(S, sfmt):
+    return _c(S, np.uint16 if sfmt == "bf16" else np.float32)
+
+
+def _acts(A, afmt):
+    return _c(A, {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[afmt])
+
+
+def qgemm(M, N, K, G, wfmt, afmt, sfmt, has_zp, A, a_scale, W, S, Z, rows=None, cols=None, lib=None):
+    """Returns (ref, bound) as float64 arrays [len(rows), len(cols)]."""
+    lib = lib or load()
+    A, W, S = _acts(A, afmt), _weights(W, wfmt), _scales(S, sfmt)
+    a_scale, Z = _c(a_scale, np.float32), _c(Z, np.uint32)
+    rows, nr = _idx(rows)
+    cols, nc = _idx(cols)
+    nr = M if rows is None else nr
+    nc = N if cols is None else nc
+    ref = np.zeros((nr, nc), dtype=np.float64)
+    bound = np.zeros((nr, nc), dtype=np.float64)
+    rc = lib.oracle_qgemm(M, N, K, G, WFMT[wfmt], AFMT[afmt], SFMT[sfmt], int(bool(has_zp)),
+                          _ptr(A), _ptr(a_scale), _ptr(W), _ptr(S), _ptr(Z),
+                          _ptr(rows), nr, _ptr(cols), nc, _ptr(ref), _ptr(bound))
+    if rc != 0:
+        raise ValueError(f"oracle_qgemm rejected its arguments (rc={rc})")
+    return ref, bound
+
+
+def dequant(N, K, G, wfmt, sfmt, has_zp, W, S, Z, cols=None, lib=None):
+    """Returns w_hat float64 [K, len(cols)]."""
+    lib = lib or load()
+    W, S, Z = _weights(W, wfmt), _scales(S, sfmt), _c(Z, np.uint32)
+    cols, nc = _idx(cols)
+    nc = N if cols is None else nc
+    out = np.zeros((K, nc), dtype=np.float64)
+    rc = lib.oracle_dequant(N, K, G, WFMT[wfmt], SFMT[sfmt], int(bool(has_zp)), _ptr(W), _ptr(S),
+                            _ptr(Z), _ptr(cols), nc, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_dequant rejected its arguments (rc={rc})")
+    return out
+
+
+def int_partials(M, N, K, G, wfmt, has_zp, Aq, W, Z, rows=None, cols=None, lib=None):
+    """Returns int64 P [len(rows), K/G, len(cols)]: per-group integer dots."""
+    lib = lib or load()
+    Aq, W, Z = _c(Aq, np.int8), _weights(W, wfmt), _c(Z, np.uint32)
+    rows, nr = _idx(rows)
+    cols, nc = _idx(cols)
+    nr = M if rows is None else nr
+    nc = N if cols is None else nc
+    P = np.zeros((nr, K // G, nc), dtype=np.int64)
+    rc = lib.oracle_int_partials(M, N, K, G, WFMT[wfmt], int(bool(has_zp)), _ptr(Aq), _ptr(W),
+                                 _ptr(Z), _ptr(rows), nr, _ptr(cols), nc, _ptr(P))
+    if rc != 0:
+        raise ValueError(f"oracle_int_partials rejected its arguments (rc={rc})")
+    return P
+
+
+def for_problem(p, rows=None, cols=None, lib=None):
+    """Oracle (ref, bound) of a workloads.Problem."""
+    return qgemm(p.M, p.N, p.K, p.G, p.wfmt, p.afmt, p.sfmt, p.has_zp, p.A, p.a_scale, p.W, p.S,
+                 p.Z, rows=rows, cols=cols, lib=lib)
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())
+
+
+def gate(out, ref, bound, rel=2e-3, atol=1e-5):
+    """Per-element parity gate: |out - ref| <= rel * bound + atol. Returns (ok, worst_ratio)."""
+    err = np.abs(np.asarray(out, dtype=np.float64) - ref)
+    lim = rel * bound + atol
+    ratio = float(np.max(err / lim)) if err.size else 0.0
+    return bool(np.all(err <= lim)), ratio

@@ -1,0 +1,296 @@
+"""Pin checks of the fp64 CPU oracle against facts fixed outside the oracle.
+
+Each ``check_*`` takes a loaded oracle library and raises AssertionError on a
+mismatch. ``test_oracle_pins.py`` runs them against the real oracle and
+``test_oracle_mutants.py`` runs them against copies of the oracle with planted
+mistakes, which every mutant must fail.
+
+* hand-computed tiny cases (tests/golden/hand_cases.json, each cited);
+* exact rational brute force on 4x8x64 inputs, written in the blockwise form
+  out = sum_g s_g * sum_{k in g} a_k * (q_k - z_g) with its own bit decoding
+  (hex digits for nibbles, struct for float patterns);
+* the integer identity (unit scales, zero-point 8, integer activations: the
+  result is the integer matmul of (q - 8), computed by numpy);
+* special cases: one-hot activations, q == z, scale doubling, zero-points all
+  8 versus the symmetric path, int8 x int8 per-group integer partials.
+
+None of these re-types the oracle's formula: the decodes take other routes
+(byte views, hex strings) and the reductions use exact rationals or numpy
+integer matmuls.
+"""
+import json
+import os
+import struct
+from fractions import Fraction
+from types import SimpleNamespace
+
+import numpy as np
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+with open(GOLDEN) as _f:
+    HAND = json.load(_f)["cases"]
+
+
+# --------------------------------------------------------------------------
+# independent decoders (not the oracle's shift-and-mask route)
+# --------------------------------------------------------------------------
+def nibbles_of_word_hex(word: int):
+    """Codes of one canonical int4 word via its hex digits: the last hex digit
+    is bits 0..3, i.e. element 0."""
+    s = format(int(word), "08x")
+    return [int(ch, 16) for ch in reversed(s)]
+
+
+def w4_codes_bytes(W: np.ndarray) -> np.ndarray:
+    """uint32 [K/8, N] -> codes [K, N] through a little-endian byte view:
+    byte b of a word holds elements 2b (low nibble) and 2b+1 (high nibble)."""
+    R, N = W.shape
+    by = np.ascontiguousarray(W.astype("<u4")).view(np.uint8).reshape(R, N, 4)
+    out = np.zeros((R, 8, N), dtype=np.int64)
+    for b in range(4):
+        out[:, 2 * b, :] = by[:, :, b] % 16
+        out[:, 2 * b + 1, :] = by[:, :, b] // 16
+    return out.reshape(R * 8, N)
+
+
+def zeros_bytes(Z: np.ndarray, N: int) -> np.ndarray:
+    R, nw = Z.shape
+    by = np.ascontiguousarray(Z.astype("<u4")).view(np.uint8).reshape(R, nw, 4)
+    out = np.zeros((R, nw, 8), dtype=np.int64)
+    for b in range(4):
+        out[:, :, 2 * b] = by[:, :, b] % 16
+        out[:, :, 2 * b + 1] = by[:, :, b] // 16
+    return out.reshape(R, nw * 8)[:, :N]
+
+
+def frac_f32(x) -> Fraction:
+    return Fraction(struct.unpack("<f", struct.pack("<f", float(x)))[0])
+
+
+def frac_bf16(bits) -> Fraction:
+    return Fraction(struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0])
+
+
+def _arr(v, dtype):
+    def conv(x):
+        return int(x, 16) if isinstance(x, str) else x
+    return np.array([[conv(x) for x in row] for row in v], dtype=dtype)
+
+
+def load_case(c):
+    wdt = np.uint32 if c["wfmt"] == "w4" else np.int8
+    W = _arr(c["W"], np.int64).astype(wdt)
+    S = _arr(c["S"], np.uint16) if c["sfmt"] == "bf16" else _arr(c["S"], np.float32)
+    A = {"f32": lambda: _arr(c["A"], np.float32), "bf16": lambda: _arr(c["A"], np.uint16),
+         "i8": lambda: _arr(c["A"], np.int8)}[c["afmt"]]()
+    Z = _arr(c["Z"], np.int64).astype(np.uint32) if c["Z"] is not None else None
+    a_scale = _arr(c["a_scale"], np.float32) if c["a_scale"] is not None else None
+    return W, S, Z, A, a_scale
+
+
+def check_hand_case(lib, case):
+    W, S, Z, A, a_scale = load_case(case)
+    ref, bound = oracle.qgemm(case["M"], case["N"], case["K"], case["G"], case["wfmt"], case["afmt"],
+                              case["sfmt"], case["has_zp"], A, a_scale, W, S, Z, lib=lib)
+    assert np.array_equal(ref, np.array(case["expected"], dtype=np.float64)), (case["id"], ref)
+    assert np.all(bound >= np.abs(ref)), case["id"]
+    if "partials" in case:
+        P = oracle.int_partials(case["M"], case["N"], case["K"], case["G"], case["wfmt"],
+                                case["has_zp"], A, W, Z, lib=lib)
+        assert np.array_equal(P, np.array(case["partials"], dtype=np.int64)), case["id"]
+
+
+# --------------------------------------------------------------------------
+# exact rational brute force, blockwise form
+# --------------------------------------------------------------------------
+def arrays_any_format(M, N, K, G, wfmt, afmt, sfmt, has_zp, seed):
+    """Seeded inputs for any format triple (not only the ABI's precisions)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if wfmt == "w4":
+        W = wl.random_words(rng, (K // 8, N))
+    else:
+        W = rng.integers(-127, 128, size=(K, N), dtype=np.int8)
+    s = wl.log_uniform(rng, 1e-3, 1e-2, (K // G, N)).astype(np.float32)
+    S = wl.f32_to_bf16_bits(s) if sfmt == "bf16" else s
+    Z = wl.random_words(rng, (K // G, (N + 7) // 8)) if has_zp else None
+    A, a_scale = wl.make_activations(rng, M, K, G, afmt, outlier_frac=0.05)
+    return SimpleNamespace(M=M, N=N, K=K, G=G, wfmt=wfmt, afmt=afmt, sfmt=sfmt, has_zp=has_zp,
+                           W=W, S=S, Z=Z, A=A, a_scale=a_scale)
+
+
+def brute_force(p):
+    M, N, K, G = p.M, p.N, p.K, p.G
+    if p.wfmt == "w4":
+        q = [[nibbles_of_word_hex(p.W[k // 8, n])[k % 8] for n in range(N)] for k in range(K)]
+    else:
+        q = [[int(p.W[k, n]) for n in range(N)] for k in range(K)]
+    if p.wfmt == "w8":
+        z = [[0] * N for _ in range(K // G)]
+    elif p.has_zp:
+        z = [[nibbles_of_word_hex(p.Z[g, n // 8])[n % 8] for n in range(N)] for g in range(K // G)]
+    else:
+        z = [[8] * N for _ in range(K // G)]
+    fs = frac_bf16 if p.sfmt == "bf16" else frac_f32
+    s = [[fs(p.S[g, n]) for n in range(N)] for g in range(K // G)]
+    if p.afmt == "f32":
+        a = [[frac_f32(p.A[m, k]) for k in range(K)] for m in range(M)]
+    elif p.afmt == "bf16":
+        a = [[frac_bf16(p.A[m, k]) for k in range(K)] for m in range(M)]
+    else:
+        a = [[frac_f32(p.a_scale[m, k // G]) * int(p.A[m, k]) for k in range(K)] for m in range(M)]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    mag = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            tot, tmag = Fraction(0), Fraction(0)
+            for g in range(K // G):
+                blk = Fraction(0)
+                for k in range(g * G, (g + 1) * G):
+                    t = a[m][k] * (q[k][n] - z[g][n])
+                    blk += t
+                    tmag += abs(t) * abs(s[g][n])
+                tot += s[g][n] * blk
+            out[m][n], mag[m][n] = tot, tmag
+    return out, mag
+
+
+COMBOS = [(w, a, s, zp) for w in ("w4", "w8") for a in ("f32", "bf16", "i8") for s in ("f32", "bf16")
+          for zp in ((False, True) if w == "w4" else (False,))]
+
+
+def check_brute_force(lib, combo, seed=None):
+    wfmt, afmt, sfmt, has_zp = combo
+    M, N, K, G = 4, 8, 64, 32
+    seed = 77 + COMBOS.index(combo) if seed is None else seed
+    p = arrays_any_format(M, N, K, G, wfmt, afmt, sfmt, has_zp, seed)
+    exact, mag = brute_force(p)
+    ref, bound = oracle.qgemm(M, N, K, G, wfmt, afmt, sfmt, has_zp, p.A, p.a_scale, p.W, p.S, p.Z,
+                              lib=lib)
+    for m in range(M):
+        for n in range(N):
+            e, b = float(exact[m][n]), float(mag[m][n])
+            assert abs(ref[m, n] - e) <= 1e-13 * b + 1e-300, (combo, m, n, ref[m, n], e)
+            assert abs(bound[m, n] - b) <= 1e-13 * b + 1e-300, (combo, m, n)
+
+
+# --------------------------------------------------------------------------
+# integer identity: unit scales, zero-point 8, integer activations
+# --------------------------------------------------------------------------
+def check_integer_identity_w4(lib, afmt="f32", sfmt="f32"):
+    M, N, K, G = 3, 64, 256, 32
+    rng = np.random.Generator(np.random.PCG64(11))
+    W = wl.random_words(rng, (K // 8, N))
+    a_int = rng.integers(-4, 5, size=(M, K)).astype(np.int64)
+    A = a_int.astype(np.float32)
+    A = wl.f32_to_bf16_bits(A) if afmt == "bf16" else A
+    S = np.ones((K // G, N), dtype=np.float32)
+    S = wl.f32_to_bf16_bits(S) if sfmt == "bf16" else S
+    ref, _ = oracle.qgemm(M, N, K, G, "w4", afmt, sfmt, False, A, None, W, S, None, lib=lib)
+    expect = a_int @ (w4_codes_bytes(W) - 8)
+    assert np.array_equal(ref, expect.astype(np.float64))
+
+
+def check_integer_identity_w8(lib):
+    M, N, K, G = 3, 40, 128, 32
+    rng = np.random.Generator(np.random.PCG64(12))
+    W = rng.integers(-127, 128, size=(K, N), dtype=np.int8)
+    a_int = rng.integers(-4, 5, size=(M, K)).astype(np.int64)
+    S = np.ones((K // G, N), dtype=np.float32)
+    ref, _ = oracle.qgemm(M, N, K, G, "w8", "f32", "f32", False, a_int.astype(np.float32), None, W, S,
+                          None, lib=lib)
+    assert np.array_equal(ref, (a_int @ W.astype(np.int64)).astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# int8 x int8 per-group integer partials (numpy integer matmul per group)
+# --------------------------------------------------------------------------
+def check_int_partials(lib, wfmt, has_zp):
+    M, N, K, G = 5, 48, 256, 32
+    prec = 4 if wfmt == "w4" else 5
+    p = wl.make_problem(M, N, K, G, prec, has_zp, seed=21)
+    P = oracle.int_partials(M, N, K, G, wfmt, has_zp, p.A, p.W, p.Z, lib=lib)
+    if wfmt == "w4":
+        q = w4_codes_bytes(p.W)
+        z = zeros_bytes(p.Z, N) if has_zp else np.full((K // G, N), 8, dtype=np.int64)
+    else:
+        q = p.W.astype(np.int64)
+        z = np.zeros((K // G, N), dtype=np.int64)
+    aq = p.A.astype(np.int64)
+    for g in range(K // G):
+        blk = aq[:, g * G:(g + 1) * G] @ (q[g * G:(g + 1) * G] - z[g][None, :])
+        assert np.array_equal(P[:, g, :], blk), g
+    # with unit scales, the fp64 result is the sum of the exact partials
+    ones = np.ones((K // G, N), dtype=np.float32)
+    a1 = np.ones((M, K // G), dtype=np.float32)
+    ref, _ = oracle.qgemm(M, N, K, G, wfmt, "i8", "f32", has_zp, p.A, a1, p.W, ones, p.Z, lib=lib)
+    assert np.array_equal(ref, P.sum(axis=1).astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# special cases
+# --------------------------------------------------------------------------
+def check_one_hot(lib, has_zp):
+    M, N, K, G = 1, 16, 256, 32
+    p = wl.make_problem(M, N, K, G, 2, has_zp, seed=31)
+    q = w4_codes_bytes(p.W)
+    z = zeros_bytes(p.Z, N) if has_zp else np.full((K // G, N), 8, dtype=np.int64)
+    for k in (0, G - 1, G, K - 1):
+        a = np.zeros((1, K), dtype=np.float32)
+        a[0, k] = 1.0
+        ref, _ = oracle.qgemm(M, N, K, G, "w4", "f32", "f32", has_zp, a, None, p.W, p.S, p.Z, lib=lib)
+        expect = p.S[k // G].astype(np.float64) * (q[k] - z[k // G])
+        assert np.array_equal(ref[0], expect), k
+    wh = oracle.dequant(N, K, G, "w4", "f32", has_zp, p.W, p.S, p.Z, lib=lib)
+    assert np.array_equal(wh, p.S.astype(np.float64).repeat(G, axis=0) * (q - z.repeat(G, axis=0)))
+
+
+def check_q_equal_z(lib):
+    M, N, K, G = 2, 16, 128, 32
+    p = wl.make_problem(M, N, K, G, 1, True, seed=41)
+    rng = np.random.Generator(np.random.PCG64(42))
+    z = rng.integers(0, 16, size=(K // G, N)).astype(np.uint8)
+    p.Z = wl.pack_zeros(z)
+    p.W = wl.pack_w4(np.repeat(z, G, axis=0))
+    ref, _ = oracle.for_problem(p, lib=lib)
+    assert np.array_equal(ref, np.zeros_like(ref))
+    p2 = wl.make_problem(M, N, K, G, 1, False, seed=43)
+    p2.W = np.full_like(p2.W, 0x88888888)
+    ref2, _ = oracle.for_problem(p2, lib=lib)
+    assert np.array_equal(ref2, np.zeros_like(ref2))
+
+
+def check_scale_doubling(lib):
+    p = wl.make_problem(3, 24, 256, 32, 2, False, seed=51)
+    ref, _ = oracle.for_problem(p, lib=lib)
+    p.S = (p.S * 2).astype(np.float32)
+    ref2, _ = oracle.for_problem(p, lib=lib)
+    assert np.array_equal(ref2, 2 * ref)
+
+
+def check_zero_points_all_eight(lib):
+    p = wl.make_problem(2, 32, 256, 128, 1, False, seed=61)
+    ref, _ = oracle.for_problem(p, lib=lib)
+    p.has_zp = True
+    p.Z = np.full((p.K // p.G, p.N // 8), 0x88888888, dtype=np.uint32)
+    ref2, _ = oracle.for_problem(p, lib=lib)
+    assert np.array_equal(ref, ref2)
+
+
+def all_checks():
+    """(name, callable(lib)) for every pin."""
+    out = [(f"hand_{c['id']}", (lambda c: lambda lib: check_hand_case(lib, c))(c)) for c in HAND]
+    out += [(f"brute_{'-'.join(map(str, c))}", (lambda c: lambda lib: check_brute_force(lib, c))(c))
+            for c in COMBOS]
+    out += [(f"identity_w4_{a}_{s}", (lambda a, s: lambda lib: check_integer_identity_w4(lib, a, s))(a, s))
+            for a in ("f32", "bf16") for s in ("f32", "bf16")]
+    out += [("identity_w8", check_integer_identity_w8)]
+    out += [(f"int_partials_{w}_{z}", (lambda w, z: lambda lib: check_int_partials(lib, w, z))(w, z))
+            for w, z in (("w4", False), ("w4", True), ("w8", False))]
+    out += [(f"one_hot_{z}", (lambda z: lambda lib: check_one_hot(lib, z))(z)) for z in (False, True)]
+    out += [("q_equal_z", check_q_equal_z), ("scale_doubling", check_scale_doubling),
+            ("zero_points_all_eight", check_zero_points_all_eight)]
+    return out

@@ -1,0 +1,68 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each mutant is a copy of oracle/oracle.c with one textual change (a plausible
+mistake: a wrong nibble order, a dropped zero-point, a transposed or reversed
+index, a sign flip, a dropped term, a wrong bf16 widening). It is compiled on
+the CPU into a temporary library and run through every pin of
+tests/oracle_pins.py; the test fails if some mutant passes all of them.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, mutated text); the original must occur exactly once.
+MUTANTS = [
+    ("nibble_order_reversed", "(word >> (4 * (k % 8)))", "(word >> (4 * (7 - k % 8)))"),
+    ("symmetric_zero_7", "return 8;", "return 7;"),
+    ("group_index_doubled", "int g = k / G;", "int g = k / (2 * G);"),
+    ("scale_column_reversed", "size_t i = (size_t)g * N + n;", "size_t i = (size_t)g * N + (N - 1 - n);"),
+    ("zero_point_dropped", "(double)(q - z)", "(double)(q)"),
+    ("zero_point_sign", "(double)(q - z)", "(double)(z - q)"),
+    ("bf16_shift", "((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
+    ("sum_sign", "sum += term;", "sum -= term;"),
+    ("bound_not_abs", "mag += fabs(term);", "mag += term;"),
+    ("zp_nibble_order", "(word >> (4 * (n % 8)))", "(word >> (4 * (7 - n % 8)))"),
+    ("a_scale_group", "a_scale[(size_t)m * (K / G) + k / G]", "a_scale[(size_t)m * (K / G)]"),
+    ("w8_column_reversed", "((const int8_t *)W)[(size_t)k * N + n]", "((const int8_t *)W)[(size_t)k * N + (N - 1 - n)]"),
+    ("w4_column_reversed", "w[(size_t)(k / 8) * N + n]", "w[(size_t)(k / 8) * N + (N - 1 - n)]"),
+    ("activation_k_reversed", "size_t i = (size_t)m * K + k;", "size_t i = (size_t)m * K + (K - 1 - k);"),
+    ("dropped_last_term", "for (int k = 0; k < K; ++k) {\n                    double term",
+     "for (int k = 0; k < K - 1; ++k) {\n                    double term"),
+    ("partials_dropped_term", "k < (g + 1) * G; ++k)", "k < (g + 1) * G - 1; ++k)"),
+    ("partials_sign", "acc += (int64_t)Aq", "acc -= (int64_t)Aq"),
+    ("zp_row_stride", "Z[(size_t)g * words_per_row + n / 8]", "Z[(size_t)g * 0 + n / 8]"),
+    ("i8_activation_unscaled", "return (double)a_scale[(size_t)m * (K / G) + k / G] * (double)",
+     "return 1.0 * (double)"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, name, orig, mut):
+    assert source.count(orig) == 1, f"mutation site for {name} must be unique"
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(source.replace(orig, mut))
+    so = str(tmp_path / f"liboracle_{name}.so")
+    subprocess.run(["gcc", "-O1", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                    str(src), "-o", so, "-lm"], check=True)
+    lib = oracle.load(so)
+    caught = []
+    for check_name, check in pins.all_checks():
+        try:
+            check(lib)
+        except (AssertionError, ValueError):
+            caught.append(check_name)
+    assert caught, f"mutant {name} passed every pin"

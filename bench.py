@@ -1,0 +1,287 @@
+"""Benchmark of the group-quantized weight-only GEMM on one MI355X.
+
+A step is one pass of the hot path (one qgemm_run) over one batch of
+synthetic input. The headline workload is the decode W4A16 g128 GEMV
+(M=1, K=4096, N=28672: the fused gate+up projection of an 8B-class layer):
+value = algorithmic bytes (packed weights + scales + activations + output)
+per second, with the inputs resident in HBM. To keep the 256 MiB Infinity
+Cache from serving the weights, consecutive steps cycle through R copies of
+the packed weights and scales whose total exceeds 640 MiB.
+
+Also reported: the MFMA path at M=1024 (TFLOP/s), the prefill crossover
+sweep against a dense bf16 torch.matmul on the same shapes, and the fp64 CPU
+oracle timed on the host cores (cpu_baseline).
+
+Timing: the K steps are captured in a HIP graph (the library's calls are
+capture-safe) and replayed; HIP events on the launch stream bracket the
+replay, with torch.cuda.synchronize() on both sides. --mode eager times a
+plain launch loop instead.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 g128 GEMV HBM GB/s at M=1; GEMM TFLOPS at M=1024; % of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 640 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Prepared:
+    """qgemm_run calls with their ctypes arguments built once (host cost per
+    launch is then the C call itself)."""
+
+    def __init__(self, qg, M, N, K, G, prec, A, Ws, Ss, Z, out, stream):
+        import torch
+        self.lib = qg.lib()
+        _, _, ws_bytes = qg.plan(M, N, K, G, prec)
+        self.ws = qg.workspace(ws_bytes, A.device)
+        vp = ctypes.c_void_p
+        self.args = []
+        for W, S in zip(Ws, Ss):
+            self.args.append((M, N, K, G, prec, int(Z is not None), vp(A.data_ptr()), None,
+                              vp(W.data_ptr()), vp(S.data_ptr()), vp(Z.data_ptr()) if Z is not None else None,
+                              vp(out.data_ptr()), vp(self.ws.data_ptr()) if self.ws is not None else None,
+                              ws_bytes, vp(stream)))
+
+    def __call__(self, i):
+        st = self.lib.qgemm_run(*self.args[i % len(self.args)])
+        if st != 0:
+            raise RuntimeError(f"qgemm_run failed: {st}")
+
+
+def time_steps(fn, steps, warmup, mode):
+    """ms per step of fn(i) for i in range(steps), after warmup steps. Runs on
+    torch's current stream, which main() sets to a side stream (graph capture
+    needs a non-default stream)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    if mode == "graph":
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):  # capture on the launch stream itself
+            for i in range(steps):
+                fn(i)
+        g.replay()              # untimed: first replay
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def device_problem(p, copies):
+    """Device tensors of a workloads.Problem with `copies` packed weight/scale copies."""
+    from tests.gpu_util import to_dev
+    import group_quantized_weight_amd as qg
+    A, a_scale, Wc, S, Z = to_dev(p)
+    W0 = qg.pack(Wc, p.K, p.N, p.prec)
+    del Wc
+    Ws, Ss = [W0], [S]
+    for _ in range(copies - 1):
+        Ws.append(W0.clone())
+        Ss.append(S.clone())
+    return A, Ws, Ss, Z
+
+
+def algorithmic_bytes(p):
+    wbytes = p.K * p.N // 2 if p.wfmt == "w4" else p.K * p.N
+    sbytes = (p.K // p.G) * p.N * (2 if p.sfmt == "bf16" else 4)
+    zbytes = (p.K // p.G) * p.N // 2 if p.has_zp else 0
+    abytes = p.M * p.K * {"bf16": 2, "f32": 4, "i8": 1}[p.afmt] + (p.M * (p.K // p.G) * 4 if p.afmt == "i8" else 0)
+    obytes = p.M * p.N * (2 if p.ofmt == "bf16" else 4)
+    return wbytes + sbytes + zbytes + abytes + obytes
+
+
+def run_workload(name, steps, warmup, mode, M=None):
+    import torch
+    import group_quantized_weight_amd as qg
+    import workloads as wl
+    p = wl.make_config(name, M=M)
+    per_copy = qg.packed_bytes(p.K, p.N, p.prec) + (p.K // p.G) * p.N * (2 if p.sfmt == "bf16" else 4)
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / per_copy)))
+    A, Ws, Ss, Z = device_problem(p, copies)
+    out = torch.empty((p.M, p.N), dtype=qg.out_dtype(p.prec), device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    call = Prepared(qg, p.M, p.N, p.K, p.G, p.prec, A, Ws, Ss, Z, out, stream)
+    ms = time_steps(call, steps, warmup, mode)
+    path, ns, ws = qg.plan(p.M, p.N, p.K, p.G, p.prec)
+    res = dict(workload=name, M=p.M, N=p.N, K=p.K, group=p.G, prec=qg._PREC_FMT[p.prec], has_zp=p.has_zp,
+               path=["gemv", "gemm"][path], nsplit=ns, copies=copies, ms=ms,
+               bytes=algorithmic_bytes(p), flops=2 * p.M * p.N * p.K)
+    res["gbs"] = res["bytes"] / (ms * 1e-3) / 1e9
+    res["tflops"] = res["flops"] / (ms * 1e-3) / 1e12
+    del A, Ws, Ss, Z, out, call
+    torch.cuda.empty_cache()
+    return res, p
+
+
+def dense_bf16(M, N, K, steps, warmup, mode):
+    """torch.matmul in bf16 on the same shape (weights rotated like the W4 run)."""
+    import torch
+    per_copy = K * N * 2
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / per_copy)))
+    A = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+    Ws = [torch.randn(K, N, dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+
+    def fn(i):
+        torch.matmul(A, Ws[i % copies], out=out)
+
+    if mode == "graph":
+        # replay check: a library call whose graph replay differs from eager stays out of the graph
+        fn(0)
+        ref = out.clone()
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=torch.cuda.current_stream()):
+            fn(0)
+        ok = True
+        for _ in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            ok &= bool(torch.equal(out, ref))
+        del g
+        if not ok:
+            log("dense bf16: graph replay differs from eager; timing eagerly")
+            mode = "eager"
+    ms = time_steps(fn, steps, warmup, mode)
+    del A, Ws, out
+    torch.cuda.empty_cache()
+    return ms
+
+
+def cpu_baseline(p, seconds=10.0):
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.for_problem(p)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / passes
+    return dict(value=algorithmic_bytes(p) / per / 1e9, unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"the whole {p.name} problem (M={p.M}, K={p.K}, N={p.N}), {passes} passes in {el:.1f} s; "
+                       f"{per * 1e3:.1f} ms per pass")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--workload", default="decode_w4a16_g128")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None, help="run one named workload only (profiling)")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM traffic per launch")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, sharding). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import group_quantized_weight_amd as qg
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    qg.lib()
+    side = torch.cuda.Stream()          # default priority
+    with torch.cuda.stream(side):
+        bench(args)
+
+
+def bench(args):
+    import group_quantized_weight_amd as qg
+    if args.only:
+        r, _ = run_workload(args.only, args.steps, args.warmup, args.mode)
+        log(json.dumps(r))
+        return
+
+    log(f"bench: {args.workload} steps={args.steps} warmup={args.warmup} mode={args.mode}")
+    head, p = run_workload(args.workload, args.steps, args.warmup, args.mode)
+    log(f"bench: {args.workload}: {head['ms'] * 1e3:.2f} us/step, {head['gbs']:.0f} GB/s")
+
+    gemm, _ = run_workload("prefill_w4a16_m1024", max(20, args.steps // 4), max(5, args.warmup // 2), args.mode)
+    log(f"bench: prefill M=1024: {gemm['ms'] * 1e3:.1f} us, {gemm['tflops']:.1f} TFLOP/s")
+
+    sweep = []
+    if not args.no_sweep:
+        for M in (1, 16, 64, 256, 1024, 4096):
+            st = 50 if M <= 256 else 20
+            r, _ = run_workload(f"prefill_w4a16_m{M}", st, 5, args.mode)
+            d_ms = dense_bf16(M, 4096, 4096, st, 5, args.mode)
+            sweep.append(dict(M=M, w4_us=r["ms"] * 1e3, bf16_us=d_ms * 1e3, w4_path=r["path"],
+                              w4_nsplit=r["nsplit"], w4_tflops=r["tflops"], w4_gbs=r["gbs"],
+                              bf16_tflops=2 * M * 4096 * 4096 / (d_ms * 1e-3) / 1e12,
+                              w4_speedup=d_ms / r["ms"]))
+            log(f"bench: sweep M={M}: w4 {r['ms'] * 1e3:.1f} us ({r['path']}), bf16 {d_ms * 1e3:.1f} us")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(p)
+        log(f"bench: cpu oracle {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16xint4->f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": head["M"], "K": head["K"], "N": head["N"],
+                   "group": head["group"], "prec": "W4_A_BF16", "path": head["path"], "nsplit": head["nsplit"],
+                   "weight_copies_rotated": head["copies"], "timing": args.mode},
+        "roofline": {"bound": "hbm", "achieved": round(head["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "gemm_m1024": {"workload": "prefill_w4a16_m1024", "us": round(gemm["ms"] * 1e3, 2),
+                       "tflops": round(gemm["tflops"], 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                       "frac": round(gemm["tflops"] / BF16_PEAK_TFLOPS, 4), "nsplit": gemm["nsplit"]},
+        "crossover": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+"""Python binding of libqgemm.so, the MI355X group-quantized weight-only GEMM.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in include/qgemm.h. PyTorch provides device memory and streams.
+If the library is not built, every call raises (there is no fallback).
+
+    import group_quantized_weight_amd as qg
+    wp = qg.pack(w_canonical, K, N, qg.W4_A_BF16)       # once per weight
+    out = qg.run(A, wp, scales, N=N, G=128, prec=qg.W4_A_BF16)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "qgemm.h")
+
+# status codes, precisions and paths (include/qgemm.h)
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EALIGN, EHIP = 0, -1, -2, -3, -4, -5
+W4_A_BF16, W4_A_F32, W8_A_F32, W4_A_I8, W8_A_I8, W4_A_BF16_OF32 = 1, 2, 3, 4, 5, 6
+PATH_AUTO, PATH_GEMV, PATH_GEMM = -1, 0, 1
+
+_PREC_FMT = {1: ("w4", "bf16", "bf16", "bf16"), 2: ("w4", "f32", "f32", "f32"),
+             3: ("w8", "f32", "f32", "f32"), 4: ("w4", "i8", "f32", "f32"),
+             5: ("w8", "i8", "f32", "f32"), 6: ("w4", "bf16", "bf16", "f32")}
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """The loaded C library; raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is not built: run `python -m group_quantized_weight_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+            L.qgemm_layout_version.restype = c_int
+            L.qgemm_layout_version.argtypes = []
+            L.qgemm_packed_bytes.restype = c_size
+            L.qgemm_packed_bytes.argtypes = [c_int, c_int, c_int]
+            L.qgemm_pack.restype = c_int
+            L.qgemm_pack.argtypes = [vp, vp, c_int, c_int, c_int, vp]
+            L.qgemm_workspace_bytes.restype = c_size
+            L.qgemm_workspace_bytes.argtypes = [c_int] * 5
+            L.qgemm_plan.restype = c_int
+            L.qgemm_plan.argtypes = [c_int] * 7 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                                   ctypes.POINTER(c_size)]
+            run_args = [c_int] * 6 + [vp] * 7 + [c_size, vp]
+            L.qgemm_run.restype = c_int
+            L.qgemm_run.argtypes = run_args
+            L.qgemm_run_ex.restype = c_int
+            L.qgemm_run_ex.argtypes = run_args + [c_int, c_int]
+            L.qgemm_strerror.restype = ctypes.c_char_p
+            L.qgemm_strerror.argtypes = [c_int]
+            _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/qgemm.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(qgemm_\w+)\s*\(", text)))
+
+
+def strerror(status: int) -> str:
+    return lib().qgemm_strerror(int(status)).decode()
+
+
+def layout_version() -> int:
+    return int(lib().qgemm_layout_version())
+
+
+def packed_bytes(K: int, N: int, prec: int) -> int:
+    return int(lib().qgemm_packed_bytes(K, N, prec))
+
+
+def padded_cols(N: int) -> int:
+    return (N + 255) // 256 * 256
+
+
+def plan(M: int, N: int, K: int, G: int, prec: int, force_path: int = PATH_AUTO, force_nsplit: int = 0):
+    """(path, nsplit, workspace_bytes) the library uses for this problem."""
+    path, ns, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    st = lib().qgemm_plan(M, N, K, G, prec, force_path, force_nsplit, ctypes.byref(path),
+                          ctypes.byref(ns), ctypes.byref(ws))
+    if st != OK:
+        raise QGemmError(st, "qgemm_plan")
+    return path.value, ns.value, ws.value
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def pack(w_canonical, K: int, N: int, prec: int):
+    """Repack canonical weights (int32 [K/8, N] words for int4, int8 [K, N] codes
+    for int8, on a GPU) into the kernel layout; returns an int32 tensor."""
+    import torch
+    nbytes = packed_bytes(K, N, prec)
+    if nbytes == 0:
+        raise QGemmError(EINVAL, "qgemm_packed_bytes")
+    rows = nbytes // (4 * padded_cols(N))
+    out = torch.empty((rows, padded_cols(N)), dtype=torch.int32, device=w_canonical.device)
+    st = lib().qgemm_pack(_ptr(w_canonical), _ptr(out), K, N, prec, _stream(w_canonical.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_pack")
+    return out
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device):
+    """A workspace of at least nbytes on device (cached per device and grown;
+    its contents before a call do not matter to the library)."""
+    import torch
+    if nbytes == 0:
+        return None
+    key = str(device)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def out_dtype(prec: int):
+    import torch
+    return torch.bfloat16 if _PREC_FMT[prec][3] == "bf16" else torch.float32
+
+
+def run(A, w_packed, scales, *, N: int, G: int, prec: int, zeros=None, a_scales=None, out=None,
+        ws=None, force_path: int = PATH_AUTO, force_nsplit: int = 0, stream=None):
+    """out[M, N] = group-quantized product (see include/qgemm.h).
+
+    A: [M, K] (bf16 / float32 / int8 per prec); w_packed: from pack();
+    scales: [K/G, N]; zeros: int32 [K/G, N/8] or None; a_scales: float32
+    [M, K/G] for int8 activations.
+    """
+    import torch
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype(prec), device=A.device)
+    _, _, need = plan(max(M, 1), N, K, G, prec, force_path, force_nsplit)
+    if ws is None:
+        ws = workspace(need, A.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().qgemm_run_ex(M, N, K, G, prec, int(zeros is not None), _ptr(A), _ptr(a_scales),
+                            _ptr(w_packed), _ptr(scales), _ptr(zeros), _ptr(out), _ptr(ws), ws_bytes,
+                            stream if stream is not None else _stream(A.device), force_path,
+                            force_nsplit)
+    if st != OK:
+        raise QGemmError(st, "qgemm_run")
+    return out

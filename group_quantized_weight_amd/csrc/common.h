@@ -1,0 +1,75 @@
+// Internal definitions shared by the HIP kernels and the C-ABI dispatcher.
+// gfx950 (CDNA4) only: wave64, MFMA, 160 KiB LDS per compute unit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+// Storage formats.
+enum WFmt { W4 = 0, W8 = 1 };                // int4 packed 8 per word | int8 packed 4 per word
+enum AFmt { A_F32 = 0, A_BF16 = 1, A_I8 = 2 };
+enum SFmt { S_F32 = 0, S_BF16 = 1 };
+enum OFmt { O_F32 = 0, O_BF16 = 1 };
+
+constexpr int kWave = 64;
+constexpr int kColAlign = 256;               // packed weights: N padded to this
+constexpr int kTileCols = 64;                // packed layout: columns per tile
+
+// GEMV path: one workgroup = 4 waves over one 64-column tile; lane l owns the
+// 4 adjacent columns 4 (l % 16) .. +3 of the tile and every 4th word-row
+// (l / 16) of its wave's K range.
+constexpr int kGemvWaves = 4;
+constexpr int kGemvThreads = kGemvWaves * kWave;
+
+// GEMM path: one workgroup = 4 waves (2 x 2), tile 128 x 128, K chunks of 128.
+constexpr int kGemmThreads = 256;
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+constexpr int kGemmKC = 128;
+
+struct GemvArgs {
+  const void *A;           // [M][K] activations
+  const float *a_scale;    // [M][K/G] (int8 activations)
+  const uint32_t *W;       // packed weights (layout version 2)
+  const void *S;           // [K/G][N]
+  const uint32_t *Z;       // [K/G][N/8] or null
+  void *out;               // [M][N] (nsplit == 1)
+  float *partial;          // [nsplit][M][Np] (nsplit > 1)
+  int M, N, K, G, Np;
+  int ngroups, nsplit;
+};
+
+struct GemmArgs {
+  const uint16_t *A;       // [M][K] bf16
+  const uint32_t *W;       // packed int4, layout version 2
+  const uint16_t *S;       // [K/G][N] bf16
+  const uint32_t *Z;       // [K/G][N/8] or null
+  void *out;               // [M][N] bf16 or float32 (nsplit == 1)
+  float *partial;          // [nsplit][M][Np] (nsplit > 1)
+  int M, N, K, G, Np;
+  int nchunks, nsplit;     // K / kGemmKC chunks split into nsplit slices
+};
+
+// Host-side launchers (defined next to their kernels). They return the HIP
+// launch status; the dispatcher has validated every argument before.
+hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, const GemvArgs &a,
+                       dim3 grid, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t stream);
+hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np,
+                       hipStream_t stream);
+// out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.
+hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
+                         hipStream_t stream);
+
+// Balanced contiguous partition of `count` items into `parts`: part z gets
+// [begin, begin + size).
+__host__ __device__ inline void split_range(int count, int parts, int z, int &begin, int &size) {
+  int base = count / parts, rem = count % parts;
+  begin = z * base + (z < rem ? z : rem);
+  size = base + (z < rem ? 1 : 0);
+}
+
+}  // namespace qg

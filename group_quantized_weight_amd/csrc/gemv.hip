@@ -1,0 +1,586 @@
+// GEMV path of the group-quantized GEMM: vector-ALU kernel for small M.
+//
+// Mapping (one workgroup = 4 waves = one 64-column tile of the packed layout):
+//   lane l       : columns 4 (l % 16) .. +3 of the tile and word-rows
+//                  r = l / 16 (mod 4) of its wave's K range; one 16-byte load
+//                  per lane per 4 rows, so each wave load reads 1 KiB of
+//                  contiguous memory (weights dense, activations broadcast:
+//                  the mapping of the page "04 · 分组量化 GEMM 内核"
+//                  (developer.aliyun.com), section 3.2, on a 64-wide wave).
+//   wave w       : a contiguous range of whole groups of the workgroup's slice.
+//   blockIdx.y   : block of MB activation rows.
+//   blockIdx.z   : K-slice z of nsplit balanced contiguous ranges of whole
+//                  groups (the z-split of the same page, section 3.3), used
+//                  only when the column tiles alone cannot fill the device;
+//                  slices write float32 partials that a second kernel adds in
+//                  the fixed order z = 0..nsplit-1.
+//
+// Per group, output element and lane the kernel forms the dot product of the
+// activations with a biased integer code and removes the bias with the sum
+// of the same activations:
+//   sum_k a_k (q_k - z) = sum_k a_k (b + q_k) - (b + z) * sum_k a_k
+// where b is the bias the dequant trick leaves in the code:
+//   bf16 activations: (b + q) is the bf16 value of pattern 0x4300 | q, i.e.
+//     128 + q (the bf16 magic number of the page "quantization-and-fused-kernels"
+//     (arganzheng.life), section 二.4); two codes are placed per 32-bit word by
+//     one and-or, then v_dot2_f32_bf16 multiplies two pairs and accumulates in
+//     float32.
+//   float32 activations: codes are split into bytes and converted with
+//     v_cvt_f32_ubyte (b = 0 for int4; b = 128 for int8 codes flipped to
+//     unsigned by xor 0x80).
+//   int8 activations: v_dot4_i32_i8 on byte codes, exact int32 per group
+//     (b = 0); the four lanes that share a column add their integer partials,
+//     so the whole group's integer dot is formed before it is scaled by
+//     a_scale * b_scale (the blockwise formula of developer.aliyun.com,
+//     section 二, and its remark that the group's integer dot must be finished
+//     before the scales are applied).
+// Then acc += s[g,n] * dot in float32 (the per-group scale of the teaching
+// GEMV, arganzheng.life section 九.4).
+//
+// Reduction: the 4 lanes of a column and then the 4 waves are added in a
+// fixed order (lane shuffles, then LDS), so results are reproducible.
+//
+// Latency: each thread issues its activation loads first and its first batch
+// of weight loads next, then writes the activations to LDS; since vector
+// loads complete in order, waiting for the activations never waits for the
+// weights, and the weight stream starts at the top of the kernel.
+#include <type_traits>
+
+#include "common.h"
+
+namespace qg {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_v;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_v;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  f32x2_t v = {x, 0.f};
+  bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+  return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xFFFFu);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Staged activations: bytes per packed word-row per activation row.
+template <int WF, int AF>
+struct Stage {
+  static constexpr int kpw = WF == W4 ? 8 : 4;  // k per packed word
+  static constexpr int bytes = AF == A_I8 ? kpw : (AF == A_BF16 ? 2 * kpw : 4 * kpw);
+};
+
+// Global -> registers: the activations of one word-row (kpw values). The
+// address is always valid (callers clamp it), so the load sits outside any
+// divergent branch and the compiler need not wait for it right away.
+template <int WF, int AF>
+__device__ __forceinline__ void load_row(const void *A, size_t k, u32x4_v &c0, u32x4_v &c1) {
+  c0 = (u32x4_v){0, 0, 0, 0};
+  c1 = c0;
+  if constexpr (AF == A_BF16) {
+    c0 = *(const u32x4_v *)((const uint16_t *)A + k);
+  } else if constexpr (AF == A_F32 && WF == W4) {
+    c0 = *(const u32x4_v *)((const float *)A + k);
+    c1 = *(const u32x4_v *)((const float *)A + k + 4);
+  } else if constexpr (AF == A_F32) {
+    c0 = *(const u32x4_v *)((const float *)A + k);
+  } else if constexpr (WF == W4) {
+    const u32x2_v v = *(const u32x2_v *)((const int8_t *)A + k);
+    c0[0] = v[0];
+    c0[1] = v[1];
+  } else {
+    c0[0] = *(const uint32_t *)((const int8_t *)A + k);
+  }
+}
+
+__device__ __forceinline__ void mask_row(bool ok, u32x4_v &c0, u32x4_v &c1) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c0[j] = ok ? c0[j] : 0u;
+    c1[j] = ok ? c1[j] : 0u;
+  }
+}
+
+// Registers -> LDS in the order the dot products consume; returns the row's
+// activation sum (float bits, or int bits for int8 codes), summed in k order.
+template <int WF, int AF>
+__device__ __forceinline__ uint32_t store_row(unsigned char *dst, const u32x4_v &c0, const u32x4_v &c1) {
+  if constexpr (AF == A_BF16) {
+    *(u32x4_v *)dst = c0;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = s + bf16_lo(c0[j]) + bf16_hi(c0[j]);
+    return __float_as_uint(s);
+  } else if constexpr (AF == A_F32 && WF == W4) {
+    // byte conversions of an interleaved word give k + {0,4,1,5} (low nibbles)
+    // and k + {2,6,3,7} (high nibbles)
+    *(u32x4_v *)dst = (u32x4_v){c0[0], c1[0], c0[1], c1[1]};
+    *(u32x4_v *)(dst + 16) = (u32x4_v){c0[2], c1[2], c0[3], c1[3]};
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += __uint_as_float(c0[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += __uint_as_float(c1[j]);
+    return __float_as_uint(s);
+  } else if constexpr (AF == A_F32) {
+    *(u32x4_v *)dst = c0;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += __uint_as_float(c0[j]);
+    return __float_as_uint(s);
+  } else if constexpr (WF == W4) {
+    // bytes k + {0,4,1,5} and k + {2,6,3,7}
+    const uint32_t lo = __builtin_amdgcn_perm(c0[1], c0[0], 0x05010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(c0[1], c0[0], 0x07030602u);
+    *(uint2 *)dst = make_uint2(lo, hi);
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += (int)(int8_t)(c0[0] >> (8 * j));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += (int)(int8_t)(c0[1] >> (8 * j));
+    return (uint32_t)s;
+  } else {
+    *(uint32_t *)dst = c0[0];
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += (int)(int8_t)(c0[0] >> (8 * j));
+    return (uint32_t)s;
+  }
+}
+
+template <int MB>
+struct BatchRows {  // weight load instructions issued together, by register budget
+  static constexpr int value = MB <= 2 ? 16 : (MB == 4 ? 8 : 4);
+};
+
+template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  using St = Stage<WF, AF>;
+  constexpr int KPW = St::kpw;
+  constexpr int AB = St::bytes;
+  constexpr int RPG = G / KPW;                        // word-rows per group: 4, 8, 16 or 32
+  constexpr int IPG = RPG / 4;                        // wave loads per group (4 rows each)
+  constexpr int BMAX = BatchRows<MB>::value;
+  constexpr int GPB = IPG >= BMAX ? 1 : (BMAX / IPG < 8 ? BMAX / IPG : 8);  // groups per batch
+  constexpr int IPB = GPB * IPG;                      // wave loads per batch
+  constexpr int SMAX = 4;                             // activation rows staged per thread up front
+  constexpr bool INT = AF == A_I8;
+  constexpr int bias = AF == A_BF16 ? 128 : ((AF == A_F32 && WF == W8) ? 128 : 0);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lk = lane >> 4, c4 = lane & 15;
+  const int tile = blockIdx.x;
+  const int ncol = tile * kTileCols + 4 * c4;         // first of this lane's 4 columns
+  const bool col_ok = ncol < a.N;
+  const int m0 = blockIdx.y * MB;
+  const int z = blockIdx.z;
+  const int R = a.K / KPW;                            // word-rows of the whole matrix
+
+  int gb, gcount;
+  split_range(a.ngroups, a.nsplit, z, gb, gcount);
+  int wg0, wgc;  // this wave's groups, local to the slice
+  split_range(gcount, kGemvWaves, wave, wg0, wgc);
+  const int rows = gcount * RPG;
+
+  // [MB][rows] staged rows plus one spare slot that threads without a row
+  // write to, so the staging stores need no divergent branch
+  const int nstage = MB * rows;
+  unsigned char *s_act = lds;                                          // [nstage + 1][AB]
+  uint32_t *s_rsum = (uint32_t *)(lds + (size_t)(nstage + 1) * AB);   // [nstage + 1]
+
+  const uint32_t *wbase = a.W + ((size_t)tile * R + (size_t)gb * RPG + lk) * kTileCols + 4 * c4;
+
+  // Scale and zero-point prefetch goes to registers with no divergent control
+  // flow (a lane past column N reads a clamped, valid address and masks the
+  // value at use), so issuing it never waits on the weight loads in flight.
+  const bool vec_s = (a.N & 3) == 0;                // 4 scales per lane in one load
+  const int scol = col_ok ? ncol : 0;
+  using SRaw = typename std::conditional<SF == S_BF16, u32x2_v, u32x4_v>::type;
+  u32x4_v wv[IPB];
+  SRaw sv[GPB];
+  uint32_t zv[GPB];
+  // a batch past the end of the wave's range re-reads its last group (valid,
+  // cached addresses) so the issue is straight-line; compute skips it
+  auto issue_batch = [&](int gfirst) {  // local group index of the batch's first group
+    const int glast = wgc > 0 ? wg0 + wgc - 1 : 0;
+#pragma unroll
+    for (int gi = 0; gi < GPB; ++gi) {
+      const int gl = gfirst + gi < glast ? gfirst + gi : glast;
+#pragma unroll
+      for (int i = 0; i < IPG; ++i)
+        wv[gi * IPG + i] =
+            __builtin_nontemporal_load((const u32x4_v *)(wbase + (size_t)(gl * RPG + 4 * i) * kTileCols));
+      // without 4-aligned rows (N % 4 != 0) the scales are read one by one at
+      // use; this load then reads the (aligned) first element and is ignored
+      const size_t si = vec_s ? (size_t)(gb + gl) * a.N + scol : 0;
+      if constexpr (SF == S_BF16)
+        sv[gi] = *(const u32x2_v *)((const uint16_t *)a.S + si);
+      else
+        sv[gi] = *(const u32x4_v *)((const float *)a.S + si);
+      if constexpr (ZP) zv[gi] = a.Z[(size_t)(gb + gl) * (a.N >> 3) + (scol >> 3)];
+    }
+  };
+  auto scales_of = [&](int gi, int gl, float *s) {
+    if (vec_s) {
+      if constexpr (SF == S_BF16) {
+        s[0] = bf16_lo(sv[gi][0]); s[1] = bf16_hi(sv[gi][0]);
+        s[2] = bf16_lo(sv[gi][1]); s[3] = bf16_hi(sv[gi][1]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[c] = __uint_as_float(sv[gi][c]);
+      }
+    } else {  // N not a multiple of 4: one scale at a time (not prefetched)
+      const size_t si = (size_t)(gb + gl) * a.N + ncol;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s[c] = 0.f;
+        if (ncol + c < a.N) {
+          if constexpr (SF == S_BF16)
+            s[c] = __uint_as_float((uint32_t)((const uint16_t *)a.S)[si + c] << 16);
+          else
+            s[c] = ((const float *)a.S)[si + c];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c] = col_ok ? s[c] : 0.f;
+  };
+
+  // ---- prologue: activation loads, first weight batch, activations to LDS ----
+  u32x4_v st0[SMAX], st1[SMAX];
+  bool st_ok[SMAX];
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    const int idx = threadIdx.x + kGemvThreads * s;
+    const int m = idx / rows, r = idx - (idx / rows) * rows;
+    st_ok[s] = idx < nstage && m0 + m < a.M;
+    const size_t k = st_ok[s] ? (size_t)(m0 + m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)m0 * a.K;
+    load_row<WF, AF>(a.A, k, st0[s], st1[s]);
+  }
+  issue_batch(wg0);  // a wave without groups re-reads valid addresses and computes nothing
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    const int idx = threadIdx.x + kGemvThreads * s;
+    mask_row(st_ok[s], st0[s], st1[s]);
+    const int slot = idx < nstage ? idx : nstage;
+    s_rsum[slot] = store_row<WF, AF>(s_act + (size_t)slot * AB, st0[s], st1[s]);
+  }
+  for (int idx = threadIdx.x + kGemvThreads * SMAX; idx < nstage; idx += kGemvThreads) {
+    const int m = idx / rows, r = idx - (idx / rows) * rows;
+    const bool ok = m0 + m < a.M;
+    u32x4_v c0, c1;
+    load_row<WF, AF>(a.A, ok ? (size_t)(m0 + m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)m0 * a.K, c0, c1);
+    mask_row(ok, c0, c1);
+    s_rsum[idx] = store_row<WF, AF>(s_act + (size_t)idx * AB, c0, c1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+  // ---- main loop over this wave's groups, GPB groups per batch ----
+  float acc[MB][4];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[m][c] = 0.f;
+
+  for (int gg = 0; gg < wgc; gg += GPB) {
+    if (gg > 0) issue_batch(wg0 + gg);
+#pragma unroll
+    for (int gi = 0; gi < GPB; ++gi) {
+      if (gg + gi >= wgc) break;
+      const int gl = wg0 + gg + gi;
+      float pf[MB][4];
+      int pi[MB][4];
+      uint32_t cs[MB];  // this lane's share of the group's activation sum
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        cs[m] = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pf[m][c] = 0.f;
+          pi[m][c] = 0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < IPG; ++i) {
+        const u32x4_v wq = wv[gi * IPG + i];
+        const int lr = gl * RPG + 4 * i + lk;  // local word-row
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          const uint32_t rs = s_rsum[m * rows + lr];
+          cs[m] = INT ? (uint32_t)((int)cs[m] + (int)rs) : __float_as_uint(__uint_as_float(cs[m]) + __uint_as_float(rs));
+        }
+        const unsigned char *arow = s_act + (size_t)lr * AB;
+        if constexpr (AF == A_BF16) {
+          uint32_t x[4][4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t w = wq[c];
+            x[c][0] = (w & 0x000F000Fu) | 0x43004300u;
+            x[c][1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+            x[c][2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+            x[c][3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+          }
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const u32x4_v av = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              float p = pf[m][c];
+              p = dot2_bf16(x[c][0], av[0], p);
+              p = dot2_bf16(x[c][1], av[1], p);
+              p = dot2_bf16(x[c][2], av[2], p);
+              p = dot2_bf16(x[c][3], av[3], p);
+              pf[m][c] = p;
+            }
+          }
+        } else if constexpr (AF == A_F32 && WF == W4) {
+          float q[4][8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t lo = wq[c] & 0x0F0F0F0Fu, hi = (wq[c] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              q[c][j] = (float)((lo >> (8 * j)) & 0xFFu);
+              q[c][4 + j] = (float)((hi >> (8 * j)) & 0xFFu);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const u32x4_v a0 = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
+            const u32x4_v a1 = *(const u32x4_v *)(arow + (size_t)m * rows * AB + 16);
+            const float av[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
+                                 __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
+                                 __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              float p = pf[m][c];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) p = __builtin_fmaf(q[c][j], av[j], p);
+              pf[m][c] = p;
+            }
+          }
+        } else if constexpr (AF == A_F32 && WF == W8) {
+          float q[4][4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t u = wq[c] ^ 0x80808080u;  // int8 code + 128 as an unsigned byte
+#pragma unroll
+            for (int j = 0; j < 4; ++j) q[c][j] = (float)((u >> (8 * j)) & 0xFFu);
+          }
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const u32x4_v a0 = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              float p = pf[m][c];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) p = __builtin_fmaf(q[c][j], __uint_as_float(a0[j]), p);
+              pf[m][c] = p;
+            }
+          }
+        } else if constexpr (AF == A_I8 && WF == W4) {
+          uint32_t lo[4], hi[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            lo[c] = wq[c] & 0x0F0F0F0Fu;
+            hi[c] = (wq[c] >> 4) & 0x0F0F0F0Fu;
+          }
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const uint2 av = *(const uint2 *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              int p = pi[m][c];
+              p = __builtin_amdgcn_sdot4((int)lo[c], (int)av.x, p, false);
+              p = __builtin_amdgcn_sdot4((int)hi[c], (int)av.y, p, false);
+              pi[m][c] = p;
+            }
+          }
+        } else {  // A_I8, W8
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const uint32_t av = *(const uint32_t *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) pi[m][c] = __builtin_amdgcn_sdot4((int)wq[c], (int)av, pi[m][c], false);
+          }
+        }
+      }
+
+      // ---- group epilogue: remove the code bias, apply the group scale ----
+      float s[4];
+      scales_of(gi, gl, s);
+      int zc[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        int zz = WF == W8 ? 0 : 8;
+        if constexpr (ZP) zz = (int)((zv[gi] >> (4 * ((ncol & 7) + c))) & 0xFu);
+        zc[c] = bias + zz;
+      }
+      if constexpr (INT) {
+        // the whole group's integer dot: add the 4 lanes (rows mod 4) sharing these columns
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          int t = (int)cs[m];
+          t += __shfl_xor(t, 16);
+          t += __shfl_xor(t, 32);
+          cs[m] = (uint32_t)t;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            int v = pi[m][c];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            pi[m][c] = v;
+          }
+        }
+        if (lk == 0) {
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const float asc = (m0 + m < a.M) ? a.a_scale[(size_t)(m0 + m) * a.ngroups + gb + gl] : 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int d = pi[m][c] - zc[c] * (int)cs[m];
+              acc[m][c] = __builtin_fmaf(asc * s[c], (float)d, acc[m][c]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float d = pf[m][c] - (float)zc[c] * __uint_as_float(cs[m]);
+            acc[m][c] = __builtin_fmaf(s[c], d, acc[m][c]);
+          }
+      }
+    }
+  }
+
+  // ---- reduction: the 4 lanes of a column, then the 4 waves (fixed order) ----
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float v = acc[m][c];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[m][c] = v;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  float *s_red = (float *)lds;  // [4][MB][64], reuses the staging area
+  if (lk == 0) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      *(float4 *)(s_red + ((size_t)wave * MB + m) * kTileCols + 4 * c4) =
+          make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+  for (int t = threadIdx.x; t < MB * kTileCols; t += kGemvThreads) {
+    const int m = t / kTileCols, col = t % kTileCols;
+    if (m0 + m >= a.M) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGemvWaves; ++w) v += s_red[((size_t)w * MB + m) * kTileCols + col];
+    const int n = tile * kTileCols + col;
+    if (a.nsplit > 1) {
+      a.partial[((size_t)z * a.M + m0 + m) * a.Np + n] = v;
+    } else if (n < a.N) {
+      const size_t o = (size_t)(m0 + m) * a.N + n;
+      if constexpr (OF == O_BF16)
+        ((uint16_t *)a.out)[o] = f32_to_bf16(v);
+      else
+        ((float *)a.out)[o] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fixed-order reduction of K-slice partials (second kernel of a split call)
+// ---------------------------------------------------------------------------
+template <int OF>
+__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ part, void *__restrict__ out,
+                                                     int M, int N, int Np, int nsplit) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    float s = 0.f;
+    for (int zz = 0; zz < nsplit; ++zz) s += part[((size_t)zz * M + m) * Np + n];
+    const size_t o = (size_t)m * N + n;
+    if constexpr (OF == O_BF16)
+      ((uint16_t *)out)[o] = f32_to_bf16(s);
+    else
+      ((float *)out)[o] = s;
+  }
+}
+
+hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
+                         hipStream_t st) {
+  dim3 grid((N + 255) / 256, M < 65535 ? M : 65535);
+  if (ofmt == O_BF16)
+    reduce_kernel<O_BF16><<<grid, 256, 0, st>>>(partial, out, M, N, Np, nsplit);
+  else
+    reduce_kernel<O_F32><<<grid, 256, 0, st>>>(partial, out, M, N, Np, nsplit);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// launcher: (wfmt, afmt, sfmt, ofmt, zp, mb, G) -> kernel instance
+// ---------------------------------------------------------------------------
+template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G>
+static hipError_t go(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  gemv_kernel<WF, AF, SF, OF, ZP, MB, G><<<grid, kGemvThreads, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int WF, int AF, int SF, int OF, bool ZP>
+static hipError_t go_mb(int mb, int G, const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+#define QG_G(MBV)                                                   \
+  return G == 32 ? go<WF, AF, SF, OF, ZP, MBV, 32>(a, grid, lds, st) \
+                 : go<WF, AF, SF, OF, ZP, MBV, 128>(a, grid, lds, st)
+  switch (mb) {
+    case 1: QG_G(1);
+    case 2: QG_G(2);
+    case 4: QG_G(4);
+    default: QG_G(8);
+  }
+#undef QG_G
+}
+
+hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, const GemvArgs &a,
+                       dim3 grid, size_t lds, hipStream_t st) {
+  const int G = a.G;
+  if (wfmt == W4 && afmt == A_BF16 && sfmt == S_BF16) {
+    if (ofmt == O_BF16)
+      return zp ? go_mb<W4, A_BF16, S_BF16, O_BF16, true>(mb, G, a, grid, lds, st)
+                : go_mb<W4, A_BF16, S_BF16, O_BF16, false>(mb, G, a, grid, lds, st);
+    return zp ? go_mb<W4, A_BF16, S_BF16, O_F32, true>(mb, G, a, grid, lds, st)
+              : go_mb<W4, A_BF16, S_BF16, O_F32, false>(mb, G, a, grid, lds, st);
+  }
+  if (wfmt == W4 && afmt == A_F32)
+    return zp ? go_mb<W4, A_F32, S_F32, O_F32, true>(mb, G, a, grid, lds, st)
+              : go_mb<W4, A_F32, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
+  if (wfmt == W8 && afmt == A_F32)
+    return go_mb<W8, A_F32, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
+  if (wfmt == W4 && afmt == A_I8)
+    return zp ? go_mb<W4, A_I8, S_F32, O_F32, true>(mb, G, a, grid, lds, st)
+              : go_mb<W4, A_I8, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
+  if (wfmt == W8 && afmt == A_I8)
+    return go_mb<W8, A_I8, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qg

@@ -1,0 +1,285 @@
+// C ABI of the group-quantized GEMM (declared in include/qgemm.h):
+// argument validation, dispatch by M, K-split sizing, workspace sizing and
+// launches on the caller's stream. No device memory is allocated here and no
+// call synchronizes the host.
+//
+// A call enqueues one kernel, or two when K is split: the split kernel writes
+// float32 partials to the workspace and a reduction kernel adds them in the
+// fixed order z = 0..nsplit-1 (the kernel boundary orders the two; no
+// device-wide fences or atomics are used).
+//
+// Dispatch follows the roofline argument of the page
+// "quantization-and-fused-kernels" (arganzheng.life), section 三.2: at small
+// M the product is bound by the weight bytes, so the vector-ALU GEMV path
+// streams the weights once; at larger M it is bound by arithmetic, and bf16
+// activations go to the MFMA path. The K-split (nsplit) and its fixed-order
+// reduction follow the z-split of the page "04 · 分组量化 GEMM 内核"
+// (developer.aliyun.com), section 3.3: a pure function of the shape and the
+// device's compute-unit count, so repeated calls (and captured graphs) take
+// the same partition and give bitwise identical results.
+#include <limits.h>
+
+#include <atomic>
+
+#include "../../include/qgemm.h"
+#include "common.h"
+
+using namespace qg;
+
+namespace {
+
+struct Formats {
+  int w, a, s, o;
+};
+
+bool prec_formats(int prec, Formats &f) {
+  switch (prec) {
+    case QG_W4_A_BF16: f = {W4, A_BF16, S_BF16, O_BF16}; return true;
+    case QG_W4_A_F32: f = {W4, A_F32, S_F32, O_F32}; return true;
+    case QG_W8_A_F32: f = {W8, A_F32, S_F32, O_F32}; return true;
+    case QG_W4_A_I8: f = {W4, A_I8, S_F32, O_F32}; return true;
+    case QG_W8_A_I8: f = {W8, A_I8, S_F32, O_F32}; return true;
+    case QG_W4_A_BF16_OF32: f = {W4, A_BF16, S_BF16, O_F32}; return true;
+    default: return false;
+  }
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+// Compute units of the current device (cached); 256 (MI355X) when no device
+// can be queried, so that planning also works on a host without a GPU.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = g_cus[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+size_t padded_cols(int N) { return ((size_t)N + kColAlign - 1) / kColAlign * kColAlign; }
+
+constexpr size_t kPartialCap = 256ull << 20;  // bytes of float32 partials at most
+constexpr size_t kGemvLdsCap = 60 * 1024;     // dynamic LDS per workgroup (static LDS comes on top)
+
+struct Plan {
+  int path = QG_PATH_GEMV;
+  int nsplit = 1;
+  int mb = 1, mblocks = 1;
+  int tiles_x = 1, tiles_y = 1;
+  int units = 1;          // groups (GEMV) or 128-k chunks (GEMM) along K
+  size_t lds = 0;
+  size_t ws = 0;
+};
+
+size_t gemv_lds(const Formats &f, int mb, int G, int ngroups, int nsplit) {
+  const int kpw = f.w == W4 ? 8 : 4;
+  const int ab = f.a == A_I8 ? kpw : (f.a == A_BF16 ? 2 * kpw : 4 * kpw);
+  const int gmax = (ngroups + nsplit - 1) / nsplit;
+  const size_t rows = (size_t)gmax * (G / kpw);
+  const size_t stage = ((size_t)mb * rows + 1) * (ab + 4);  // staged rows + a spare slot
+  const size_t red = (size_t)kGemvWaves * mb * kTileCols * 4;
+  size_t b = stage > red ? stage : red;
+  return (b + 15) / 16 * 16;
+}
+
+// Balanced split: the smallest nsplit giving the same per-slice count.
+int balance(int units, int nsplit) {
+  if (nsplit < 1) nsplit = 1;
+  if (nsplit > units) nsplit = units;
+  const int per = (units + nsplit - 1) / nsplit;
+  return (units + per - 1) / per;
+}
+
+int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int force_nsplit, Plan &p) {
+  const int cus = device_cus();
+  const size_t Np = padded_cols(N);
+  const bool gemm_ok = f.a == A_BF16 && G == 128 && K % kGemmKC == 0;
+  int path = force_path;
+  if (path == QG_PATH_AUTO) path = (M > 8 && gemm_ok) ? QG_PATH_GEMM : QG_PATH_GEMV;
+  if (path == QG_PATH_GEMM && !gemm_ok) return QG_EUNSUPPORTED;
+  if (path != QG_PATH_GEMV && path != QG_PATH_GEMM) return QG_EINVAL;
+  p.path = path;
+
+  long long base;
+  if (path == QG_PATH_GEMV) {
+    p.mb = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    p.mblocks = (M + p.mb - 1) / p.mb;
+    p.tiles_x = (int)(Np / kTileCols);
+    p.tiles_y = p.mblocks;
+    p.units = K / G;
+  } else {
+    p.tiles_x = (int)(Np / kGemmBN);
+    p.tiles_y = (M + kGemmBM - 1) / kGemmBM;
+    p.units = K / kGemmKC;
+  }
+  base = (long long)p.tiles_x * p.tiles_y;  // workgroups without a K-split
+
+  // K-split: only when the tiles alone leave compute units idle; then aim at
+  // two workgroups per compute unit.
+  int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((2LL * cus + base - 1) / base));
+  ns = balance(p.units, ns);
+  if (path == QG_PATH_GEMV)
+    while (ns < p.units && gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) ns = balance(p.units, ns + 1);
+  if (force_nsplit <= 0)
+    while (ns > 1 && (size_t)ns * M * Np * 4 > kPartialCap) {
+      const int lower = balance(p.units, ns - 1);
+      if (path == QG_PATH_GEMV && gemv_lds(f, p.mb, G, p.units, lower) > kGemvLdsCap) break;
+      ns = lower;
+    }
+  if (path == QG_PATH_GEMV) {
+    if (gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) return QG_EUNSUPPORTED;
+    p.lds = gemv_lds(f, p.mb, G, p.units, ns);
+  }
+  p.nsplit = ns;
+  p.ws = p.nsplit > 1 ? (size_t)p.nsplit * M * Np * 4 : 0;
+  return QG_OK;
+}
+
+// Shape checks shared by every entry point. Returns a status code.
+int check_shape(int M, int N, int K, int G, int prec, int has_zp, Formats &f) {
+  if (!prec_formats(prec, f)) return QG_EUNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0) return QG_EINVAL;
+  if (G != 32 && G != 128) return QG_EUNSUPPORTED;
+  if (K % G != 0) return QG_EINVAL;
+  if (has_zp && (f.w != W4 || N % 8 != 0)) return QG_EUNSUPPORTED;
+  if (padded_cols(N) > (size_t)INT_MAX) return QG_EUNSUPPORTED;
+  // grid limits: K-rows of the repack and row blocks of the GEMV
+  if ((f.w == W4 ? K / 8 : K / 4) > 65535) return QG_EUNSUPPORTED;
+  if ((M + 7) / 8 > 65535) return QG_EUNSUPPORTED;
+  return QG_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int qgemm_layout_version(void) { return 2; }
+
+size_t qgemm_packed_bytes(int K, int N, int prec) {
+  Formats f;
+  if (!prec_formats(prec, f) || K <= 0 || N <= 0) return 0;
+  if (f.w == W4 ? K % 8 : K % 4) return 0;
+  const size_t rows = f.w == W4 ? (size_t)K / 8 : (size_t)K / 4;
+  return rows * padded_cols(N) * 4;
+}
+
+int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, void *stream) {
+  Formats f;
+  if (!prec_formats(prec, f)) return QG_EUNSUPPORTED;
+  if (K <= 0 || N <= 0 || !w_canonical || !w_packed) return QG_EINVAL;
+  if (f.w == W4 ? K % 8 : K % 4) return QG_EINVAL;
+  if ((f.w == W4 ? K / 8 : K / 4) > 65535 || padded_cols(N) > (size_t)INT_MAX) return QG_EUNSUPPORTED;
+  if (!aligned16(w_canonical) || !aligned16(w_packed)) return QG_EALIGN;
+  const hipError_t e = launch_pack(f.w, w_canonical, (uint32_t *)w_packed, K, N, (int)padded_cols(N),
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_plan(int M, int N, int K, int group, int prec, int force_path, int force_nsplit, int *path,
+               int *nsplit, size_t *workspace_bytes) {
+  Formats f;
+  int st = check_shape(M, N, K, group, prec, 0, f);
+  if (st != QG_OK) return st;
+  Plan p;
+  st = make_plan(M > 0 ? M : 1, N, K, group, f, force_path, force_nsplit, p);
+  if (st != QG_OK) return st;
+  if (path) *path = p.path;
+  if (nsplit) *nsplit = p.nsplit;
+  if (workspace_bytes) *workspace_bytes = M > 0 ? p.ws : 0;
+  return QG_OK;
+}
+
+size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec) {
+  size_t ws = 0;
+  if (qgemm_plan(M, N, K, group, prec, QG_PATH_AUTO, 0, nullptr, nullptr, &ws) != QG_OK) return 0;
+  return ws;
+}
+
+int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const void *A,
+                 const void *a_scales, const void *w_packed, const void *scales, const void *zeros,
+                 void *out, void *workspace, size_t workspace_bytes, void *stream, int force_path,
+                 int force_nsplit) {
+  Formats f;
+  int st = check_shape(M, N, K, group, prec, has_zp, f);
+  if (st != QG_OK) return st;
+  if (M == 0) return QG_OK;
+  if (!A || !w_packed || !scales || !out) return QG_EINVAL;
+  if (f.a == A_I8 && !a_scales) return QG_EINVAL;
+  if (has_zp && !zeros) return QG_EINVAL;
+  if (!aligned16(A) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(out) ||
+      (f.a == A_I8 && !aligned16(a_scales)) || (has_zp && !aligned16(zeros)))
+    return QG_EALIGN;
+  Plan p;
+  st = make_plan(M, N, K, group, f, force_path, force_nsplit, p);
+  if (st != QG_OK) return st;
+  if (p.ws > 0) {
+    if (!workspace || workspace_bytes < p.ws) return QG_EWORKSPACE;
+    if (!aligned16(workspace)) return QG_EALIGN;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  float *partial = p.nsplit > 1 ? (float *)workspace : nullptr;
+  const int Np = (int)padded_cols(N);
+  hipError_t e;
+  if (p.path == QG_PATH_GEMV) {
+    GemvArgs a;
+    a.A = A;
+    a.a_scale = (const float *)a_scales;
+    a.W = (const uint32_t *)w_packed;
+    a.S = scales;
+    a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
+    a.out = out;
+    a.partial = partial;
+    a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np;
+    a.ngroups = K / group;
+    a.nsplit = p.nsplit;
+    e = launch_gemv(f.w, f.a, f.s, f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.mblocks, p.nsplit),
+                    p.lds, s);
+  } else {
+    GemmArgs a;
+    a.A = (const uint16_t *)A;
+    a.W = (const uint32_t *)w_packed;
+    a.S = (const uint16_t *)scales;
+    a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
+    a.out = out;
+    a.partial = partial;
+    a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np;
+    a.nchunks = K / kGemmKC;
+    a.nsplit = p.nsplit;
+    e = launch_gemm(f.o, has_zp != 0, group, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), s);
+  }
+  if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, partial, out, M, N, Np, p.nsplit, s);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_run(int M, int N, int K, int group, int prec, int has_zp, const void *A,
+              const void *a_scales, const void *w_packed, const void *scales, const void *zeros,
+              void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  return qgemm_run_ex(M, N, K, group, prec, has_zp, A, a_scales, w_packed, scales, zeros, out, workspace,
+                      workspace_bytes, stream, QG_PATH_AUTO, 0);
+}
+
+const char *qgemm_strerror(int status) {
+  switch (status) {
+    case QG_OK: return "ok";
+    case QG_EINVAL: return "invalid argument (null pointer, bad size, or K not a multiple of the group)";
+    case QG_EUNSUPPORTED: return "unsupported combination (group size, precision, zero-points or limits)";
+    case QG_EWORKSPACE: return "workspace missing or smaller than qgemm_workspace_bytes()";
+    case QG_EALIGN: return "pointer not 16-byte aligned";
+    case QG_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+/*
+ * qgemm.h -- C ABI of the group-quantized weight-only GEMM for MI355X (gfx950).
+ *
+ * It computes, for m < M and n < N,
+ *
+ *     out[m,n] = sum_g  s[g,n] * sum_{k in group g}  a[m,k] * (q[k,n] - z[g,n])
+ *
+ * with groups of G consecutive k (G = 32 or 128). This is the quantity of the
+ * page "04 · 分组量化 GEMM 内核" (developer.aliyun.com), section 二
+ * (out[m][n] = sum_g a_scale[m][g] * b_scale[n][g] * sum_{k in g} Aq*Wq), and
+ * of the W4A16 GEMM of the page "quantization-and-fused-kernels"
+ * (arganzheng.life), section 三.1 (int4 weights with per-group scales
+ * [K/g, N] and optional int4-packed zero-points [K/g, N/8], real value
+ * s * (q - z), fp32 accumulation).
+ *
+ * Conventions (all arrays row-major, caller-owned):
+ *   - int4 weights (canonical): uint32 [K/8][N]; the code of k = 8r + j sits
+ *     in bits 4j..4j+3 of word (r, n) (arganzheng.life section 二.4).
+ *     Without zero-points the zero-point is 8, so code c means c - 8
+ *     (section 九.4); a signed int4 value v in [-8, 7] is stored as v + 8.
+ *   - int8 weights (canonical): int8 [K][N], codes in [-127, 127], zero-point 0
+ *     (Q8_0, developer.aliyun.com section 二).
+ *   - scales: [K/G][N], bf16 or float32 by precision (below).
+ *   - zero-points: uint32 [K/G][N/8], column n = 8c + j in bits 4j..4j+3 of
+ *     word (g, c); int4 weights only; requires N % 8 == 0.
+ *   - activations: [M][K], bf16, float32, or int8 codes with float32 per-group
+ *     scales a_scales [M][K/G] (a = a_scale * code).
+ *   - out: [M][N], bf16 (rounded to nearest even once, at the end) or float32.
+ *   Accumulation is float32 throughout (arganzheng.life section 二.2).
+ *
+ * Memory and streams: every pointer passed to qgemm_pack / qgemm_run is a
+ * device pointer owned by the caller. The library allocates no device memory.
+ * All work is enqueued on `stream` (a hipStream_t; NULL is the null stream);
+ * no call synchronizes the host or copies between host and device.
+ *
+ * Errors: arguments are validated before anything is enqueued; on error
+ * nothing is launched and nothing is written.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    QG_OK = 0,
+    QG_EINVAL = -1,        /* null pointer, negative/zero size, K % G != 0          */
+    QG_EUNSUPPORTED = -2,  /* G not 32/128, unknown prec, zero-points not allowed  */
+    QG_EWORKSPACE = -3,    /* workspace smaller than qgemm_workspace_bytes()        */
+    QG_EALIGN = -4,        /* a pointer is not 16-byte aligned                      */
+    QG_EHIP = -5           /* the HIP runtime reported an error                     */
+};
+
+/* Precisions: weight codes | activations | scales | out. */
+enum {
+    QG_W4_A_BF16 = 1,      /* int4  | bf16                  | bf16    | bf16    */
+    QG_W4_A_F32 = 2,       /* int4  | float32               | float32 | float32 */
+    QG_W8_A_F32 = 3,       /* int8  | float32               | float32 | float32 */
+    QG_W4_A_I8 = 4,        /* int4  | int8 + a_scales f32   | float32 | float32 */
+    QG_W8_A_I8 = 5,        /* int8  | int8 + a_scales f32   | float32 | float32 */
+    QG_W4_A_BF16_OF32 = 6  /* int4  | bf16                  | bf16    | float32 */
+};
+
+/* Paths (for qgemm_plan / qgemm_run_ex). */
+enum {
+    QG_PATH_AUTO = -1,
+    QG_PATH_GEMV = 0,      /* vector-ALU path: weight streaming, any M               */
+    QG_PATH_GEMM = 1       /* MFMA path: bf16 activations (prec 1 and 6), G == 128    */
+};
+
+/*
+ * Version of the packed weight layout written by qgemm_pack. A packed buffer
+ * saved by one version must be re-packed if the version differs.
+ *
+ * Layout version 2. Np = N rounded up to a multiple of 256 (columns >= N are
+ * zero); R = K/8 (int4) or K/4 (int8) word-rows. The words are stored in
+ * tiles of 64 columns, each tile's rows one after another:
+ *     word (r, n) is at index ((n / 64) * R + r) * 64 + (n % 64)
+ *   int4: word (r, n) holds the 8 codes of k = 8r .. 8r+7 of column n with the
+ *         even k in the low half-word and the odd k in the high half-word:
+ *         bits 4p..4p+3 hold k = 8r + {0,2,4,6,1,3,5,7}[p].
+ *   int8: byte j of word (r, n) is the code of k = 4r + j.
+ */
+int qgemm_layout_version(void);
+
+/* Bytes of the packed weight buffer for a K x N weight of precision prec
+ * (0 if the arguments are invalid). */
+size_t qgemm_packed_bytes(int K, int N, int prec);
+
+/*
+ * Repack canonical weights (device pointer, layout above) into the kernel
+ * layout (device pointer of qgemm_packed_bytes(K, N, prec) bytes). Requires
+ * K % 8 == 0 (int4) or K % 4 == 0 (int8). Enqueued on `stream`.
+ */
+int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, void *stream);
+
+/*
+ * Device workspace bytes qgemm_run needs for this problem (0: none, and the
+ * workspace pointer may be NULL). The workspace holds the float32 partial
+ * sums of a K-split; its contents before a call do not matter. Calls that
+ * share a workspace must not run concurrently.
+ */
+size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec);
+
+/*
+ * The plan qgemm_run_ex would use: path (QG_PATH_GEMV or QG_PATH_GEMM),
+ * nsplit (number of K-slices of whole groups whose float32 partial sums are
+ * added in the fixed order z = 0, 1, ..., nsplit-1) and workspace bytes.
+ * force_path: QG_PATH_AUTO or a path; force_nsplit: <= 0 for automatic, else
+ * the requested split (clamped to [1, K/G]). The plan is a pure function of
+ * the arguments and the device's compute-unit count.
+ */
+int qgemm_plan(int M, int N, int K, int group, int prec, int force_path, int force_nsplit,
+               int *path, int *nsplit, size_t *workspace_bytes);
+
+/*
+ * out = the group-quantized product described at the top of this file.
+ * Enqueues one kernel, or two when K is split (nsplit > 1: the partial sums
+ * of the K-slices, then their fixed-order reduction).
+ *   M >= 0 (M == 0 is a no-op), N >= 1, K >= 1, K % group == 0, group in {32, 128}.
+ *   A:         activations [M][K] (bf16 / float32 / int8 by prec)
+ *   a_scales:  float32 [M][K/G] for *_A_I8, else NULL
+ *   w_packed:  output of qgemm_pack
+ *   scales:    [K/G][N] (bf16 for prec 1 and 6, else float32)
+ *   zeros:     uint32 [K/G][N/8] when has_zp (int4 only, N % 8 == 0), else NULL
+ *   out:       [M][N] (bf16 for prec 1, else float32)
+ *   workspace: device memory of at least qgemm_workspace_bytes() (see there)
+ * All pointers must be 16-byte aligned. Results are bitwise reproducible for
+ * a given plan (fixed partition and fixed summation orders, no floating-point
+ * atomics).
+ */
+int qgemm_run(int M, int N, int K, int group, int prec, int has_zp, const void *A,
+              const void *a_scales, const void *w_packed, const void *scales, const void *zeros,
+              void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* qgemm_run with an explicit plan (see qgemm_plan); for tests and tuning. */
+int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const void *A,
+                 const void *a_scales, const void *w_packed, const void *scales,
+                 const void *zeros, void *out, void *workspace, size_t workspace_bytes,
+                 void *stream, int force_path, int force_nsplit);
+
+/* Human-readable text of a status code. */
+const char *qgemm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

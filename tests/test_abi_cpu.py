@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and validates arguments before anything is launched."""
+import ctypes
+
+import pytest
+
+import group_quantized_weight_amd as qg
+
+# fake, 16-byte aligned device addresses: validation fails before any use
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+
+
+def run(M=1, N=256, K=256, G=32, prec=qg.W4_A_BF16, zp=0, A=P, asc=None, W=P, S=P, Z=None, out=P2,
+        ws=None, ws_bytes=0, path=-1, ns=0):
+    return qg.lib().qgemm_run_ex(M, N, K, G, prec, zp, A, asc, W, S, Z, out, ws, ws_bytes, None, path, ns)
+
+
+def test_library_exports_header_symbols():
+    lib = qg.lib()
+    names = qg.header_functions()
+    assert "qgemm_run" in names and "qgemm_pack" in names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_layout_and_sizes():
+    assert qg.layout_version() == 2
+    assert qg.packed_bytes(4096, 28672, qg.W4_A_BF16) == 4096 // 8 * 28672 * 4
+    assert qg.packed_bytes(2048, 11000, qg.W8_A_F32) == 2048 // 4 * 11008 * 4
+    assert qg.packed_bytes(4096, 1, qg.W4_A_F32) == 4096 // 8 * 256 * 4
+    assert qg.packed_bytes(12, 8, qg.W4_A_F32) == 0       # K % 8 != 0
+    assert qg.packed_bytes(64, 8, 99) == 0                # unknown precision
+    for s in (qg.OK, qg.EINVAL, qg.EUNSUPPORTED, qg.EWORKSPACE, qg.EALIGN, qg.EHIP):
+        assert qg.strerror(s)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(prec=0), qg.EUNSUPPORTED),
+    (dict(prec=7), qg.EUNSUPPORTED),
+    (dict(M=-1), qg.EINVAL),
+    (dict(N=0), qg.EINVAL),
+    (dict(K=0), qg.EINVAL),
+    (dict(G=64), qg.EUNSUPPORTED),
+    (dict(G=16), qg.EUNSUPPORTED),
+    (dict(K=100), qg.EINVAL),                          # K % G != 0 (the pages' CPU-fallback case)
+    (dict(K=160, G=32), qg.OK),                        # plan is fine; rejected later only if pointers bad
+    (dict(zp=1, Z=P, N=250), qg.EUNSUPPORTED),         # zero-points need N % 8 == 0
+    (dict(zp=1, Z=P, prec=qg.W8_A_F32), qg.EUNSUPPORTED),
+    (dict(zp=1, Z=None), qg.EINVAL),
+    (dict(A=None), qg.EINVAL),
+    (dict(W=None), qg.EINVAL),
+    (dict(S=None), qg.EINVAL),
+    (dict(out=None), qg.EINVAL),
+    (dict(prec=qg.W4_A_I8, asc=None), qg.EINVAL),
+    (dict(A=MIS), qg.EALIGN),
+    (dict(out=MIS), qg.EALIGN),
+    (dict(prec=qg.W4_A_I8, asc=MIS), qg.EALIGN),
+    (dict(path=qg.PATH_GEMM, prec=qg.W4_A_F32), qg.EUNSUPPORTED),
+    (dict(path=qg.PATH_GEMM, G=32, M=64), qg.EUNSUPPORTED),
+    (dict(path=5), qg.EINVAL),
+])
+def test_validation_before_launch(kw, status):
+    st = run(**kw)
+    if status == qg.OK:
+        # a valid call would launch: only check that validation itself passes by planning
+        assert qg.lib().qgemm_plan(1, kw.get("N", 256), kw["K"], kw["G"], qg.W4_A_BF16, -1, 0,
+                                   None, None, None) == qg.OK
+    else:
+        assert st == status, (kw, st)
+
+
+def test_m_zero_is_noop():
+    assert run(M=0, A=None, W=None, S=None, out=None) == qg.OK
+
+
+def test_workspace_checked_before_launch():
+    # a narrow decode shape needs a K-split, hence a workspace
+    path, ns, ws = qg.plan(1, 4096, 4096, 128, qg.W4_A_BF16)
+    assert ns > 1 and ws == ns * 4096 * 4
+    st = run(M=1, N=4096, K=4096, G=128, ws=None, ws_bytes=0)
+    assert st == qg.EWORKSPACE
+    st = run(M=1, N=4096, K=4096, G=128, ws=P, ws_bytes=ws - 1)
+    assert st == qg.EWORKSPACE
+    st = run(M=1, N=4096, K=4096, G=128, ws=MIS, ws_bytes=ws)
+    assert st == qg.EALIGN
+    # the wide decode shape fills the device with column tiles alone
+    assert qg.plan(1, 28672, 4096, 128, qg.W4_A_BF16)[1:] == (1, 0)
+
+
+def test_pack_validation():
+    L = qg.lib()
+    assert L.qgemm_pack(None, P, 64, 8, qg.W4_A_BF16, None) == qg.EINVAL
+    assert L.qgemm_pack(P, P2, 60, 8, qg.W4_A_BF16, None) == qg.EINVAL   # K % 8
+    assert L.qgemm_pack(P, P2, 64, 8, 42, None) == qg.EUNSUPPORTED
+    assert L.qgemm_pack(P, MIS, 64, 8, qg.W4_A_BF16, None) == qg.EALIGN
+
+
+CASES = [(1, 28672, 4096, 128, 1), (8, 28672, 8192, 128, 1), (1, 128256, 4096, 128, 1),
+         (32, 11264, 2048, 32, 2), (32, 11000, 2048, 32, 5), (1, 256, 256, 32, 2)]
+CASES += [(M, 4096, 4096, 128, 1) for M in (1, 16, 64, 256, 1024, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K,G,prec", CASES)
+def test_plan_is_pure_and_consistent(M, N, K, G, prec):
+    a = qg.plan(M, N, K, G, prec)
+    b = qg.plan(M, N, K, G, prec)
+    assert a == b
+    path, ns, ws = a
+    assert 1 <= ns <= K // G
+    assert ws == qg.lib().qgemm_workspace_bytes(M, N, K, G, prec)
+    assert (ws == 0) == (ns == 1)
+    if prec in (1, 6) and M > 8:
+        assert path == qg.PATH_GEMM
+    if M <= 8:
+        assert path == qg.PATH_GEMV
+
+
+def test_forced_plans():
+    for ns in (1, 2, 3, 7, 32, 1000):
+        path, got, ws = qg.plan(1, 1000, 4096, 128, qg.W4_A_BF16, qg.PATH_GEMV, ns)
+        assert got == min(ns, 32) or got <= 32
+        assert (ws == 0) == (got == 1)
+    path, ns, ws = qg.plan(300, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMM, 3)
+    assert path == qg.PATH_GEMM and ns == 3
+    path, ns, ws = qg.plan(300, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMV, 0)
+    assert path == qg.PATH_GEMV

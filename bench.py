@@ -39,26 +39,26 @@ def log(*a):
 
 
 class Prepared:
-    """qgemm_run calls with their ctypes arguments built once (host cost per
+    """qgemm_run_ex calls with their ctypes arguments built once (host cost per
     launch is then the C call itself)."""
 
-    def __init__(self, qg, M, N, K, G, prec, A, Ws, Ss, Z, out, stream):
-        import torch
+    def __init__(self, qg, M, N, K, G, prec, A, a_scale, Ws, Ss, Z, out, stream, force_path=-1, force_nsplit=0):
         self.lib = qg.lib()
-        _, _, ws_bytes = qg.plan(M, N, K, G, prec)
+        _, _, ws_bytes = qg.plan(M, N, K, G, prec, force_path, force_nsplit)
         self.ws = qg.workspace(ws_bytes, A.device)
         vp = ctypes.c_void_p
         self.args = []
         for W, S in zip(Ws, Ss):
-            self.args.append((M, N, K, G, prec, int(Z is not None), vp(A.data_ptr()), None,
+            self.args.append((M, N, K, G, prec, int(Z is not None), vp(A.data_ptr()),
+                              vp(a_scale.data_ptr()) if a_scale is not None else None,
                               vp(W.data_ptr()), vp(S.data_ptr()), vp(Z.data_ptr()) if Z is not None else None,
                               vp(out.data_ptr()), vp(self.ws.data_ptr()) if self.ws is not None else None,
-                              ws_bytes, vp(stream)))
+                              ws_bytes, vp(stream), force_path, force_nsplit))
 
     def __call__(self, i):
-        st = self.lib.qgemm_run(*self.args[i % len(self.args)])
+        st = self.lib.qgemm_run_ex(*self.args[i % len(self.args)])
         if st != 0:
-            raise RuntimeError(f"qgemm_run failed: {st}")
+            raise RuntimeError(f"qgemm_run_ex failed: {st}")
 
 
 def time_steps(fn, steps, warmup, mode):
@@ -105,7 +105,7 @@ def device_problem(p, copies):
     for _ in range(copies - 1):
         Ws.append(W0.clone())
         Ss.append(S.clone())
-    return A, Ws, Ss, Z
+    return A, a_scale, Ws, Ss, Z
 
 
 def algorithmic_bytes(p):
@@ -117,25 +117,25 @@ def algorithmic_bytes(p):
     return wbytes + sbytes + zbytes + abytes + obytes
 
 
-def run_workload(name, steps, warmup, mode, M=None):
+def run_workload(name, steps, warmup, mode, M=None, force_path=-1, force_nsplit=0):
     import torch
     import group_quantized_weight_amd as qg
     import workloads as wl
     p = wl.make_config(name, M=M)
     per_copy = qg.packed_bytes(p.K, p.N, p.prec) + (p.K // p.G) * p.N * (2 if p.sfmt == "bf16" else 4)
     copies = max(1, min(64, math.ceil(ROTATE_BYTES / per_copy)))
-    A, Ws, Ss, Z = device_problem(p, copies)
+    A, a_scale, Ws, Ss, Z = device_problem(p, copies)
     out = torch.empty((p.M, p.N), dtype=qg.out_dtype(p.prec), device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    call = Prepared(qg, p.M, p.N, p.K, p.G, p.prec, A, Ws, Ss, Z, out, stream)
+    call = Prepared(qg, p.M, p.N, p.K, p.G, p.prec, A, a_scale, Ws, Ss, Z, out, stream, force_path, force_nsplit)
     ms = time_steps(call, steps, warmup, mode)
-    path, ns, ws = qg.plan(p.M, p.N, p.K, p.G, p.prec)
+    path, ns, ws = qg.plan(p.M, p.N, p.K, p.G, p.prec, force_path, force_nsplit)
     res = dict(workload=name, M=p.M, N=p.N, K=p.K, group=p.G, prec=qg._PREC_FMT[p.prec], has_zp=p.has_zp,
                path=["gemv", "gemm"][path], nsplit=ns, copies=copies, ms=ms,
                bytes=algorithmic_bytes(p), flops=2 * p.M * p.N * p.K)
     res["gbs"] = res["bytes"] / (ms * 1e-3) / 1e9
     res["tflops"] = res["flops"] / (ms * 1e-3) / 1e12
-    del A, Ws, Ss, Z, out, call
+    del A, a_scale, Ws, Ss, Z, out, call
     torch.cuda.empty_cache()
     return res, p
 
@@ -203,6 +203,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="run one named workload only (profiling)")
+    ap.add_argument("--force-path", type=int, default=-1, help="with --only: QG_PATH_* to force")
+    ap.add_argument("--force-nsplit", type=int, default=0, help="with --only: K-split to force")
     ap.add_argument("--traffic", default=None, help="JSON file with measured HBM traffic per launch")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -223,7 +225,8 @@ def main():
 def bench(args):
     import group_quantized_weight_amd as qg
     if args.only:
-        r, _ = run_workload(args.only, args.steps, args.warmup, args.mode)
+        r, _ = run_workload(args.only, args.steps, args.warmup, args.mode, force_path=args.force_path,
+                            force_nsplit=args.force_nsplit)
         log(json.dumps(r))
         return
 

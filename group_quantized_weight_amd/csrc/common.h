@@ -20,9 +20,9 @@ constexpr int kTileCols = 64;                // packed layout: columns per tile
 
 // GEMV path: one workgroup = 4 waves over one 64-column tile; lane l owns the
 // 4 adjacent columns 4 (l % 16) .. +3 of the tile and every 4th word-row
-// (l / 16) of its wave's K range.
-constexpr int kGemvWaves = 4;
-constexpr int kGemvThreads = kGemvWaves * kWave;
+// (l / 16) of its wave's K range. (Eight waves per workgroup measured slower:
+// fewer workgroups fit per compute unit.)
+__host__ __device__ constexpr int gemv_waves(int) { return 4; }
 
 // GEMM path: one workgroup = 4 waves (2 x 2), tile 128 x 128, K chunks of 128.
 constexpr int kGemmThreads = 256;

@@ -47,14 +47,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_g));
 }
 
+// The bf16 magic pattern 0x4300 in both halves as an opaque VGPR value, so
+// that (w & mask) | magic compiles to one v_and_or_b32.
+__device__ __forceinline__ uint32_t bf16_magic_pair() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  return m;
+}
+
 // One packed word (8 codes, even k low / odd k high) -> 8 bf16 values 128 + q
 // in k order, as an MFMA operand.
-__device__ __forceinline__ bf16x8_t dequant_word(uint32_t w) {
+__device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, uint32_t magic) {
   u32x4_t x;
-  x[0] = (w & 0x000F000Fu) | 0x43004300u;
-  x[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  x[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  x[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  x[0] = (w & 0x000F000Fu) | magic;
+  x[1] = ((w >> 4) & 0x000F000Fu) | magic;
+  x[2] = ((w >> 8) & 0x000F000Fu) | magic;
+  x[3] = ((w >> 12) & 0x000F000Fu) | magic;
   return __builtin_bit_cast(bf16x8_t, x);
 }
 
@@ -129,6 +137,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     }
   };
 
+  const uint32_t magic = bf16_magic_pair();
   f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         const int s = gi * SPG + ks;  // k-step within the chunk
         bf16x8_t bfr[4];
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant_word(bcur[s][fn]);
+        for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant_word(bcur[s][fn], magic);
 #pragma unroll
         for (int fm = 0; fm < 4; ++fm) {
           const bf16x8_t afr = *(const bf16x8_t *)(abuf + (64 * wm + 16 * fm + li) * kLdsRowBytes +

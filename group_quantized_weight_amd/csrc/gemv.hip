@@ -37,8 +37,11 @@
 // Then acc += s[g,n] * dot in float32 (the per-group scale of the teaching
 // GEMV, arganzheng.life section 九.4).
 //
-// Reduction: the 4 lanes of a column and then the 4 waves are added in a
+// Reduction: the 4 lanes of a column and then the waves are added in a
 // fixed order (lane shuffles, then LDS), so results are reproducible.
+//
+// Latency hiding comes from many resident waves: each wave streams about one
+// batch of loads and computes while the other waves' loads are in flight.
 //
 // Latency: each thread issues its activation loads first and its first batch
 // of weight loads next, then writes the activations to LDS; since vector
@@ -55,6 +58,11 @@ typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_v;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_v;
 
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle) and the
+// cache policy for streamed weights (non-temporal).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCachePolicyStream = 2;
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
@@ -62,6 +70,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   f32x2_t v = {x, 0.f};
   bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
   return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xFFFFu);
+}
+
+// The bf16 magic pattern 0x4300 in both halves, as an opaque VGPR value: with
+// one constant in a VGPR (the mask goes to an SGPR) the (w & mask) | magic
+// step compiles to a single v_and_or_b32 (a VOP3 encoding cannot hold two
+// literal constants).
+__device__ __forceinline__ uint32_t bf16_magic_pair() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  return m;
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -160,7 +178,10 @@ struct BatchRows {  // weight load instructions issued together, by register bud
 };
 
 template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(gemv_waves(MB) * kWave)
+void gemv_kernel(GemvArgs a) {
+  constexpr int kGemvWaves = gemv_waves(MB);
+  constexpr int kGemvThreads = kGemvWaves * kWave;
   extern __shared__ __align__(16) unsigned char lds[];
   using St = Stage<WF, AF>;
   constexpr int KPW = St::kpw;
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   constexpr int BMAX = BatchRows<MB>::value;
   constexpr int GPB = IPG >= BMAX ? 1 : (BMAX / IPG < 8 ? BMAX / IPG : 8);  // groups per batch
   constexpr int IPB = GPB * IPG;                      // wave loads per batch
-  constexpr int SMAX = 4;                             // activation rows staged per thread up front
+  constexpr int SMAX = 2;                             // activation rows staged per thread up front
   constexpr bool INT = AF == A_I8;
   constexpr int bias = AF == A_BF16 ? 128 : ((AF == A_F32 && WF == W8) ? 128 : 0);
 
@@ -196,13 +217,26 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   unsigned char *s_act = lds;                                          // [nstage + 1][AB]
   uint32_t *s_rsum = (uint32_t *)(lds + (size_t)(nstage + 1) * AB);   // [nstage + 1]
 
-  const uint32_t *wbase = a.W + ((size_t)tile * R + (size_t)gb * RPG + lk) * kTileCols + 4 * c4;
+  // Weights, scales and zero-points are read through buffer resources: the
+  // tile's base and the group's offset are wave-uniform (SGPRs) and each lane
+  // adds one fixed byte offset, so issuing a load costs no vector arithmetic.
+  // (A buffer load past num_records returns 0 instead of faulting.)
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.W + (size_t)tile * R * kTileCols), (short)0, R * kTileCols * 4, kBufferWord3);
+  const int w_voff = (lk * kTileCols + 4 * c4) * 4;
 
   // Scale and zero-point prefetch goes to registers with no divergent control
   // flow (a lane past column N reads a clamped, valid address and masks the
   // value at use), so issuing it never waits on the weight loads in flight.
   const bool vec_s = (a.N & 3) == 0;                // 4 scales per lane in one load
   const int scol = col_ok ? ncol : 0;
+  constexpr int SB = SF == S_BF16 ? 2 : 4;          // bytes per scale
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.S, (short)0, a.ngroups * a.N * SB, kBufferWord3);
+  const int s_voff = vec_s ? scol * SB : 0;
+  const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.Z, (short)0, ZP ? a.ngroups * (a.N >> 3) * 4 : 0, kBufferWord3);
+  const int z_voff = (scol >> 3) * 4;
   using SRaw = typename std::conditional<SF == S_BF16, u32x2_v, u32x4_v>::type;
   u32x4_v wv[IPB];
   SRaw sv[GPB];
@@ -216,16 +250,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
       const int gl = gfirst + gi < glast ? gfirst + gi : glast;
 #pragma unroll
       for (int i = 0; i < IPG; ++i)
-        wv[gi * IPG + i] =
-            __builtin_nontemporal_load((const u32x4_v *)(wbase + (size_t)(gl * RPG + 4 * i) * kTileCols));
+        wv[gi * IPG + i] = __builtin_bit_cast(
+            u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff, ((gb + gl) * RPG + 4 * i) * kTileCols * 4,
+                                                           kCachePolicyStream));
       // without 4-aligned rows (N % 4 != 0) the scales are read one by one at
-      // use; this load then reads the (aligned) first element and is ignored
-      const size_t si = vec_s ? (size_t)(gb + gl) * a.N + scol : 0;
+      // use; this load then reads the first element and is ignored
+      const int s_soff = vec_s ? (gb + gl) * a.N * SB : 0;
       if constexpr (SF == S_BF16)
-        sv[gi] = *(const u32x2_v *)((const uint16_t *)a.S + si);
+        sv[gi] = __builtin_bit_cast(u32x2_v, __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, s_voff, s_soff, 0));
       else
-        sv[gi] = *(const u32x4_v *)((const float *)a.S + si);
-      if constexpr (ZP) zv[gi] = a.Z[(size_t)(gb + gl) * (a.N >> 3) + (scol >> 3)];
+        sv[gi] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, s_voff, s_soff, 0));
+      if constexpr (ZP)
+        zv[gi] = __builtin_amdgcn_raw_buffer_load_b32(z_rsrc, z_voff, (gb + gl) * (a.N >> 3) * 4, 0);
     }
   };
   auto scales_of = [&](int gi, int gl, float *s) {
@@ -286,6 +322,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   // ---- main loop over this wave's groups, GPB groups per batch ----
+  const uint32_t magic = bf16_magic_pair();
   float acc[MB][4];
 #pragma unroll
   for (int m = 0; m < MB; ++m)
@@ -325,10 +362,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const uint32_t w = wq[c];
-            x[c][0] = (w & 0x000F000Fu) | 0x43004300u;
-            x[c][1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-            x[c][2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-            x[c][3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+            x[c][0] = (w & 0x000F000Fu) | magic;
+            x[c][1] = ((w >> 4) & 0x000F000Fu) | magic;
+            x[c][2] = ((w >> 8) & 0x000F000Fu) | magic;
+            x[c][3] = ((w >> 12) & 0x000F000Fu) | magic;
           }
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
@@ -465,7 +502,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // ---- reduction: the 4 lanes of a column, then the 4 waves (fixed order) ----
+  // ---- reduction: the 4 lanes of a column, then the waves (fixed order) ----
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -478,7 +515,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  float *s_red = (float *)lds;  // [4][MB][64], reuses the staging area
+  float *s_red = (float *)lds;  // [waves][MB][64], reuses the staging area
   if (lk == 0) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -542,7 +579,7 @@ hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N
 // ---------------------------------------------------------------------------
 template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G>
 static hipError_t go(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  gemv_kernel<WF, AF, SF, OF, ZP, MB, G><<<grid, kGemvThreads, lds, st>>>(a);
+  gemv_kernel<WF, AF, SF, OF, ZP, MB, G><<<grid, gemv_waves(MB) * kWave, lds, st>>>(a);
   return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ size_t gemv_lds(const Formats &f, int mb, int G, int ngroups, int nsplit) {
   const int gmax = (ngroups + nsplit - 1) / nsplit;
   const size_t rows = (size_t)gmax * (G / kpw);
   const size_t stage = ((size_t)mb * rows + 1) * (ab + 4);  // staged rows + a spare slot
-  const size_t red = (size_t)kGemvWaves * mb * kTileCols * 4;
+  const size_t red = (size_t)gemv_waves(mb) * mb * kTileCols * 4;
   size_t b = stage > red ? stage : red;
   return (b + 15) / 16 * 16;
 }
@@ -156,6 +156,9 @@ int check_shape(int M, int N, int K, int G, int prec, int has_zp, Formats &f) {
   // grid limits: K-rows of the repack and row blocks of the GEMV
   if ((f.w == W4 ? K / 8 : K / 4) > 65535) return QG_EUNSUPPORTED;
   if ((M + 7) / 8 > 65535) return QG_EUNSUPPORTED;
+  // buffer resources address scales, zero-points and one weight tile with
+  // 32-bit byte offsets
+  if ((size_t)(K / G) * N * 4 > (size_t)INT_MAX || (size_t)K * kTileCols > (size_t)INT_MAX) return QG_EUNSUPPORTED;
   return QG_OK;
 }
 

@@ -205,7 +205,10 @@ def main():
     ap.add_argument("--only", default=None, help="run one named workload only (profiling)")
     ap.add_argument("--force-path", type=int, default=-1, help="with --only: QG_PATH_* to force")
     ap.add_argument("--force-nsplit", type=int, default=0, help="with --only: K-split to force")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM traffic per launch")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.txt"),
+                    help="measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE summary)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="time a plain device copy of this many MiB instead (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, sharding). "
@@ -222,8 +225,45 @@ def main():
         bench(args)
 
 
+def copy_calibration(mib, steps, warmup):
+    """A plain device-to-device copy of `mib` MiB per step: the known-size
+    kernel whose FETCH_SIZE / WRITE_SIZE readings scale the counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = time_steps(lambda i: dst.copy_(src), steps, warmup, "eager")
+    log(json.dumps(dict(copy_mib=mib, bytes_each_way=n, ms=ms, gbs=2 * n / (ms * 1e-3) / 1e9)))
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(path, workload):
+    """HBM bytes per launch from the counter summary, or None when there is
+    none for this workload or the kernel source changed since it was taken.
+    Lines: `traffic <workload> <source file> <sha256[:16]> <bytes per launch>`."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 5 and parts[0] == "traffic" and parts[1] == workload:
+                src = os.path.join(ROOT, parts[2])
+                if os.path.exists(src) and source_digest(src) == parts[3]:
+                    return int(parts[4])
+                log(f"bench: {parts[2]} changed since its counters were taken: traffic unknown")
+    return None
+
+
 def bench(args):
     import group_quantized_weight_amd as qg
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, args.steps, args.warmup)
+        return
     if args.only:
         r, _ = run_workload(args.only, args.steps, args.warmup, args.mode, force_path=args.force_path,
                             force_nsplit=args.force_nsplit)
@@ -254,10 +294,7 @@ def bench(args):
         cpu = cpu_baseline(p)
         log(f"bench: cpu oracle {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get(args.workload)
+    traffic = measured_traffic(args.traffic, args.workload)
 
     line = {
         "metric": METRIC,

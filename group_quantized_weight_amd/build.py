@@ -29,6 +29,9 @@ def flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             # packed fp32 instructions are kept out of every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA operands and results in ordinary VGPRs: the per-group fp32
+            # promotion then reads them without accumulator-register moves
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-Wall"]
 
 

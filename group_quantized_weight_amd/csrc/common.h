@@ -49,7 +49,8 @@ struct GemmArgs {
   const uint32_t *Z;       // [K/G][N/8] or null
   void *out;               // [M][N] bf16 or float32 (nsplit == 1)
   float *partial;          // [nsplit][M][Np] (nsplit > 1)
-  int M, N, K, G, Np;
+  float *asum;             // [K/128][Mp] activation sums per group (workspace)
+  int M, N, K, G, Np, Mp;  // Mp = M rounded up to kGemmBM
   int nchunks, nsplit;     // K / kGemmKC chunks split into nsplit slices
 };
 

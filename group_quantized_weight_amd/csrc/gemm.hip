@@ -1,25 +1,34 @@
 // MFMA path of the group-quantized GEMM: bf16 activations, int4 weights,
-// bf16 scales, optional int4 zero-points; for M large enough that the work
-// is a dense contraction (prefill).
+// bf16 scales, optional int4 zero-points, groups of 128; for M large enough
+// that the work is a dense contraction (prefill).
 //
 // Structure (the W4A16 main loop of the page "quantization-and-fused-kernels"
 // (arganzheng.life), section 三.1: int4 tile -> unpack in registers -> matrix
-// instruction in bf16 with float32 accumulation):
-//   - workgroup tile 128 x 128 (4 waves, 2 x 2, each 64 x 64 = 4 x 4 MFMA
-//     tiles of v_mfma_f32_16x16x32_bf16), K in chunks of 128;
-//   - activations: global -> registers -> LDS (double buffered, rows padded
-//     by 16 bytes against bank conflicts) -> MFMA A fragments;
-//   - weights: each lane loads its packed words straight from global memory
-//     (16 bytes = 4 adjacent columns x 8 k) and turns each word into four
-//     bf16 pairs (128 + q) with one and-or per pair (bf16 magic number
-//     0x4300, section 二.4 of the same page); the four columns of one load
-//     feed the four MFMA column tiles of the wave, so MFMA column j of tile f
-//     is physical column n + 4j + f;
+// instruction in bf16 with float32 accumulation; and the multi-stage
+// global-to-shared pipeline of its section 三.3, item 2):
+//   - workgroup tile 128 x 128 (4 waves, 2 x 2, each 64 x 64 = 4 x 4 tiles of
+//     v_mfma_f32_16x16x32_bf16); K in chunks of 128 = one group;
+//   - every operand of a chunk (activation tile, packed weight tile, scales,
+//     zero-points, activation sums) is copied by buffer loads straight into
+//     LDS (no registers on the way), into a ring of 3 stages: two chunks are
+//     in flight while one is consumed. Each wave waits for its own copies of
+//     the chunk (vmcnt counts them in issue order), then a barrier makes every
+//     wave's copies visible;
+//   - the activation tile's 16-byte pieces are XOR-swizzled with the row
+//     index, so the MFMA fragment reads of 16 rows hit 16 different 4-bank
+//     groups; rows past M are clamped to row M-1 (their results are dropped);
+//   - weights: each lane reads 16 bytes of packed words (4 adjacent columns x
+//     8 k) and turns each word into four bf16 pairs (128 + q) with one and-or
+//     per pair (bf16 magic number 0x4300, section 二.4 of the same page); the
+//     four columns feed the four MFMA column tiles of the wave, so MFMA column
+//     j of tile f is physical column n + 4j + f;
 //   - per group, the MFMA accumulates sum_k a_k (128 + q_k) on top of the
-//     initial value -(128 + z) * sum_k a_k, which is sum_k a_k (q_k - z); the
-//     group's scale is then applied in float32 (acc += s * P), the per-block
-//     scale promotion of the same page, section 四.3. The (q - z) values are
-//     exact in bf16 and the scale never rounds into a bf16 weight.
+//     initial value -(128 + z) * sum_k a_k, which gives sum_k a_k (q_k - z);
+//     the group's scale is then applied in float32 (acc += s * P), the
+//     per-block promotion of the same page, section 四.3. The (q - z) values
+//     are exact in bf16 and the scale never rounds into a bf16 weight. The
+//     per-(group, row) activation sums come from asum_kernel, a pre-pass that
+//     adds each group's 128 values in a fixed order;
 //   - with nsplit > 1, K-slices of whole chunks write float32 partial tiles
 //     that a second kernel adds in the fixed order z = 0..nsplit-1 (the
 //     z-split and fixed-order reduce of the page "04 · 分组量化 GEMM 内核"
@@ -31,15 +40,33 @@ namespace qg {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_g;
 typedef __attribute__((ext_vector_type(2))) float f32x2_g;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kLdsRowBytes = kGemmKC * 2 + 16;              // padded A row in LDS
-constexpr int kLdsABytes = kGemmBM * kLdsRowBytes;          // one A buffer
+// One LDS stage: [activations 128 x 256 B][weights 2 tiles x 16 rows x 256 B]
+// [scales 128 x 2 B][activation sums 128 x 4 B][zero-points 16 x 4 B].
+// Each small slot is as large as one wave-wide copy writes (lanes past the
+// useful part copy neighbouring data into the slot's tail, never read).
+constexpr int kStages = 3;
+constexpr int kARow = kGemmKC * 2;                   // 256 B per activation row
+constexpr int kAOff = 0;
+constexpr int kBOff = kAOff + kGemmBM * kARow;       // 32 KiB
+constexpr int kSOff = kBOff + 2 * 16 * 256;          // + 8 KiB
+constexpr int kQOff = kSOff + 1024;
+constexpr int kZOff = kQOff + 1024;
+constexpr int kStageBytes = kZOff + 256;             // 43264
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kPolicyStream = 2;                     // non-temporal
 
-__device__ __forceinline__ float dot2_ones(uint32_t a, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_g, a),
-                                         __builtin_bit_cast(bf16x2_g, 0x3F803F80u), c, false);
+// s_waitcnt with only the vector-memory counter limited (expcnt and lgkmcnt
+// at their maxima), followed by the workgroup barrier; the memory clobber
+// keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -66,75 +93,84 @@ __device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, uint32_t magic) {
   return __builtin_bit_cast(bf16x8_t, x);
 }
 
-template <int OF, bool ZP, int G>
+template <typename T>
+__device__ __forceinline__ T lds_read(const unsigned char *base, int off) {
+  return *(const T *)(base + off);
+}
+
+template <int OF, bool ZP>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
-  static_assert(G == 32 || G == 128, "group size");
-  constexpr int GPC = kGemmKC / G;   // groups per chunk
-  constexpr int SPG = G / 32;        // MFMA k-steps per group
-  __shared__ __align__(16) unsigned char s_a[2][kLdsABytes];
-  __shared__ __align__(16) float s_sum[2][GPC][kGemmBM];
+  __shared__ __align__(16) unsigned char s_ring[kStages * kStageBytes];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 15, lk = lane >> 4;
   const int m0 = blockIdx.y * kGemmBM;
   const int n0 = blockIdx.x * kGemmBN;
-  const int nw = n0 + 64 * wn;              // first column of this wave
-  const int ncol = nw + 4 * li;             // this lane's 4 columns (one per column tile)
+  const int ncol = n0 + 64 * wn + 4 * li;   // this lane's 4 columns (one per column tile)
 
   int cb, ccount;
   split_range(a.nchunks, a.nsplit, blockIdx.z, cb, ccount);
 
-  // A staging role: row t/2, k half (t&1) of the chunk: 8 x 16 bytes
-  const int ar = t >> 1, ah = t & 1;
-  const bool a_ok = m0 + ar < a.M;
-  const uint16_t *a_src = a.A + (size_t)(m0 + (a_ok ? ar : 0)) * a.K + 64 * ah;
-  // B role: per k-step s, word-row 4s + lk of the chunk, columns 4 li .. +3 of
-  // the wave's 64-column tile of the packed layout (tile-major: a wave load of
-  // 4 consecutive rows is 1 KiB of contiguous memory)
+  // ---- copies into a stage (issue order per wave: small slot, weights,
+  // activations; every wave issues 10 copies plus at most one small one) ----
   const int R = a.K / 8;
-  const uint32_t *b_src = a.W + ((size_t)(nw / kTileCols) * R + lk) * kTileCols + 4 * li;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.A + (size_t)m0 * a.K), (short)0, 0x7FFFFFFF, kBufWord3);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.W + (size_t)(n0 / kTileCols) * R * kTileCols), (short)0, 0x7FFFFFFF, kBufWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.S, (short)0, a.nchunks * a.N * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t q_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.asum, (short)0, a.nchunks * a.Mp * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.Z, (short)0, ZP ? a.nchunks * (a.N >> 3) * 4 : 0, kBufWord3);
 
-  u32x4_t areg[8];
-  u32x4_t bcur[4], bnext[4];
+  // activations: copy j of this wave writes LDS bytes (4j + wave) KiB of the
+  // tile: pieces p = 64 (4j + wave) + lane; piece p is row p/16, physical
+  // slot p%16, holding logical 16-byte chunk (p%16) ^ (row%16) of the row.
+  int a_voff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = (4 * j + wave) * 64 + lane;
+    const int r = p >> 4, c = (p & 15) ^ (r & 15);
+    const int row = min(m0 + r, a.M - 1) - m0;
+    a_voff[j] = row * (a.K * 2) + c * 16;
+  }
+  // weights: copy j of wave w writes bytes 2048 w + 1024 j of the 8 KiB
+  // weight slot = column tile w/2, word-rows 4((2w + j) % 4) .. +3 of the chunk
+  const int b_tile = wave >> 1;
+  const int b_voff = b_tile * R * 256 + lane * 16;
 
-  auto load_a = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      areg[i] = a_ok ? *(const u32x4_t *)(a_src + (size_t)c * kGemmKC + 8 * i) : (u32x4_t){0, 0, 0, 0};
-  };
-  auto load_b = [&](int c, u32x4_t *dst) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      dst[s] = __builtin_nontemporal_load(
-          (const u32x4_t *)(b_src + (size_t)(c * (kGemmKC / 8) + 4 * s) * kTileCols));
-  };
-  auto stage_a = [&](int buf) {
-    unsigned char *dst = &s_a[buf][ar * kLdsRowBytes + 128 * ah];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4_t *)(dst + 16 * i) = areg[i];
-    // activation sums per (row, group) of this chunk, fixed order
-    if constexpr (G == 128) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s = dot2_ones(areg[i][j], s);
-      const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0xB1, 0xF, 0xF, false));
-      if (ah == 0) s_sum[buf][0][ar] = s + other;
-    } else {
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 4 * gg; i < 4 * gg + 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s = dot2_ones(areg[i][j], s);
-        s_sum[buf][2 * ah + gg][ar] = s;
-      }
+  auto issue = [&](int chunk, int stage) {
+    unsigned char *st = s_ring + stage * kStageBytes;
+    // The small copies read past their useful part and, at the last chunk,
+    // past the end of their array: those lanes rely on the buffer's range
+    // check (which returns zeros), so the whole offset is in the VGPR
+    // operand: the SGPR offset is not range-checked.
+    if (wave == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void *)(st + kSOff), 16,
+                                               (chunk * a.N + n0) * 2 + lane * 16, 0, 0, 0);
+    } else if (wave == 1) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q_rsrc, (lds_void *)(st + kQOff), 16,
+                                               (chunk * a.Mp + m0) * 4 + lane * 16, 0, 0, 0);
+    } else if (ZP && wave == 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_void *)(st + kZOff), 4,
+                                               (chunk * (a.N >> 3) + (n0 >> 3)) * 4 + lane * 4, 0, 0, 0);
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = (2 * wave + j) & 3;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void *)(st + kBOff + wave * 2048 + j * 1024), 16,
+                                               b_voff, (chunk * 16 * kTileCols + q * 4 * kTileCols) * 4,
+                                               0, kPolicyStream);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(st + kAOff + (4 * j + wave) * 1024), 16,
+                                               a_voff[j], chunk * kGemmKC * 2, 0, 0);
   };
 
   const uint32_t magic = bf16_magic_pair();
@@ -144,86 +180,83 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  if (ccount > 0) {
-    load_a(cb);
-    load_b(cb, bcur);
-    stage_a(0);
-  }
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < ccount) issue(cb + st, st);
 
+  const int a_row0 = 64 * wm + li;                   // + 16 fm
+  const int s_off = kSOff + (64 * wn + 4 * li) * 2;
+  const int q_off = kQOff + (64 * wm + 4 * lk) * 4;  // + 64 fm
+  const int z_off = kZOff + ((64 * wn + 4 * li) >> 3) * 4;
+  const int z_shift = (4 * li) & 7;                  // 0 or 4: first nibble of the lane's 4 columns
+  const int b_off = kBOff + wn * 4096 + lk * 256 + li * 16;  // + 1024 s
+
+  int stage = 0;
   for (int it = 0; it < ccount; ++it) {
-    const int c = cb + it;
-    const int buf = it & 1;
-    const bool more = it + 1 < ccount;
-    if (more) {
-      load_a(c + 1);
-      load_b(c + 1, bnext);
+    // this wave's copies of the chunk are done once at most the next chunk's
+    // 10 (or 11) copies are outstanding; the barrier then covers every wave
+    if (it + 1 < ccount)
+      wait_vm_then_barrier<10>();
+    else
+      wait_vm_then_barrier<0>();
+    if (it + kStages - 1 < ccount) {
+      int ns = stage + kStages - 1;
+      if (ns >= kStages) ns -= kStages;
+      issue(cb + it + kStages - 1, ns);
     }
-    const unsigned char *abuf = s_a[buf];
+    const unsigned char *sb = s_ring + stage * kStageBytes;
+
+    const u32x2_t sv = lds_read<u32x2_t>(sb, s_off);
+    float sc[4];
+    sc[0] = __uint_as_float(sv[0] << 16);
+    sc[1] = __uint_as_float(sv[0] & 0xFFFF0000u);
+    sc[2] = __uint_as_float(sv[1] << 16);
+    sc[3] = __uint_as_float(sv[1] & 0xFFFF0000u);
+    f32x4_t rs[4];
 #pragma unroll
-    for (int gi = 0; gi < GPC; ++gi) {
-      const int g = c * GPC + gi;
-      // scales (and zero-points) of this lane's 4 columns
-      float sc[4] = {0.f, 0.f, 0.f, 0.f};
-      int zp[4] = {8, 8, 8, 8};
-      if (ncol < a.N) {
-        const size_t si = (size_t)g * a.N + ncol;
-        if ((a.N & 3) == 0) {
-          const uint2 v = *(const uint2 *)(a.S + si);
-          sc[0] = __uint_as_float(v.x << 16);
-          sc[1] = __uint_as_float(v.x & 0xFFFF0000u);
-          sc[2] = __uint_as_float(v.y << 16);
-          sc[3] = __uint_as_float(v.y & 0xFFFF0000u);
-        } else {
+    for (int fm = 0; fm < 4; ++fm) rs[fm] = lds_read<f32x4_t>(sb, q_off + 64 * fm);
+
+    f32x4_t P[4][4];
+    f32x4_t init[4];
+    if constexpr (ZP) {
+      const uint32_t zw = lds_read<uint32_t>(sb, z_off) >> (4 * z_shift);
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
-            if (ncol + f < a.N) sc[f] = __uint_as_float((uint32_t)a.S[si + f] << 16);
-        }
-        if constexpr (ZP) {
-          const uint32_t zw = a.Z[(size_t)g * (a.N >> 3) + (ncol >> 3)];
+      for (int fn = 0; fn < 4; ++fn) {
+        const float bias = -(float)(128 + (int)((zw >> (4 * fn)) & 0xFu));
 #pragma unroll
-          for (int f = 0; f < 4; ++f) zp[f] = (int)((zw >> (4 * (ncol & 7) + 4 * f)) & 0xFu);
-        }
+        for (int fm = 0; fm < 4; ++fm) P[fm][fn] = rs[fm] * bias;
       }
-      // initial accumulators: -(128 + z) * sum_k a_k for the 4 rows each lane holds
-      f32x4_t rs[4];
+    } else {
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-        rs[fm] = *(const f32x4_t *)&s_sum[buf][gi][64 * wm + 16 * fm + 4 * lk];
-      f32x4_t P[4][4];
-#pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 4; ++fn) P[fm][fn] = rs[fm] * (float)(-(128 + zp[fn]));
+      for (int fm = 0; fm < 4; ++fm) init[fm] = rs[fm] * -136.0f;
+    }
 
 #pragma unroll
-      for (int ks = 0; ks < SPG; ++ks) {
-        const int s = gi * SPG + ks;  // k-step within the chunk
-        bf16x8_t bfr[4];
+    for (int s = 0; s < 4; ++s) {
+      const u32x4_t bw = lds_read<u32x4_t>(sb, b_off + 1024 * s);
+      bf16x8_t bfr[4];
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant_word(bcur[s][fn], magic);
+      for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant_word(bw[fn], magic);
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) {
-          const bf16x8_t afr = *(const bf16x8_t *)(abuf + (64 * wm + 16 * fm + li) * kLdsRowBytes +
-                                                   (32 * s + 8 * lk) * 2);
+      for (int fm = 0; fm < 4; ++fm) {
+        const int r = a_row0 + 16 * fm;
+        const bf16x8_t afr = lds_read<bf16x8_t>(sb, kAOff + r * kARow + 16 * ((4 * s + lk) ^ li));
 #pragma unroll
-          for (int fn = 0; fn < 4; ++fn)
+        for (int fn = 0; fn < 4; ++fn) {
+          if (!ZP && s == 0)
+            P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], init[fm], 0, 0, 0);
+          else
             P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], P[fm][fn], 0, 0, 0);
         }
       }
-#pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(sc[fn], P[fm][fn][r], acc[fm][fn][r]);
     }
-    if (more) stage_a(buf ^ 1);
-    __syncthreads();
-    if (more) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bcur[s] = bnext[s];
-    }
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(sc[fn], P[fm][fn][r], acc[fm][fn][r]);
+    stage = stage + 1 == kStages ? 0 : stage + 1;
   }
 
   // ---- epilogue ----
@@ -241,50 +274,63 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
       }
     return;
   }
-
+  if (ncol >= a.N) return;   // N % 8 == 0: a lane's 4 columns are all in or all out
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row_base + 16 * fm + r;
-      if (row >= a.M || ncol >= a.N) continue;
+      if (row >= a.M) continue;
       const size_t o = (size_t)row * a.N + ncol;
       if constexpr (OF == O_BF16) {
-        uint16_t *out = (uint16_t *)a.out;
-        const uint32_t p01 = pack_bf16x2(acc[fm][0][r], acc[fm][1][r]);
-        const uint32_t p23 = pack_bf16x2(acc[fm][2][r], acc[fm][3][r]);
-        if ((a.N & 3) == 0) {
-          *(uint2 *)(out + o) = make_uint2(p01, p23);
-        } else {
-          const uint16_t h[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-            if (ncol + f < a.N) out[o + f] = h[f];
-        }
+        *(u32x2_t *)((uint16_t *)a.out + o) =
+            (u32x2_t){pack_bf16x2(acc[fm][0][r], acc[fm][1][r]), pack_bf16x2(acc[fm][2][r], acc[fm][3][r])};
       } else {
-        float *out = (float *)a.out;
-        if ((a.N & 3) == 0) {
-          *(f32x4_t *)(out + o) = (f32x4_t){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
-        } else {
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-            if (ncol + f < a.N) out[o + f] = acc[fm][f][r];
-        }
+        *(f32x4_t *)((float *)a.out + o) = (f32x4_t){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
       }
     }
 }
 
-template <int OF, bool ZP, int G>
+// ---------------------------------------------------------------------------
+// Activation sums: asum[g][m] = sum_{k in group g} a[m][k] (groups of 128),
+// for m < M; row stride Mp. Each lane adds its 8 values in k order, then the
+// 16 lanes of a group combine in a fixed butterfly. A wave covers 4 groups of
+// one row; a workgroup 16 groups.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void asum_kernel(const uint16_t *__restrict__ A, float *__restrict__ asum, int M,
+                                                  int K, int Mp) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.y;
+  const int g = blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  const bool ok = g < K / 128;
+  float s = 0.f;
+  if (ok) {
+    const u32x4_t v = *(const u32x4_t *)(A + (size_t)m * K + (size_t)g * 128 + 8 * (lane & 15));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s += __uint_as_float(v[j] << 16);
+      s += __uint_as_float(v[j] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+  if (ok && (lane & 15) == 0) asum[(size_t)g * Mp + m] = s;
+}
+
+template <int OF, bool ZP>
 static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
-  gemm_kernel<OF, ZP, G><<<grid, kGemmThreads, 0, st>>>(a);
+  gemm_kernel<OF, ZP><<<grid, kGemmThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-// Only groups of 128 take this path (the dispatcher sends G = 32 to the GEMV).
+// The dispatcher sends only G == 128, K % 128 == 0, N % 8 == 0 here.
 hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t st) {
-  if (G != 128) return hipErrorInvalidValue;
-  if (ofmt == O_BF16) return zp ? go<O_BF16, true, 128>(a, grid, st) : go<O_BF16, false, 128>(a, grid, st);
-  return zp ? go<O_F32, true, 128>(a, grid, st) : go<O_F32, false, 128>(a, grid, st);
+  if (G != 128 || a.K % kGemmKC != 0 || a.N % 8 != 0) return hipErrorInvalidValue;
+  asum_kernel<<<dim3((a.K / 128 + 15) / 16, a.M), 256, 0, st>>>(a.A, a.asum, a.M, a.K, a.Mp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ofmt == O_BF16) return zp ? go<O_BF16, true>(a, grid, st) : go<O_BF16, false>(a, grid, st);
+  return zp ? go<O_F32, true>(a, grid, st) : go<O_F32, false>(a, grid, st);
 }
 
 }  // namespace qg

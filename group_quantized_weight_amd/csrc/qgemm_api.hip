@@ -6,7 +6,8 @@
 // A call enqueues one kernel, or two when K is split: the split kernel writes
 // float32 partials to the workspace and a reduction kernel adds them in the
 // fixed order z = 0..nsplit-1 (the kernel boundary orders the two; no
-// device-wide fences or atomics are used).
+// device-wide fences or atomics are used). The MFMA path adds a pre-pass
+// that writes per-group activation sums to the start of the workspace.
 //
 // Dispatch follows the roofline argument of the page
 // "quantization-and-fused-kernels" (arganzheng.life), section 三.2: at small
@@ -78,8 +79,17 @@ struct Plan {
   int tiles_x = 1, tiles_y = 1;
   int units = 1;          // groups (GEMV) or 128-k chunks (GEMM) along K
   size_t lds = 0;
+  size_t asum = 0;        // MFMA path: bytes of activation sums at the start of the workspace
   size_t ws = 0;
 };
+
+size_t padded_rows(int M) { return ((size_t)M + kGemmBM - 1) / kGemmBM * kGemmBM; }
+
+// MFMA path: float32 activation sums [K/128][Mp], rounded up to 256 bytes.
+size_t gemm_asum_bytes(int M, int K) {
+  const size_t b = (size_t)(K / kGemmKC) * padded_rows(M) * 4;
+  return (b + 255) / 256 * 256;
+}
 
 size_t gemv_lds(const Formats &f, int mb, int G, int ngroups, int nsplit) {
   const int kpw = f.w == W4 ? 8 : 4;
@@ -103,7 +113,8 @@ int balance(int units, int nsplit) {
 int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int force_nsplit, Plan &p) {
   const int cus = device_cus();
   const size_t Np = padded_cols(N);
-  const bool gemm_ok = f.a == A_BF16 && G == 128 && K % kGemmKC == 0;
+  const bool gemm_ok = f.a == A_BF16 && G == 128 && K % kGemmKC == 0 && N % 8 == 0 && M <= 65535 &&
+                       gemm_asum_bytes(M, K) <= (size_t)INT_MAX;
   int path = force_path;
   if (path == QG_PATH_AUTO) path = (M > 8 && gemm_ok) ? QG_PATH_GEMM : QG_PATH_GEMV;
   if (path == QG_PATH_GEMM && !gemm_ok) return QG_EUNSUPPORTED;
@@ -141,7 +152,8 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
     p.lds = gemv_lds(f, p.mb, G, p.units, ns);
   }
   p.nsplit = ns;
-  p.ws = p.nsplit > 1 ? (size_t)p.nsplit * M * Np * 4 : 0;
+  p.asum = path == QG_PATH_GEMM ? gemm_asum_bytes(M, K) : 0;
+  p.ws = p.asum + (p.nsplit > 1 ? (size_t)p.nsplit * M * Np * 4 : 0);
   return QG_OK;
 }
 
@@ -232,7 +244,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     if (!aligned16(workspace)) return QG_EALIGN;
   }
   hipStream_t s = (hipStream_t)stream;
-  float *partial = p.nsplit > 1 ? (float *)workspace : nullptr;
+  float *partial = p.nsplit > 1 ? (float *)((char *)workspace + p.asum) : nullptr;
   const int Np = (int)padded_cols(N);
   hipError_t e;
   if (p.path == QG_PATH_GEMV) {
@@ -257,7 +269,8 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
     a.out = out;
     a.partial = partial;
-    a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np;
+    a.asum = (float *)workspace;
+    a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np; a.Mp = (int)padded_rows(M);
     a.nchunks = K / kGemmKC;
     a.nsplit = p.nsplit;
     e = launch_gemm(f.o, has_zp != 0, group, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), s);

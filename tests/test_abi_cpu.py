@@ -110,7 +110,11 @@ def test_plan_is_pure_and_consistent(M, N, K, G, prec):
     path, ns, ws = a
     assert 1 <= ns <= K // G
     assert ws == qg.lib().qgemm_workspace_bytes(M, N, K, G, prec)
-    assert (ws == 0) == (ns == 1)
+    if path == qg.PATH_GEMV:
+        assert (ws == 0) == (ns == 1)
+    else:  # activation sums [K/128][M rounded up to 128] float32, then the split partials
+        asum = -(-(K // 128) * (-(-M // 128) * 128) * 4 // 256) * 256
+        assert ws == asum + (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)
     if prec in (1, 6) and M > 8:
         assert path == qg.PATH_GEMM
     if M <= 8:
@@ -124,5 +128,9 @@ def test_forced_plans():
         assert (ws == 0) == (got == 1)
     path, ns, ws = qg.plan(300, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMM, 3)
     assert path == qg.PATH_GEMM and ns == 3
+    # the MFMA path needs N % 8 == 0; automatic dispatch sends other N to the GEMV
+    with pytest.raises(qg.QGemmError):
+        qg.plan(300, 1001, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMM, 0)
+    assert qg.plan(300, 1001, 1024, 128, qg.W4_A_BF16)[0] == qg.PATH_GEMV
     path, ns, ws = qg.plan(300, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMV, 0)
     assert path == qg.PATH_GEMV

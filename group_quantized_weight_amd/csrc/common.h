@@ -24,8 +24,9 @@ constexpr int kTileCols = 64;                // packed layout: columns per tile
 // fewer workgroups fit per compute unit.)
 __host__ __device__ constexpr int gemv_waves(int) { return 4; }
 
-// GEMM path: one workgroup = 4 waves (2 x 2), tile 128 x 128, K chunks of 128.
-constexpr int kGemmThreads = 256;
+// GEMM path: one workgroup = 8 waves (two halves of 2 x 2 waves that split
+// the workgroup's chunks), tile 128 x 128, K chunks of 128.
+constexpr int kGemmThreads = 512;
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmKC = 128;

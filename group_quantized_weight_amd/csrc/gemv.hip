@@ -41,7 +41,9 @@
 // fixed order (lane shuffles, then LDS), so results are reproducible.
 //
 // Latency hiding comes from many resident waves: each wave streams about one
-// batch of loads and computes while the other waves' loads are in flight.
+// batch of loads and computes while the other waves' loads are in flight;
+// single-row bf16 decode also issues its next (small) batch before computing
+// the current one.
 //
 // Latency: each thread issues its activation loads first and its first batch
 // of weight loads next, then writes the activations to LDS; since vector
@@ -189,8 +191,16 @@ void gemv_kernel(GemvArgs a) {
   constexpr int RPG = G / KPW;                        // word-rows per group: 4, 8, 16 or 32
   constexpr int IPG = RPG / 4;                        // wave loads per group (4 rows each)
   constexpr int BMAX = BatchRows<MB>::value;
-  constexpr int GPB = IPG >= BMAX ? 1 : (BMAX / IPG < 8 ? BMAX / IPG : 8);  // groups per batch
+  // Single-row bf16 decode issues the next small batch (4 loads) before it
+  // computes the current one (NB = 2 register slots); the other
+  // configurations, heavier in vector ALU work per byte, issue one large
+  // batch and compute it before issuing the next (NB = 1). Each measured
+  // best for its cases on MI355X.
+  constexpr bool kSmallBatches = MB == 1 && AF == A_BF16;
+  constexpr int GPB = kSmallBatches ? (IPG >= 4 ? 1 : 4 / IPG)
+                                    : (IPG >= BMAX ? 1 : (BMAX / IPG < 8 ? BMAX / IPG : 8));  // groups per batch
   constexpr int IPB = GPB * IPG;                      // wave loads per batch
+  constexpr int NB = kSmallBatches ? 2 : 1;           // batch slots in registers
   constexpr int SMAX = 2;                             // activation rows staged per thread up front
   constexpr bool INT = AF == A_I8;
   constexpr int bias = AF == A_BF16 ? 128 : ((AF == A_F32 && WF == W8) ? 128 : 0);
@@ -238,40 +248,47 @@ void gemv_kernel(GemvArgs a) {
       (void *)a.Z, (short)0, ZP ? a.ngroups * (a.N >> 3) * 4 : 0, kBufferWord3);
   const int z_voff = (scol >> 3) * 4;
   using SRaw = typename std::conditional<SF == S_BF16, u32x2_v, u32x4_v>::type;
-  u32x4_v wv[IPB];
-  SRaw sv[GPB];
-  uint32_t zv[GPB];
-  // a batch past the end of the wave's range re-reads its last group (valid,
-  // cached addresses) so the issue is straight-line; compute skips it
-  auto issue_batch = [&](int gfirst) {  // local group index of the batch's first group
+  u32x4_v wv[NB][IPB];
+  SRaw sv[NB][GPB];
+  uint32_t zv[NB][GPB];
+  // Issue is straight-line: a group past the end of the wave's range uses
+  // the last group's offsets, and a batch wholly past the end sets the top
+  // bit of the per-lane offset, which the buffer's range check turns into a
+  // zero result without a memory access (every resource here has at most
+  // INT_MAX bytes). Compute skips both.
+  auto issue_batch = [&](int gfirst, int slot) {  // local group index of the batch's first group
     const int glast = wgc > 0 ? wg0 + wgc - 1 : 0;
+    const int dead = gfirst > glast ? (int)0x80000000u : 0;
 #pragma unroll
     for (int gi = 0; gi < GPB; ++gi) {
       const int gl = gfirst + gi < glast ? gfirst + gi : glast;
 #pragma unroll
       for (int i = 0; i < IPG; ++i)
-        wv[gi * IPG + i] = __builtin_bit_cast(
-            u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff, ((gb + gl) * RPG + 4 * i) * kTileCols * 4,
+        wv[slot][gi * IPG + i] = __builtin_bit_cast(
+            u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff | dead,
+                                                           ((gb + gl) * RPG + 4 * i) * kTileCols * 4,
                                                            kCachePolicyStream));
       // without 4-aligned rows (N % 4 != 0) the scales are read one by one at
       // use; this load then reads the first element and is ignored
       const int s_soff = vec_s ? (gb + gl) * a.N * SB : 0;
       if constexpr (SF == S_BF16)
-        sv[gi] = __builtin_bit_cast(u32x2_v, __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, s_voff, s_soff, 0));
+        sv[slot][gi] =
+            __builtin_bit_cast(u32x2_v, __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, s_voff | dead, s_soff, 0));
       else
-        sv[gi] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, s_voff, s_soff, 0));
+        sv[slot][gi] =
+            __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, s_voff | dead, s_soff, 0));
       if constexpr (ZP)
-        zv[gi] = __builtin_amdgcn_raw_buffer_load_b32(z_rsrc, z_voff, (gb + gl) * (a.N >> 3) * 4, 0);
+        zv[slot][gi] = __builtin_amdgcn_raw_buffer_load_b32(z_rsrc, z_voff | dead, (gb + gl) * (a.N >> 3) * 4, 0);
     }
   };
-  auto scales_of = [&](int gi, int gl, float *s) {
+  auto scales_of = [&](int slot, int gi, int gl, float *s) {
     if (vec_s) {
       if constexpr (SF == S_BF16) {
-        s[0] = bf16_lo(sv[gi][0]); s[1] = bf16_hi(sv[gi][0]);
-        s[2] = bf16_lo(sv[gi][1]); s[3] = bf16_hi(sv[gi][1]);
+        s[0] = bf16_lo(sv[slot][gi][0]); s[1] = bf16_hi(sv[slot][gi][0]);
+        s[2] = bf16_lo(sv[slot][gi][1]); s[3] = bf16_hi(sv[slot][gi][1]);
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) s[c] = __uint_as_float(sv[gi][c]);
+        for (int c = 0; c < 4; ++c) s[c] = __uint_as_float(sv[slot][gi][c]);
       }
     } else {  // N not a multiple of 4: one scale at a time (not prefetched)
       const size_t si = (size_t)(gb + gl) * a.N + ncol;
@@ -301,7 +318,10 @@ void gemv_kernel(GemvArgs a) {
     const size_t k = st_ok[s] ? (size_t)(m0 + m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)m0 * a.K;
     load_row<WF, AF>(a.A, k, st0[s], st1[s]);
   }
-  issue_batch(wg0);  // a wave without groups re-reads valid addresses and computes nothing
+  // the first batch (NB - 1 batches with NB > 1); a wave without groups
+  // issues dead batches and computes nothing
+#pragma unroll
+  for (int b = 0; b < (NB > 1 ? NB - 1 : 1); ++b) issue_batch(wg0 + b * GPB, b);
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
     const int idx = threadIdx.x + kGemvThreads * s;
@@ -329,175 +349,185 @@ void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[m][c] = 0.f;
 
-  for (int gg = 0; gg < wgc; gg += GPB) {
-    if (gg > 0) issue_batch(wg0 + gg);
+  // batch b sits in slot b % NB
+  const int nbatch = (wgc + GPB - 1) / GPB;
+  for (int b0 = 0; b0 < nbatch; b0 += NB) {
 #pragma unroll
-    for (int gi = 0; gi < GPB; ++gi) {
-      if (gg + gi >= wgc) break;
-      const int gl = wg0 + gg + gi;
-      float pf[MB][4];
-      int pi[MB][4];
-      uint32_t cs[MB];  // this lane's share of the group's activation sum
+    for (int u = 0; u < NB; ++u) {
+      const int gg = (b0 + u) * GPB;  // first group of the batch, relative to wg0
+      if (gg >= wgc) break;
+      if constexpr (NB > 1)
+        issue_batch(wg0 + gg + (NB - 1) * GPB, (u + NB - 1) % NB);  // into the slot computed last
+      else if (gg > 0)
+        issue_batch(wg0 + gg, 0);
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        cs[m] = 0;
+      for (int gi = 0; gi < GPB; ++gi) {
+        if (gg + gi >= wgc) break;
+        const int gl = wg0 + gg + gi;
+        float pf[MB][4];
+        int pi[MB][4];
+        uint32_t cs[MB];  // this lane's share of the group's activation sum
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          cs[m] = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            pf[m][c] = 0.f;
+            pi[m][c] = 0;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < IPG; ++i) {
+          const u32x4_v wq = wv[u][gi * IPG + i];
+          const int lr = gl * RPG + 4 * i + lk;  // local word-row
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const uint32_t rs = s_rsum[m * rows + lr];
+            cs[m] = INT ? (uint32_t)((int)cs[m] + (int)rs) : __float_as_uint(__uint_as_float(cs[m]) + __uint_as_float(rs));
+          }
+          const unsigned char *arow = s_act + (size_t)lr * AB;
+          if constexpr (AF == A_BF16) {
+            uint32_t x[4][4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t w = wq[c];
+              x[c][0] = (w & 0x000F000Fu) | magic;
+              x[c][1] = ((w >> 4) & 0x000F000Fu) | magic;
+              x[c][2] = ((w >> 8) & 0x000F000Fu) | magic;
+              x[c][3] = ((w >> 12) & 0x000F000Fu) | magic;
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+              const u32x4_v av = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                float p = pf[m][c];
+                p = dot2_bf16(x[c][0], av[0], p);
+                p = dot2_bf16(x[c][1], av[1], p);
+                p = dot2_bf16(x[c][2], av[2], p);
+                p = dot2_bf16(x[c][3], av[3], p);
+                pf[m][c] = p;
+              }
+            }
+          } else if constexpr (AF == A_F32 && WF == W4) {
+            float q[4][8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t lo = wq[c] & 0x0F0F0F0Fu, hi = (wq[c] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                q[c][j] = (float)((lo >> (8 * j)) & 0xFFu);
+                q[c][4 + j] = (float)((hi >> (8 * j)) & 0xFFu);
+              }
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+              const u32x4_v a0 = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
+              const u32x4_v a1 = *(const u32x4_v *)(arow + (size_t)m * rows * AB + 16);
+              const float av[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
+                                   __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
+                                   __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                float p = pf[m][c];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) p = __builtin_fmaf(q[c][j], av[j], p);
+                pf[m][c] = p;
+              }
+            }
+          } else if constexpr (AF == A_F32 && WF == W8) {
+            float q[4][4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t u = wq[c] ^ 0x80808080u;  // int8 code + 128 as an unsigned byte
+#pragma unroll
+              for (int j = 0; j < 4; ++j) q[c][j] = (float)((u >> (8 * j)) & 0xFFu);
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+              const u32x4_v a0 = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                float p = pf[m][c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p = __builtin_fmaf(q[c][j], __uint_as_float(a0[j]), p);
+                pf[m][c] = p;
+              }
+            }
+          } else if constexpr (AF == A_I8 && WF == W4) {
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              lo[c] = wq[c] & 0x0F0F0F0Fu;
+              hi[c] = (wq[c] >> 4) & 0x0F0F0F0Fu;
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+              const uint2 av = *(const uint2 *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                int p = pi[m][c];
+                p = __builtin_amdgcn_sdot4((int)lo[c], (int)av.x, p, false);
+                p = __builtin_amdgcn_sdot4((int)hi[c], (int)av.y, p, false);
+                pi[m][c] = p;
+              }
+            }
+          } else {  // A_I8, W8
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+              const uint32_t av = *(const uint32_t *)(arow + (size_t)m * rows * AB);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) pi[m][c] = __builtin_amdgcn_sdot4((int)wq[c], (int)av, pi[m][c], false);
+            }
+          }
+        }
+
+        // ---- group epilogue: remove the code bias, apply the group scale ----
+        float s[4];
+        scales_of(u, gi, gl, s);
+        int zc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          pf[m][c] = 0.f;
-          pi[m][c] = 0;
+          int zz = WF == W8 ? 0 : 8;
+          if constexpr (ZP) zz = (int)((zv[u][gi] >> (4 * ((ncol & 7) + c))) & 0xFu);
+          zc[c] = bias + zz;
         }
-      }
-#pragma unroll
-      for (int i = 0; i < IPG; ++i) {
-        const u32x4_v wq = wv[gi * IPG + i];
-        const int lr = gl * RPG + 4 * i + lk;  // local word-row
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const uint32_t rs = s_rsum[m * rows + lr];
-          cs[m] = INT ? (uint32_t)((int)cs[m] + (int)rs) : __float_as_uint(__uint_as_float(cs[m]) + __uint_as_float(rs));
-        }
-        const unsigned char *arow = s_act + (size_t)lr * AB;
-        if constexpr (AF == A_BF16) {
-          uint32_t x[4][4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t w = wq[c];
-            x[c][0] = (w & 0x000F000Fu) | magic;
-            x[c][1] = ((w >> 4) & 0x000F000Fu) | magic;
-            x[c][2] = ((w >> 8) & 0x000F000Fu) | magic;
-            x[c][3] = ((w >> 12) & 0x000F000Fu) | magic;
-          }
+        if constexpr (INT) {
+          // the whole group's integer dot: add the 4 lanes (rows mod 4) sharing these columns
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
-            const u32x4_v av = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
+            int t = (int)cs[m];
+            t += __shfl_xor(t, 16);
+            t += __shfl_xor(t, 32);
+            cs[m] = (uint32_t)t;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              float p = pf[m][c];
-              p = dot2_bf16(x[c][0], av[0], p);
-              p = dot2_bf16(x[c][1], av[1], p);
-              p = dot2_bf16(x[c][2], av[2], p);
-              p = dot2_bf16(x[c][3], av[3], p);
-              pf[m][c] = p;
+              int v = pi[m][c];
+              v += __shfl_xor(v, 16);
+              v += __shfl_xor(v, 32);
+              pi[m][c] = v;
             }
           }
-        } else if constexpr (AF == A_F32 && WF == W4) {
-          float q[4][8];
+          if (lk == 0) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t lo = wq[c] & 0x0F0F0F0Fu, hi = (wq[c] >> 4) & 0x0F0F0F0Fu;
+            for (int m = 0; m < MB; ++m) {
+              const float asc = (m0 + m < a.M) ? a.a_scale[(size_t)(m0 + m) * a.ngroups + gb + gl] : 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              q[c][j] = (float)((lo >> (8 * j)) & 0xFFu);
-              q[c][4 + j] = (float)((hi >> (8 * j)) & 0xFFu);
+              for (int c = 0; c < 4; ++c) {
+                const int d = pi[m][c] - zc[c] * (int)cs[m];
+                acc[m][c] = __builtin_fmaf(asc * s[c], (float)d, acc[m][c]);
+              }
             }
           }
+        } else {
 #pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const u32x4_v a0 = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
-            const u32x4_v a1 = *(const u32x4_v *)(arow + (size_t)m * rows * AB + 16);
-            const float av[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
-                                 __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
-                                 __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+          for (int m = 0; m < MB; ++m)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              float p = pf[m][c];
-#pragma unroll
-              for (int j = 0; j < 8; ++j) p = __builtin_fmaf(q[c][j], av[j], p);
-              pf[m][c] = p;
+              const float d = pf[m][c] - (float)zc[c] * __uint_as_float(cs[m]);
+              acc[m][c] = __builtin_fmaf(s[c], d, acc[m][c]);
             }
-          }
-        } else if constexpr (AF == A_F32 && WF == W8) {
-          float q[4][4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t u = wq[c] ^ 0x80808080u;  // int8 code + 128 as an unsigned byte
-#pragma unroll
-            for (int j = 0; j < 4; ++j) q[c][j] = (float)((u >> (8 * j)) & 0xFFu);
-          }
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const u32x4_v a0 = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              float p = pf[m][c];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) p = __builtin_fmaf(q[c][j], __uint_as_float(a0[j]), p);
-              pf[m][c] = p;
-            }
-          }
-        } else if constexpr (AF == A_I8 && WF == W4) {
-          uint32_t lo[4], hi[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            lo[c] = wq[c] & 0x0F0F0F0Fu;
-            hi[c] = (wq[c] >> 4) & 0x0F0F0F0Fu;
-          }
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const uint2 av = *(const uint2 *)(arow + (size_t)m * rows * AB);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              int p = pi[m][c];
-              p = __builtin_amdgcn_sdot4((int)lo[c], (int)av.x, p, false);
-              p = __builtin_amdgcn_sdot4((int)hi[c], (int)av.y, p, false);
-              pi[m][c] = p;
-            }
-          }
-        } else {  // A_I8, W8
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const uint32_t av = *(const uint32_t *)(arow + (size_t)m * rows * AB);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) pi[m][c] = __builtin_amdgcn_sdot4((int)wq[c], (int)av, pi[m][c], false);
-          }
         }
-      }
-
-      // ---- group epilogue: remove the code bias, apply the group scale ----
-      float s[4];
-      scales_of(gi, gl, s);
-      int zc[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        int zz = WF == W8 ? 0 : 8;
-        if constexpr (ZP) zz = (int)((zv[gi] >> (4 * ((ncol & 7) + c))) & 0xFu);
-        zc[c] = bias + zz;
-      }
-      if constexpr (INT) {
-        // the whole group's integer dot: add the 4 lanes (rows mod 4) sharing these columns
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          int t = (int)cs[m];
-          t += __shfl_xor(t, 16);
-          t += __shfl_xor(t, 32);
-          cs[m] = (uint32_t)t;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            int v = pi[m][c];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            pi[m][c] = v;
-          }
-        }
-        if (lk == 0) {
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const float asc = (m0 + m < a.M) ? a.a_scale[(size_t)(m0 + m) * a.ngroups + gb + gl] : 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int d = pi[m][c] - zc[c] * (int)cs[m];
-              acc[m][c] = __builtin_fmaf(asc * s[c], (float)d, acc[m][c]);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float d = pf[m][c] - (float)zc[c] * __uint_as_float(cs[m]);
-            acc[m][c] = __builtin_fmaf(s[c], d, acc[m][c]);
-          }
       }
     }
   }

@@ -328,8 +328,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 // for m < M; row stride Mp. One wave per row: lane l reads 16 bytes of each
 // 1 KiB block of the row (block j covers groups 4j .. 4j+3; lanes 16i .. 16i+15
 // hold group 4j + i), adds its 8 values in k order, and the 16 lanes of a
-// group combine in a fixed butterfly. Up to 8 blocks are loaded before any
-// is added, so every lane keeps 8 loads in flight.
+// group (one DPP row) combine in a fixed order of row rotations. Up to 8
+// blocks are loaded before any is added, so every lane keeps 8 loads in
+// flight.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void asum_kernel(const uint16_t *__restrict__ A, float *__restrict__ asum, int M,
                                                   int K, int Mp) {
@@ -357,8 +358,12 @@ __global__ __launch_bounds__(256) void asum_kernel(const uint16_t *__restrict__ 
         s += __uint_as_float(v[u][q] << 16);
         s += __uint_as_float(v[u][q] & 0xFFFF0000u);
       }
-#pragma unroll
-      for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+      // fixed-order sum over the 16 lanes of the group with DPP row rotations
+      // (lane 0 of the row ends with ((s0 + s8) + (s4 + s12)) + ...)
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x128, 0xF, 0xF, false));  // row_ror:8
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x124, 0xF, 0xF, false));  // row_ror:4
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x122, 0xF, 0xF, false));  // row_ror:2
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x121, 0xF, 0xF, false));  // row_ror:1
       if (g < ngroups && (lane & 15) == 0) asum[(size_t)g * Mp + m] = s;
     }
   }

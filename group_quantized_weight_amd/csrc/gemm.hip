@@ -209,25 +209,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn) bias[fn] = -(float)(128 + (int)((zw >> (4 * fn)) & 0xFu));
     }
+    // The 16 activation fragments of the chunk (k-step s, row tile fm) are
+    // read from LDS two fragments ahead of their MFMAs, so the read latency
+    // is covered by the MFMAs of the two previous fragments.
+    auto a_frag = [&](int q) {
+      const int s = q >> 2, fm = q & 3;
+      return lds_read<bf16x8_t>(sb, kAOff + (a_row0 + 16 * fm) * kARow + 16 * ((4 * s + lk) ^ li));
+    };
+    bf16x8_t af[3];
+    af[0] = a_frag(0);
+    af[1] = a_frag(1);
+    bf16x8_t bfr[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t bfr[4];
+    for (int q = 0; q < 16; ++q) {
+      const int s = q >> 2, fm = q & 3;
+      if (q + 2 < 16) af[(q + 2) % 3] = a_frag(q + 2);
+      if (fm == 0) {
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant_word(bw[s][fn], magic);
+        for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant_word(bw[s][fn], magic);
+      }
+      const bf16x8_t afr = af[q % 3];
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm) {
-        const int r = a_row0 + 16 * fm;
-        const bf16x8_t afr = lds_read<bf16x8_t>(sb, kAOff + r * kARow + 16 * ((4 * s + lk) ^ li));
+      for (int fn = 0; fn < 4; ++fn) {
+        if (s == 0) {
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) {
-          if (s == 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[fm][fn][q] = __builtin_fmaf(sc[fn], P[fm][fn][q], acc[fm][fn][q]);
-            const f32x4_t init = rs[fm] * bias[fn];
-            P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], init, 0, 0, 0);
-          } else {
-            P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], P[fm][fn], 0, 0, 0);
-          }
+          for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(sc[fn], P[fm][fn][r], acc[fm][fn][r]);
+          const f32x4_t init = rs[fm] * bias[fn];
+          P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], init, 0, 0, 0);
+        } else {
+          P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], P[fm][fn], 0, 0, 0);
         }
       }
     }

@@ -24,9 +24,9 @@ constexpr int kTileCols = 64;                // packed layout: columns per tile
 // fewer workgroups fit per compute unit.)
 __host__ __device__ constexpr int gemv_waves(int) { return 4; }
 
-// GEMM path: one workgroup = 8 waves (two halves of 2 x 2 waves that split
-// the workgroup's chunks), tile 128 x 128, K chunks of 128.
-constexpr int kGemmThreads = 512;
+// GEMM path: one workgroup = 4 waves (each 128 x 32), tile 128 x 128, K
+// chunks of 128.
+constexpr int kGemmThreads = 256;
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmKC = 128;
@@ -50,7 +50,7 @@ struct GemmArgs {
   const uint32_t *Z;       // [K/G][N/8] or null
   void *out;               // [M][N] bf16 or float32 (nsplit == 1)
   float *partial;          // [nsplit][M][Np] (nsplit > 1)
-  float *asum;             // [K/128][Mp] activation sums per group (workspace)
+  float *asum;             // [K/128][Mp] activation sums per group, x -136 without zero-points (workspace)
   int M, N, K, G, Np, Mp;  // Mp = M rounded up to kGemmBM
   int nchunks, nsplit;     // K / kGemmKC chunks split into nsplit slices
 };

@@ -7,10 +7,11 @@
 // instruction in bf16 with float32 accumulation; and the multi-stage
 // global-to-shared pipeline of its section 三.3, item 2):
 //   - workgroup tile 128 x 128, K in chunks of 128 = one group; 8 waves in
-//     two halves of 2 x 2 (each wave 64 x 64 = 4 x 4 tiles of
-//     v_mfma_f32_16x16x32_bf16). The halves take alternate chunks of the
-//     workgroup's K-range, so each SIMD runs two waves; at the end half 1
-//     hands its accumulators to half 0 through LDS;
+//     two halves of 4 (each wave 128 rows x 32 columns = 8 x 2 tiles of
+//     v_mfma_f32_16x16x32_bf16, so each dequantized weight fragment feeds 8
+//     MFMAs). The halves take alternate chunks of the workgroup's K-range,
+//     so each SIMD runs two waves; at the end half 1 hands its accumulators
+//     to half 0 through LDS;
 //   - the chunk's activation tile, scales, zero-points and activation sums
 //     are copied by buffer loads straight into LDS (no registers on the way),
 //     into a ring of 4 stages (two chunks in use, two in flight). Each wave
@@ -19,12 +20,12 @@
 //   - the activation tile's 16-byte pieces are XOR-swizzled with the row
 //     index, so the MFMA fragment reads of 16 rows hit 16 different 4-bank
 //     groups; rows past M are clamped to row M-1 (their results are dropped);
-//   - weights: each lane loads 16 bytes of packed words (4 adjacent columns x
+//   - weights: each lane loads 8 bytes of packed words (2 adjacent columns x
 //     8 k) into registers one chunk ahead, and turns each word into four bf16
 //     pairs (128 + q) with one and-or per pair (bf16 magic number 0x4300,
-//     section 二.4 of the same page); the four columns feed the four MFMA
+//     section 二.4 of the same page); the two columns feed the two MFMA
 //     column tiles of the wave, so MFMA column j of tile f is physical column
-//     n + 4j + f;
+//     n + 2j + f;
 //   - per group, the MFMA accumulates sum_k a_k (128 + q_k) on top of the
 //     initial value -(128 + z) * sum_k a_k, which gives sum_k a_k (q_k - z);
 //     the group's scale is then applied in float32 (acc += s * P), the
@@ -49,13 +50,12 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_g;
 typedef __attribute__((ext_vector_type(2))) float f32x2_g;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One LDS stage holds one chunk's operands that every wave of a half shares:
+// One LDS stage holds the operands of one chunk that all waves share:
 // [activations 128 x 256 B][scales 128 x 2 B][activation sums 128 x 4 B]
 // [zero-points 16 x 4 B]. Each small slot is as large as one wave-wide copy
 // writes (lanes past the useful part copy neighbouring data into the slot's
 // tail, never read). The packed weights go straight to registers.
-constexpr int kHalves = 2;                           // the workgroup's K-split
-constexpr int kStages = 4;                           // 2 chunks in use, 2 in flight
+constexpr int kStages = 3;                           // 1 chunk in use, 2 in flight
 constexpr int kARow = kGemmKC * 2;                   // 256 B per activation row
 constexpr int kAOff = 0;
 constexpr int kSOff = kAOff + kGemmBM * kARow;       // 32 KiB
@@ -64,13 +64,15 @@ constexpr int kZOff = kQOff + 1024;
 constexpr int kStageBytes = kZOff + 256;             // 35072
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kPolicyStream = 2;                     // non-temporal
-static_assert(kStages * kStageBytes >= 4 * 64 * 64 * 4, "the ring also holds one half's accumulators");
 
-// Wait for this wave's outstanding global loads (including the copies into
-// LDS) and LDS reads, then the workgroup barrier; the memory clobber keeps
-// the compiler from moving memory accesses across it.
-__device__ __forceinline__ void wait_all_then_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Wait until at most N of this wave's global loads (including the copies
+// into LDS) are outstanding and its LDS reads are done, then the workgroup
+// barrier; the memory clobber keeps the compiler from moving memory
+// accesses across it. Loads complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -102,240 +104,233 @@ __device__ __forceinline__ T lds_read(const unsigned char *base, int off) {
   return *(const T *)(base + off);
 }
 
-// 8 waves: two halves of 4 (2 x 2, each wave 64 x 64 of the tile). Half h
-// takes the chunks cb + h, cb + h + 2, ... of the workgroup's K-slice, so
-// two waves share each SIMD and one's MFMAs cover the other's waits. At the
-// end, half 1 hands its accumulators to half 0 through LDS, which adds them
-// (half 0 + half 1, a fixed order) and writes the tile.
+// 4 waves, one per SIMD: wave w owns all 128 rows and the 32 columns
+// n0 + 32 w .. +31 of the tile (8 x 2 MFMA tiles), so a weight fragment is
+// dequantized once and feeds 8 MFMAs.
 template <int OF, bool ZP>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) unsigned char s_ring[kStages * kStageBytes];
+  constexpr int FM = 8, FN = 2;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int half = wave >> 2, qw = wave & 3;           // qw: wave within its half
-  const int wm = qw >> 1, wn = qw & 1;
   const int li = lane & 15, lk = lane >> 4;
   const int m0 = blockIdx.y * kGemmBM;
   const int n0 = blockIdx.x * kGemmBN;
-  const int ncol = n0 + 64 * wn + 4 * li;   // this lane's 4 columns (one per column tile)
+  const int cw = 32 * wave + 2 * li;                   // this lane's 2 columns, within the tile
+  const int ncol = n0 + cw;
 
   int cb, ccount;
   split_range(a.nchunks, a.nsplit, blockIdx.z, cb, ccount);
 
   const int R = a.K / 8;
+  // activation rows past M read zeros through the range check (the row
+  // offset is in the VGPR operand; the chunk offset in the SGPR one stays
+  // inside a valid row)
+  const int a_rows = a.M - m0 < kGemmBM ? a.M - m0 : kGemmBM;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.A + (size_t)m0 * a.K), (short)0, 0x7FFFFFFF, kBufWord3);
+      (void *)(a.A + (size_t)m0 * a.K), (short)0, a_rows * a.K * 2, kBufWord3);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.W + (size_t)(n0 / kTileCols) * R * kTileCols), (short)0, 0x7FFFFFFF, kBufWord3);
+      (void *)(a.W + (size_t)(n0 / kTileCols) * R * kTileCols), (short)0, 2 * R * kTileCols * 4, kBufWord3);
   const __amdgpu_buffer_rsrc_t s_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void *)a.S, (short)0, a.nchunks * a.N * 2, kBufWord3);
   const __amdgpu_buffer_rsrc_t q_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void *)a.asum, (short)0, a.nchunks * a.Mp * 4, kBufWord3);
   const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)a.Z, (short)0, ZP ? a.nchunks * (a.N >> 3) * 4 : 0, kBufWord3);
+  // Every load is issued unconditionally (straight-line code, so the
+  // compiler counts the loads in flight exactly); a load for a chunk past
+  // the slice sets the top bit of its VGPR offset, which the range check of
+  // the buffer (every resource here has at most INT_MAX bytes) turns into a
+  // zero result without a memory access. Such copies write zeros into a
+  // stage no later chunk uses.
+  constexpr int kDead = (int)0x80000000u;
 
-  // activations: copy j of wave qw writes LDS bytes (4j + qw) KiB of the
-  // tile: pieces p = 64 (4j + qw) + lane; piece p is row p/16, physical
-  // slot p%16, holding logical 16-byte chunk (p%16) ^ (row%16) of the row.
-  int a_voff[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int p = (4 * j + qw) * 64 + lane;
-    const int r = p >> 4, c = (p & 15) ^ (r & 15);
-    const int row = min(m0 + r, a.M - 1) - m0;
-    a_voff[j] = row * (a.K * 2) + c * 16;
-  }
-  // weights: per k-step s, word-row 4s + lk of the chunk, columns 4 li .. +3
-  // of the wave's 64-column tile (a wave reads 1 KiB of contiguous memory)
-  const int b_voff = wn * R * 256 + lk * 256 + li * 16;
+  // activations: copy j of wave w writes LDS bytes (4j + w) KiB of the tile:
+  // pieces p = 64 (4j + w) + lane; piece p is row p/16 = 16 j + r0, physical
+  // slot p%16, holding logical 16-byte chunk (p%16) ^ (row%16) of the row
+  // (row%16 = r0%16 does not depend on j).
+  const int r0 = 4 * wave + lk;
+  const int a_voff0 = r0 * (a.K * 2) + ((lane & 15) ^ (r0 & 15)) * 16;
+  const int a_vstep = 16 * a.K * 2;          // + j rows of 16
+  // weights: per k-step s, word-row 4s + lk of the chunk and the lane's two
+  // adjacent columns (8 bytes; 16 lanes read a 128-byte row segment). MFMA
+  // column j of tile f is column n0 + 32 w + 2j + f.
+  const int b_voff = ((cw >> 6) * R * kTileCols + lk * kTileCols + (cw & 63)) * 4;
 
-  // The copies of a chunk into LDS, issued by the 4 waves of the half that
-  // uses it. The small copies read past their useful part and, at the last
-  // chunk, past the end of their array: those lanes rely on the buffer's
-  // range check (which returns zeros), so the whole offset is in the VGPR
-  // operand (the SGPR offset is not range-checked).
-  auto issue = [&](int chunk, int stage) {
-    unsigned char *st = s_ring + stage * kStageBytes;
-    if (qw == 0) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void *)(st + kSOff), 16,
-                                               (chunk * a.N + n0) * 2 + lane * 16, 0, 0, 0);
-    } else if (qw == 1) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(q_rsrc, (lds_void *)(st + kQOff), 16,
-                                               (chunk * a.Mp + m0) * 4 + lane * 16, 0, 0, 0);
-    } else if (ZP && qw == 2) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_void *)(st + kZOff), 4,
-                                               (chunk * (a.N >> 3) + (n0 >> 3)) * 4 + lane * 4, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(st + kAOff + (4 * j + qw) * 1024), 16,
-                                               a_voff[j], chunk * kGemmKC * 2, 0, 0);
+  auto load_b = [&](int chunk, int s, int dead) {
+    return __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, b_voff | dead, (chunk * 16 + 4 * s) * kTileCols * 4,
+                                                      kPolicyStream));
   };
-  auto load_b = [&](int chunk, u32x4_t *dst) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      dst[s] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_voff, (chunk * 16 + 4 * s) * 256, kPolicyStream));
+  // The small copies read past their useful part and, at the last chunk,
+  // past the end of their array: those lanes rely on the buffer's range
+  // check (which returns zeros), so the whole offset is in the VGPR operand
+  // (the SGPR offset is not range-checked).
+  auto copy_small = [&](int chunk, int stage, int dead) {
+    unsigned char *st = s_ring + stage * kStageBytes;
+    if (wave == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void *)(st + kSOff), 16,
+                                               ((chunk * a.N + n0) * 2 + lane * 16) | dead, 0, 0, 0);
+    } else if (wave == 1) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q_rsrc, (lds_void *)(st + kQOff), 16,
+                                               ((chunk * a.Mp + m0) * 4 + lane * 16) | dead, 0, 0, 0);
+    } else if (ZP && wave == 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_void *)(st + kZOff), 4,
+                                               ((chunk * (a.N >> 3) + (n0 >> 3)) * 4 + lane * 4) | dead, 0, 0,
+                                               0);
+    }
+  };
+  auto copy_a = [&](int chunk, int stage, int j, int dead) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(s_ring + stage * kStageBytes + kAOff +
+                                                                  (4 * j + wave) * 1024),
+                                             16, (a_voff0 + j * a_vstep) | dead, chunk * kGemmKC * 2, 0, 0);
   };
 
   const uint32_t magic = bf16_magic_pair();
-  const int a_row0 = 64 * wm + li;                   // + 16 fm
-  const int s_off = kSOff + (64 * wn + 4 * li) * 2;
-  const int q_off = kQOff + (64 * wm + 4 * lk) * 4;  // + 64 fm
-  const int z_off = kZOff + ((64 * wn + 4 * li) >> 3) * 4;
-  const int z_shift = (4 * li) & 7;                  // 0 or 4: first nibble of the lane's 4 columns
+  const int s_off = kSOff + cw * 2;
+  const int q_off = kQOff + 4 * lk * 4;              // + 64 fm
+  const int z_off = kZOff + (cw >> 3) * 4;
+  const int z_shift = 4 * (cw & 7);                  // first nibble of the lane's 2 columns
 
-  f32x4_t acc[4][4], P[4][4];
+  f32x4_t acc[FM][FN], P[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = P[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float sc[4] = {0.f, 0.f, 0.f, 0.f};   // scales of the chunk whose sums are in P
+    for (int j = 0; j < FN; ++j) acc[i][j] = P[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float sc[FN] = {0.f, 0.f};   // scales of the chunk whose sums are in P
+  u32x2_t bcur[4], bnext[4];
 
-  // One chunk on the MFMA units, software-pipelined with the promotion of
-  // the wave's previous chunk: tile (fm, fn) of P is first added into acc
-  // with the previous chunk's scales, then restarted from -(128 + z) * sum(a)
-  // by the chunk's first k-step, so the float32 promotion overlaps the MFMAs.
-  auto run_chunk = [&](const unsigned char *sb, const u32x4_t *bw) {
-    const u32x2_t sv = lds_read<u32x2_t>(sb, s_off);
-    f32x4_t rs[4];
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm) rs[fm] = lds_read<f32x4_t>(sb, q_off + 64 * fm);
-    float bias[4] = {-136.f, -136.f, -136.f, -136.f};
+  // Chunk i (local) lives in stage i % 3. While chunk i is computed, its
+  // MFMA sequence also issues, one piece per activation fragment, the
+  // weight loads of chunk i + 1 (first, into registers) and then the copies
+  // of chunk i + 2 into the stage chunk i - 1 used: every wave has passed
+  // the barrier at the top of chunk i, so every wave is done with it.
+  // Spreading the loads keeps the compute unit's address unit from stalling
+  // every wave with one burst. At the top of chunk i, at most the 9 copies
+  // of chunk i + 1 may still be in flight (they were issued after the weight
+  // loads of chunk i), so vmcnt(8) covers chunk i's copies and weights on
+  // every wave (waves 0..2 also wait for their small copy, issued early).
+  //
+  // One chunk on the MFMA units is software-pipelined with the promotion of
+  // the previous chunk: tile (fm, fn) of P is first added into acc with the
+  // previous chunk's scales, then restarted from -(128 + z) * sum(a) by the
+  // chunk's first k-step. (Without zero-points the pre-pass already stores
+  // -136 * sum(a).)
+  auto run_chunk = [&](int i) {
+    const unsigned char *sb = s_ring + (i % kStages) * kStageBytes;
+    const int db = i + 1 < ccount ? 0 : kDead, dc = i + 2 < ccount ? 0 : kDead;
+    const int cs = (i + 2) % kStages;
+    const uint32_t sv = lds_read<uint32_t>(sb, s_off);
+    float bias[FN] = {1.f, 1.f};
     if constexpr (ZP) {
-      const uint32_t zw = lds_read<uint32_t>(sb, z_off) >> (4 * z_shift);
+      const uint32_t zw = lds_read<uint32_t>(sb, z_off) >> z_shift;
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn) bias[fn] = -(float)(128 + (int)((zw >> (4 * fn)) & 0xFu));
+      for (int fn = 0; fn < FN; ++fn) bias[fn] = -(float)(128 + (int)((zw >> (4 * fn)) & 0xFu));
     }
-    // The 16 activation fragments of the chunk (k-step s, row tile fm) are
-    // read from LDS two fragments ahead of their MFMAs, so the read latency
-    // is covered by the MFMAs of the two previous fragments.
+    // The 32 activation fragments of the chunk (k-step s, row tile fm) are
+    // read from LDS two fragments ahead of their MFMAs.
     auto a_frag = [&](int q) {
-      const int s = q >> 2, fm = q & 3;
-      return lds_read<bf16x8_t>(sb, kAOff + (a_row0 + 16 * fm) * kARow + 16 * ((4 * s + lk) ^ li));
+      const int s = q / FM, fm = q % FM;
+      return lds_read<bf16x8_t>(sb, kAOff + (16 * fm + li) * kARow + 16 * ((4 * s + lk) ^ li));
     };
     bf16x8_t af[3];
     af[0] = a_frag(0);
     af[1] = a_frag(1);
-    bf16x8_t bfr[4];
+    bf16x8_t bfr[FN];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int s = q >> 2, fm = q & 3;
-      if (q + 2 < 16) af[(q + 2) % 3] = a_frag(q + 2);
+    for (int q = 0; q < 4 * FM; ++q) {
+      const int s = q / FM, fm = q % FM;
+      if (q + 2 < 4 * FM) af[(q + 2) % 3] = a_frag(q + 2);
+      // loads for later chunks, one piece per fragment
+      if (q < 4)
+        bnext[q] = load_b(cb + i + 1, q, db);
+      else if (q == 4)
+        copy_small(cb + i + 2, cs, dc);
+      else if (q >= 6 && (q - 6) % 3 == 0 && (q - 6) / 3 < 8)
+        copy_a(cb + i + 2, cs, (q - 6) / 3, dc);
       if (fm == 0) {
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant_word(bw[s][fn], magic);
+        for (int fn = 0; fn < FN; ++fn) bfr[fn] = dequant_word(bcur[s][fn], magic);
       }
       const bf16x8_t afr = af[q % 3];
+      f32x4_t rs;
+      if (s == 0) rs = lds_read<f32x4_t>(sb, q_off + 64 * fm);
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn) {
+      for (int fn = 0; fn < FN; ++fn) {
         if (s == 0) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(sc[fn], P[fm][fn][r], acc[fm][fn][r]);
-          const f32x4_t init = rs[fm] * bias[fn];
+          const f32x4_t init = ZP ? rs * bias[fn] : rs;
           P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], init, 0, 0, 0);
         } else {
           P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], P[fm][fn], 0, 0, 0);
         }
       }
     }
-    sc[0] = __uint_as_float(sv[0] << 16);
-    sc[1] = __uint_as_float(sv[0] & 0xFFFF0000u);
-    sc[2] = __uint_as_float(sv[1] << 16);
-    sc[3] = __uint_as_float(sv[1] & 0xFFFF0000u);
+    sc[0] = __uint_as_float(sv << 16);
+    sc[1] = __uint_as_float(sv & 0xFFFF0000u);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bcur[s] = bnext[s];
   };
 
-  // Local chunk i (= cb + i) lives in stage i % 4 and belongs to half i % 2.
-  // Round r uses chunks 2r (half 0) and 2r + 1 (half 1); the copies for
-  // round r + 1 are issued right after the barrier that opens round r, into
-  // the stages round r - 1 used (every wave has passed that barrier, so
-  // every wave is done with them).
-  const int rounds = (ccount + 1) >> 1;
-  const int mine = half;                 // local chunk of round 0 for this wave
-  u32x4_t bcur[4], bnext[4];
-  if (mine < ccount) {
-    issue(cb + mine, mine);
-    load_b(cb + mine, bcur);
-  }
-  for (int r = 0; r < rounds; ++r) {
-    const int i = 2 * r + mine;          // this wave's local chunk of round r
-    wait_all_then_barrier();
-    const bool more = i + 2 < ccount;
-    if (more) {
-      issue(cb + i + 2, (i + 2) & 3);
-      load_b(cb + i + 2, bnext);
-    }
-    if (i < ccount) run_chunk(s_ring + (i & 3) * kStageBytes, bcur);
-    if (more) {
+  // prologue: copies of chunk 0, weights of chunk 0, copies of chunk 1
+  {
+    const int d0 = ccount > 0 ? 0 : kDead, d1 = ccount > 1 ? 0 : kDead;
+    copy_small(cb, 0, d0);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bcur[s] = bnext[s];
-    }
+    for (int j = 0; j < 8; ++j) copy_a(cb, 0, j, d0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bcur[s] = load_b(cb, s, d0);
+    copy_small(cb + 1, 1, d1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) copy_a(cb + 1, 1, j, d1);
+  }
+  for (int i = 0; i < ccount; ++i) {
+    wait_then_barrier<8>();
+    run_chunk(i);
   }
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[fm][fn][q] = __builtin_fmaf(sc[fn], P[fm][fn][q], acc[fm][fn][q]);
 
-  // ---- half 1 hands its accumulators to half 0 (LDS, lane-major so the
-  // accesses are contiguous: element e of lane l at (qw, e, l)) ----
-  wait_all_then_barrier();
-  float *s_acc = (float *)s_ring;
-  if (half == 1) {
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s_acc[((qw * 64 + (fm * 16 + fn * 4 + q)) * 64) + lane] = acc[fm][fn][q];
-  }
-  wait_all_then_barrier();
-  if (half == 1) return;
-#pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[fm][fn][q] += s_acc[((qw * 64 + (fm * 16 + fn * 4 + q)) * 64) + lane];
-
-  // ---- epilogue ----
-  const int row_base = m0 + 64 * wm + 4 * lk;
+  // ---- epilogue: rows m0 + 16 fm + 4 lk + r, columns ncol, ncol + 1 ----
+  const int row_base = m0 + 4 * lk;
   if (a.nsplit > 1) {
     // K-slice partials; a second kernel adds them in the order z = 0..nsplit-1
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row_base + 16 * fm + r;
         if (row < a.M)
-          *(f32x4_t *)&a.partial[((size_t)blockIdx.z * a.M + row) * a.Np + ncol] =
-              (f32x4_t){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
+          *(f32x2_g *)&a.partial[((size_t)blockIdx.z * a.M + row) * a.Np + ncol] =
+              (f32x2_g){acc[fm][0][r], acc[fm][1][r]};
       }
     return;
   }
-  if (ncol >= a.N) return;   // N % 8 == 0: a lane's 4 columns are all in or all out
+  if (ncol >= a.N) return;   // N % 8 == 0: a lane's 2 columns are both in or both out
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row_base + 16 * fm + r;
       if (row >= a.M) continue;
       const size_t o = (size_t)row * a.N + ncol;
-      if constexpr (OF == O_BF16) {
-        *(u32x2_t *)((uint16_t *)a.out + o) =
-            (u32x2_t){pack_bf16x2(acc[fm][0][r], acc[fm][1][r]), pack_bf16x2(acc[fm][2][r], acc[fm][3][r])};
-      } else {
-        *(f32x4_t *)((float *)a.out + o) = (f32x4_t){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
-      }
+      if constexpr (OF == O_BF16)
+        *(uint32_t *)((uint16_t *)a.out + o) = pack_bf16x2(acc[fm][0][r], acc[fm][1][r]);
+      else
+        *(f32x2_g *)((float *)a.out + o) = (f32x2_g){acc[fm][0][r], acc[fm][1][r]};
     }
 }
 
 // ---------------------------------------------------------------------------
-// Activation sums: asum[g][m] = sum_{k in group g} a[m][k] (groups of 128),
-// for m < M; row stride Mp. One wave per row: lane l reads 16 bytes of each
+// Activation sums: asum[g][m] = mult * sum_{k in group g} a[m][k] (groups of
+// 128), for m < M; row stride Mp. One wave per row: lane l reads 16 bytes of each
 // 1 KiB block of the row (block j covers groups 4j .. 4j+3; lanes 16i .. 16i+15
 // hold group 4j + i), adds its 8 values in k order, and the 16 lanes of a
 // group (one DPP row) combine in a fixed order of row rotations. Up to 8
@@ -343,7 +338,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 // flight.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void asum_kernel(const uint16_t *__restrict__ A, float *__restrict__ asum, int M,
-                                                  int K, int Mp) {
+                                                  int K, int Mp, float mult) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
@@ -374,7 +369,7 @@ __global__ __launch_bounds__(256) void asum_kernel(const uint16_t *__restrict__ 
       s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x124, 0xF, 0xF, false));  // row_ror:4
       s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x122, 0xF, 0xF, false));  // row_ror:2
       s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x121, 0xF, 0xF, false));  // row_ror:1
-      if (g < ngroups && (lane & 15) == 0) asum[(size_t)g * Mp + m] = s;
+      if (g < ngroups && (lane & 15) == 0) asum[(size_t)g * Mp + m] = s * mult;
     }
   }
 }
@@ -388,7 +383,8 @@ static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
 // The dispatcher sends only G == 128, K % 128 == 0, N % 8 == 0 here.
 hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t st) {
   if (G != 128 || a.K % kGemmKC != 0 || a.N % 8 != 0) return hipErrorInvalidValue;
-  asum_kernel<<<(a.M + 3) / 4, 256, 0, st>>>(a.A, a.asum, a.M, a.K, a.Mp);
+  // without zero-points the MFMA starts from -(128 + 8) * sum(a): store that
+  asum_kernel<<<(a.M + 3) / 4, 256, 0, st>>>(a.A, a.asum, a.M, a.K, a.Mp, zp ? 1.f : -136.f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ofmt == O_BF16) return zp ? go<O_BF16, true>(a, grid, st) : go<O_BF16, false>(a, grid, st);

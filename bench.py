@@ -131,7 +131,7 @@ def run_workload(name, steps, warmup, mode, M=None, force_path=-1, force_nsplit=
     ms = time_steps(call, steps, warmup, mode)
     path, ns, ws = qg.plan(p.M, p.N, p.K, p.G, p.prec, force_path, force_nsplit)
     res = dict(workload=name, M=p.M, N=p.N, K=p.K, group=p.G, prec=qg._PREC_FMT[p.prec], has_zp=p.has_zp,
-               path=["gemv", "gemm"][path], nsplit=ns, copies=copies, ms=ms,
+               path=["gemv", "gemm", "small"][path], nsplit=ns, copies=copies, ms=ms,
                bytes=algorithmic_bytes(p), flops=2 * p.M * p.N * p.K)
     res["gbs"] = res["bytes"] / (ms * 1e-3) / 1e9
     res["tflops"] = res["flops"] / (ms * 1e-3) / 1e12

@@ -23,7 +23,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "qgemm.h")
 # status codes, precisions and paths (include/qgemm.h)
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EALIGN, EHIP = 0, -1, -2, -3, -4, -5
 W4_A_BF16, W4_A_F32, W8_A_F32, W4_A_I8, W8_A_I8, W4_A_BF16_OF32 = 1, 2, 3, 4, 5, 6
-PATH_AUTO, PATH_GEMV, PATH_GEMM = -1, 0, 1
+PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SMALL = -1, 0, 1, 2
 
 _PREC_FMT = {1: ("w4", "bf16", "bf16", "bf16"), 2: ("w4", "f32", "f32", "f32"),
              3: ("w8", "f32", "f32", "f32"), 4: ("w4", "i8", "f32", "f32"),

@@ -55,11 +55,24 @@ struct GemmArgs {
   int nchunks, nsplit;     // K / kGemmKC chunks split into nsplit slices
 };
 
+struct SmallArgs {
+  const uint16_t *A;       // [M][K] bf16, M <= 64
+  const uint32_t *W;       // packed int4, layout version 2
+  const uint16_t *S;       // [K/128][N] bf16
+  const uint32_t *Z;       // [K/128][N/8] or null
+  void *out;               // [M][N] bf16 or float32 (nsplit == 1)
+  float *partial;          // [nsplit][M][Np] (nsplit > 1)
+  int M, N, K, Np;
+  int ngroups, nsplit;     // K / 128 groups split into nsplit slices
+};
+
 // Host-side launchers (defined next to their kernels). They return the HIP
 // launch status; the dispatcher has validated every argument before.
 hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, const GemvArgs &a,
                        dim3 grid, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t stream);
+// mb = ceil(M / 16) row blocks; grid (Np / 64, nsplit)
+hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np,
                        hipStream_t stream);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.

@@ -1,0 +1,248 @@
+// Small-M MFMA path of the group-quantized GEMM (bf16 activations, int4
+// weights, bf16 scales, optional int4 zero-points, groups of 128), for the
+// band of M where the product is still bound by the weight bytes but a
+// vector-ALU GEMV runs out of arithmetic (the small-M specialisation of the
+// page "quantization-and-fused-kernels" (arganzheng.life), section 三.3,
+// item 6, and the roofline argument of its section 三.2).
+//
+// Structure: the weights stream once, as in the GEMV path, and the dot
+// products run on v_mfma_f32_16x16x32_bf16 with M padded to MB blocks of 16
+// rows:
+//   - a workgroup (4 waves) covers one 64-column tile of the packed layout
+//     and a K-slice of whole groups (slice z of nsplit, the z-split of the
+//     page "04 · 分组量化 GEMM 内核" (developer.aliyun.com), section 3.3);
+//     each wave takes a contiguous share of the slice's groups;
+//   - per group, each lane loads 16 bytes of packed words per k-step (4
+//     adjacent columns x 8 k; a wave reads 1 KiB of contiguous memory) and
+//     turns each word into four bf16 pairs (128 + q) (bf16 magic number
+//     0x4300, section 二.4 of the first page); MFMA column j of tile f is
+//     physical column 4j + f of the 64-column tile;
+//   - activation fragments are read from global memory (rows past M read as
+//     zeros); the bias is removed on the MFMA units too: a second MFMA per
+//     k-step multiplies the same fragment by the constant -(128 + z) of each
+//     column (exact in bf16), so P = sum_k a_k (q_k - z) without a pre-pass;
+//   - the group's scale is applied in float32 (acc += s * P);
+//   - the 4 waves' results are added in wave order (waves 1..3 through LDS),
+//     then written to the output (nsplit == 1) or to float32 partials that a
+//     second kernel adds in the order z = 0..nsplit-1.
+#include "common.h"
+
+namespace qg {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_s;
+typedef __attribute__((ext_vector_type(4))) float f32x4_s;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_s;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_s;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_s;
+typedef __attribute__((ext_vector_type(2))) float f32x2_s;
+
+constexpr int kWaves = 4;
+constexpr int kBufWord3s = 0x00020000;
+constexpr int kStreamPolicy = 2;    // non-temporal
+
+__device__ __forceinline__ uint32_t magic_pair() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  return m;
+}
+
+__device__ __forceinline__ bf16x8_s dequant(uint32_t w, uint32_t magic) {
+  u32x4_s x;
+  x[0] = (w & 0x000F000Fu) | magic;
+  x[1] = ((w >> 4) & 0x000F000Fu) | magic;
+  x[2] = ((w >> 8) & 0x000F000Fu) | magic;
+  x[3] = ((w >> 12) & 0x000F000Fu) | magic;
+  return __builtin_bit_cast(bf16x8_s, x);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  f32x2_s v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_s));
+}
+
+// Eight copies of the bf16 value -(128 + z): the correction operand.
+__device__ __forceinline__ bf16x8_s bias_operand(int z) {
+  const uint32_t h = bf16x2_bits(-(float)(128 + z), -(float)(128 + z));
+  const u32x4_s x = {h, h, h, h};
+  return __builtin_bit_cast(bf16x8_s, x);
+}
+
+}  // namespace
+
+template <int MB, int OF, bool ZP>
+__global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a) {
+  extern __shared__ __align__(16) unsigned char s_red[];   // [waves - 1][MB * 16][64] float32
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  const int tile = blockIdx.x;
+  const int z = blockIdx.y;
+  const int R = a.K / 8;
+
+  int gb, gcount, wg0, wgc;
+  split_range(a.ngroups, a.nsplit, z, gb, gcount);
+  split_range(gcount, kWaves, wave, wg0, wgc);
+
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.W + (size_t)tile * R * kTileCols), (short)0, R * kTileCols * 4, kBufWord3s);
+  const int w_voff = (lk * kTileCols + 4 * li) * 4;
+  // scales and zero-points of the lane's 4 columns (N % 8 == 0: all 4 are
+  // in or all out; a lane past N reads column 0's and its results are
+  // dropped)
+  const int ncol = tile * kTileCols + 4 * li;
+  const int scol = ncol < a.N ? ncol : 0;
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.S, (short)0, a.ngroups * a.N * 2, kBufWord3s);
+  const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.Z, (short)0, ZP ? a.ngroups * (a.N >> 3) * 4 : 0, kBufWord3s);
+  // activations: fragment (fm, s) of lane (li, lk) is row 16 fm + li,
+  // k = 128 g + 32 s + 8 lk .. +7; rows past M read zeros (range check of
+  // the VGPR offset; the group offset in the SGPR operand stays in the row)
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.A, (short)0, a.M * a.K * 2, kBufWord3s);
+
+  const uint32_t magic = magic_pair();
+  f32x4_s acc[MB][4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_s){0.f, 0.f, 0.f, 0.f};
+
+  // one group's loads; the next group's are issued before the current one is
+  // computed (a group past the wave's range re-reads the wave's last one, or
+  // the matrix's last one for a wave without groups: valid addresses,
+  // results unused)
+  struct GroupLoads {
+    u32x4_s w[4];
+    bf16x8_s af[MB][4];
+    u32x2_s sv;
+    uint32_t zw;
+  };
+  auto issue = [&](int gi, GroupLoads &L) {
+    const int g = min(gb + wg0 + (gi < wgc ? gi : (wgc > 0 ? wgc - 1 : 0)), a.ngroups - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      L.w[s] = __builtin_bit_cast(u32x4_s, __builtin_amdgcn_raw_buffer_load_b128(
+                                               w_rsrc, w_voff, (g * 16 + 4 * s) * kTileCols * 4, kStreamPolicy));
+#pragma unroll
+    for (int fm = 0; fm < MB; ++fm)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        L.af[fm][s] = __builtin_bit_cast(
+            bf16x8_s, __builtin_amdgcn_raw_buffer_load_b128(
+                          a_rsrc, ((16 * fm + li) * a.K + 32 * s + 8 * lk) * 2, g * 256, 0));
+    L.sv = __builtin_bit_cast(u32x2_s, __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, scol * 2, g * a.N * 2, 0));
+    L.zw = 0x88888888u;
+    if constexpr (ZP)
+      L.zw = __builtin_amdgcn_raw_buffer_load_b32(z_rsrc, (scol >> 3) * 4, g * (a.N >> 3) * 4, 0) >>
+             (4 * (scol & 7));
+  };
+  auto compute = [&](const GroupLoads &L) {
+    bf16x8_s corr[4];
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) corr[fn] = bias_operand((int)((L.zw >> (4 * fn)) & 0xFu));
+    f32x4_s P[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P[i][j] = (f32x4_s){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_s bfr[4];
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant(L.w[s][fn], magic);
+#pragma unroll
+      for (int fm = 0; fm < MB; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+          P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(L.af[fm][s], bfr[fn], P[fm][fn], 0, 0, 0);
+          P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(L.af[fm][s], corr[fn], P[fm][fn], 0, 0, 0);
+        }
+    }
+    const float sc[4] = {__uint_as_float(L.sv[0] << 16), __uint_as_float(L.sv[0] & 0xFFFF0000u),
+                         __uint_as_float(L.sv[1] << 16), __uint_as_float(L.sv[1] & 0xFFFF0000u)};
+#pragma unroll
+    for (int fm = 0; fm < MB; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(sc[fn], P[fm][fn][r], acc[fm][fn][r]);
+  };
+
+  GroupLoads cur, nxt;
+  issue(0, cur);
+  for (int gi = 0; gi < wgc; ++gi) {
+    issue(gi + 1, nxt);
+    compute(cur);
+    cur = nxt;
+  }
+
+  // ---- the 4 waves' results, added in wave order: waves 1..3 hand theirs
+  // to wave 0 through LDS (element (16 fm + 4 lk + r, 4 li + fn) of wave w at
+  // s_red[(((w - 1) * MB + fm) * 16 + 4 lk + r) * 64 + 4 li + fn]) ----
+  float *red = (float *)s_red;
+  if (wave > 0) {
+#pragma unroll
+    for (int fm = 0; fm < MB; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *(f32x4_s *)&red[(((wave - 1) * MB + fm) * 16 + 4 * lk + r) * 64 + 4 * li] =
+            (f32x4_s){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  if (wave > 0) return;
+
+  const int n = tile * kTileCols + 4 * li;
+#pragma unroll
+  for (int fm = 0; fm < MB; ++fm)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * fm + 4 * lk + r;
+      f32x4_s v = (f32x4_s){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += *(const f32x4_s *)&red[(((w - 1) * MB + fm) * 16 + 4 * lk + r) * 64 + 4 * li];
+      if (row >= a.M) continue;
+      if (a.nsplit > 1) {
+        *(f32x4_s *)&a.partial[((size_t)z * a.M + row) * a.Np + n] = v;
+      } else if (n < a.N) {
+        const size_t o = (size_t)row * a.N + n;
+        if constexpr (OF == O_BF16)
+          *(u32x2_s *)((uint16_t *)a.out + o) = (u32x2_s){bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
+        else
+          *(f32x4_s *)((float *)a.out + o) = v;
+      }
+    }
+}
+
+template <int MB, int OF, bool ZP>
+static hipError_t go_small(const SmallArgs &a, dim3 grid, hipStream_t st) {
+  const size_t lds = (size_t)(kWaves - 1) * MB * 16 * 64 * 4;
+  gemm_small_kernel<MB, OF, ZP><<<grid, kWaves * kWave, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int OF, bool ZP>
+static hipError_t go_small_mb(int mb, const SmallArgs &a, dim3 grid, hipStream_t st) {
+  switch (mb) {
+    case 1: return go_small<1, OF, ZP>(a, grid, st);
+    case 2: return go_small<2, OF, ZP>(a, grid, st);
+    case 3: return go_small<3, OF, ZP>(a, grid, st);
+    case 4: return go_small<4, OF, ZP>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The dispatcher sends only bf16 activations, G == 128, N % 8 == 0 and
+// M <= 64 here (mb = ceil(M / 16) row blocks of 16).
+hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t st) {
+  if (a.N % 8 != 0 || a.K % 128 != 0 || mb < 1 || mb > 4 || a.M > 16 * mb) return hipErrorInvalidValue;
+  if (ofmt == O_BF16) return zp ? go_small_mb<O_BF16, true>(mb, a, grid, st) : go_small_mb<O_BF16, false>(mb, a, grid, st);
+  return zp ? go_small_mb<O_F32, true>(mb, a, grid, st) : go_small_mb<O_F32, false>(mb, a, grid, st);
+}
+
+}  // namespace qg

@@ -11,9 +11,12 @@
 //
 // Dispatch follows the roofline argument of the page
 // "quantization-and-fused-kernels" (arganzheng.life), section 三.2: at small
-// M the product is bound by the weight bytes, so the vector-ALU GEMV path
-// streams the weights once; at larger M it is bound by arithmetic, and bf16
-// activations go to the MFMA path. The K-split (nsplit) and its fixed-order
+// M the product is bound by the weight bytes, so the weights stream once:
+// through the vector-ALU GEMV path at M = 1 (and for fp32 / int8 activations
+// or groups of 32 up to M = 8), through the small-M MFMA path for bf16
+// activations at 2 <= M <= 64 (measured faster than the GEMV from M = 2 and
+// than the tiled GEMM up to M = 64); at larger M the product is bound by
+// arithmetic and bf16 activations go to the tiled MFMA GEMM. The K-split (nsplit) and its fixed-order
 // reduction follow the z-split of the page "04 · 分组量化 GEMM 内核"
 // (developer.aliyun.com), section 3.3: a pure function of the shape and the
 // device's compute-unit count, so repeated calls (and captured graphs) take
@@ -70,6 +73,7 @@ int device_cus() {
 size_t padded_cols(int N) { return ((size_t)N + kColAlign - 1) / kColAlign * kColAlign; }
 
 constexpr size_t kPartialCap = 256ull << 20;  // bytes of float32 partials at most
+constexpr int kSmallMaxM = 64;                // rows the small-M MFMA path takes (4 blocks of 16)
 constexpr size_t kGemvLdsCap = 60 * 1024;     // dynamic LDS per workgroup (static LDS comes on top)
 
 struct Plan {
@@ -115,10 +119,13 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   const size_t Np = padded_cols(N);
   const bool gemm_ok = f.a == A_BF16 && G == 128 && K % kGemmKC == 0 && N % 8 == 0 && M <= 65535 &&
                        gemm_asum_bytes(M, K) <= (size_t)INT_MAX;
+  const bool small_ok = f.a == A_BF16 && G == 128 && N % 8 == 0 && M <= kSmallMaxM &&
+                        (size_t)M * K * 2 <= (size_t)INT_MAX;
   int path = force_path;
-  if (path == QG_PATH_AUTO) path = (M > 8 && gemm_ok) ? QG_PATH_GEMM : QG_PATH_GEMV;
-  if (path == QG_PATH_GEMM && !gemm_ok) return QG_EUNSUPPORTED;
-  if (path != QG_PATH_GEMV && path != QG_PATH_GEMM) return QG_EINVAL;
+  if (path == QG_PATH_AUTO)
+    path = (M >= 2 && small_ok) ? QG_PATH_SMALL : (M > 8 && gemm_ok) ? QG_PATH_GEMM : QG_PATH_GEMV;
+  if ((path == QG_PATH_GEMM && !gemm_ok) || (path == QG_PATH_SMALL && !small_ok)) return QG_EUNSUPPORTED;
+  if (path != QG_PATH_GEMV && path != QG_PATH_GEMM && path != QG_PATH_SMALL) return QG_EINVAL;
   p.path = path;
 
   long long base;
@@ -128,6 +135,11 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
     p.tiles_x = (int)(Np / kTileCols);
     p.tiles_y = p.mblocks;
     p.units = K / G;
+  } else if (path == QG_PATH_SMALL) {
+    p.mb = (M + 15) / 16;
+    p.tiles_x = (int)(Np / kTileCols);
+    p.tiles_y = 1;
+    p.units = K / 128;
   } else {
     p.tiles_x = (int)(Np / kGemmBN);
     p.tiles_y = (M + kGemmBM - 1) / kGemmBM;
@@ -261,6 +273,18 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.nsplit = p.nsplit;
     e = launch_gemv(f.w, f.a, f.s, f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.mblocks, p.nsplit),
                     p.lds, s);
+  } else if (p.path == QG_PATH_SMALL) {
+    SmallArgs a;
+    a.A = (const uint16_t *)A;
+    a.W = (const uint32_t *)w_packed;
+    a.S = (const uint16_t *)scales;
+    a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
+    a.out = out;
+    a.partial = partial;
+    a.M = M; a.N = N; a.K = K; a.Np = Np;
+    a.ngroups = K / 128;
+    a.nsplit = p.nsplit;
+    e = launch_gemm_small(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.nsplit), s);
   } else {
     GemmArgs a;
     a.A = (const uint16_t *)A;

@@ -69,8 +69,10 @@ enum {
 enum {
     QG_PATH_AUTO = -1,
     QG_PATH_GEMV = 0,      /* vector-ALU path: weight streaming, any M               */
-    QG_PATH_GEMM = 1       /* MFMA path: bf16 activations (prec 1 and 6), G == 128,
+    QG_PATH_GEMM = 1,      /* MFMA path: bf16 activations (prec 1 and 6), G == 128,
                               N % 8 == 0, M <= 65535                                   */
+    QG_PATH_SMALL = 2      /* small-M MFMA path: weights streamed once, M <= 64,
+                              bf16 activations, G == 128, N % 8 == 0                  */
 };
 
 /*
@@ -109,7 +111,7 @@ int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, 
 size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec);
 
 /*
- * The plan qgemm_run_ex would use: path (QG_PATH_GEMV or QG_PATH_GEMM),
+ * The plan qgemm_run_ex would use: path (QG_PATH_GEMV, QG_PATH_GEMM or QG_PATH_SMALL),
  * nsplit (number of K-slices of whole groups whose float32 partial sums are
  * added in the fixed order z = 0, 1, ..., nsplit-1) and workspace bytes.
  * force_path: QG_PATH_AUTO or a path; force_nsplit: <= 0 for automatic, else

@@ -60,6 +60,9 @@ def test_layout_and_sizes():
     (dict(path=qg.PATH_GEMM, prec=qg.W4_A_F32), qg.EUNSUPPORTED),
     (dict(path=qg.PATH_GEMM, G=32, M=64), qg.EUNSUPPORTED),
     (dict(path=5), qg.EINVAL),
+    (dict(path=qg.PATH_SMALL, prec=qg.W4_A_F32, M=16), qg.EUNSUPPORTED),
+    (dict(path=qg.PATH_SMALL, G=32, M=16), qg.EUNSUPPORTED),
+    (dict(path=qg.PATH_SMALL, G=128, K=256, M=65), qg.EUNSUPPORTED),
 ])
 def test_validation_before_launch(kw, status):
     st = run(**kw)
@@ -110,14 +113,17 @@ def test_plan_is_pure_and_consistent(M, N, K, G, prec):
     path, ns, ws = a
     assert 1 <= ns <= K // G
     assert ws == qg.lib().qgemm_workspace_bytes(M, N, K, G, prec)
-    if path == qg.PATH_GEMV:
+    if path in (qg.PATH_GEMV, qg.PATH_SMALL):
         assert (ws == 0) == (ns == 1)
+        assert ws == (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)
     else:  # activation sums [K/128][M rounded up to 128] float32, then the split partials
         asum = -(-(K // 128) * (-(-M // 128) * 128) * 4 // 256) * 256
         assert ws == asum + (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)
-    if prec in (1, 6) and M > 8:
+    if prec in (1, 6) and G == 128 and N % 8 == 0 and 2 <= M <= 64:
+        assert path == qg.PATH_SMALL
+    elif prec in (1, 6) and M > 64:
         assert path == qg.PATH_GEMM
-    if M <= 8:
+    elif M <= 8:
         assert path == qg.PATH_GEMV
 
 
@@ -128,7 +134,13 @@ def test_forced_plans():
         assert (ws == 0) == (got == 1)
     path, ns, ws = qg.plan(300, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMM, 3)
     assert path == qg.PATH_GEMM and ns == 3
-    # the MFMA path needs N % 8 == 0; automatic dispatch sends other N to the GEMV
+    path, ns, ws = qg.plan(40, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_SMALL, 0)
+    assert path == qg.PATH_SMALL and ns >= 1
+    with pytest.raises(qg.QGemmError):   # small-M path: at most 64 rows
+        qg.plan(65, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_SMALL, 0)
+    with pytest.raises(qg.QGemmError):   # ... bf16 activations and groups of 128 only
+        qg.plan(16, 1000, 1024, 32, qg.W4_A_BF16, qg.PATH_SMALL, 0)
+    # the MFMA paths need N % 8 == 0; automatic dispatch sends other N to the GEMV
     with pytest.raises(qg.QGemmError):
         qg.plan(300, 1001, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMM, 0)
     assert qg.plan(300, 1001, 1024, 128, qg.W4_A_BF16)[0] == qg.PATH_GEMV

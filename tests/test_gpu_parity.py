@@ -51,13 +51,26 @@ def test_gemm_small(prec, zp, M):
     p = wl.make_problem(M, N, K, 128, prec, zp, seed=2000 + 10 * M + prec + zp, outlier_frac=0.01)
     d = Dev(p)
     path, ns, _ = qg.plan(M, N, K, 128, prec)
-    assert path == qg.PATH_GEMM
-    out = to_f64(d.run())
+    assert path == (qg.PATH_SMALL if M <= 64 else qg.PATH_GEMM)
+    out = to_f64(d.run(force_path=qg.PATH_GEMM))
     ref, bound = oracle.for_problem(p)
     check(out, ref, bound, f"gemm prec={prec} zp={zp} M={M} nsplit={ns}", bf16_out=prec == 1)
 
 
-@pytest.mark.parametrize("path,M", [(0, 1), (0, 5), (1, 40), (1, 200)])
+@pytest.mark.parametrize("prec,zp", [(1, False), (1, True), (6, False), (6, True)])
+@pytest.mark.parametrize("M", [1, 2, 9, 16, 17, 33, 48, 64])
+def test_small_m_path(prec, zp, M):
+    """The small-M MFMA path (weights streamed once, M <= 64), automatic split."""
+    N, K = 1000, 1024
+    p = wl.make_problem(M, N, K, 128, prec, zp, seed=2500 + 10 * M + prec + zp, outlier_frac=0.01)
+    d = Dev(p)
+    _, ns, _ = qg.plan(M, N, K, 128, prec, qg.PATH_SMALL)
+    out = to_f64(d.run(force_path=qg.PATH_SMALL))
+    ref, bound = oracle.for_problem(p)
+    check(out, ref, bound, f"small-M prec={prec} zp={zp} M={M} nsplit={ns}", bf16_out=prec == 1)
+
+
+@pytest.mark.parametrize("path,M", [(0, 1), (0, 5), (1, 40), (1, 200), (2, 17), (2, 64)])
 @pytest.mark.parametrize("ns", [1, 2, 3, 8])
 def test_forced_nsplit_and_determinism(path, M, ns):
     N, K = 776, 1024
@@ -85,7 +98,7 @@ def test_edge_shapes():
 # ---------------------------------------------------------------------------
 # invariants with exact answers
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("path,M", [(0, 1), (0, 6), (1, 33)])
+@pytest.mark.parametrize("path,M", [(0, 1), (0, 6), (1, 33), (2, 20)])
 def test_integer_identity_bitwise(path, M):
     """Unit scales, zero-point 8, integer activations: fp32 output equals the
     integer matmul of (q - 8) exactly."""
@@ -115,7 +128,7 @@ def test_int8_partials_bit_exact(prec, zp, M):
     assert np.array_equal(out, P.sum(axis=1).astype(np.float64))
 
 
-@pytest.mark.parametrize("prec,path,M", [(6, 0, 1), (6, 1, 40), (2, 0, 3), (3, 0, 1), (4, 0, 2)])
+@pytest.mark.parametrize("prec,path,M", [(6, 0, 1), (6, 1, 40), (6, 2, 24), (2, 0, 3), (3, 0, 1), (4, 0, 2)])
 def test_scale_doubling_bitwise(prec, path, M):
     p = wl.make_problem(M, 512, 1024, 128 if prec == 6 else 32, prec, False, seed=8000 + M)
     o1 = to_f64(Dev(p).run(force_path=path))
@@ -127,7 +140,7 @@ def test_scale_doubling_bitwise(prec, path, M):
     assert np.array_equal(o2, 2 * o1)
 
 
-@pytest.mark.parametrize("path,M", [(0, 1), (0, 8), (1, 64)])
+@pytest.mark.parametrize("path,M", [(0, 1), (0, 8), (1, 64), (2, 16)])
 def test_zero_points_all_eight_equal_symmetric(path, M):
     p = wl.make_problem(M, 1024, 1024, 128, 1, False, seed=9000 + M, outlier_frac=0.01)
     o1 = Dev(p).run(force_path=path)
@@ -137,7 +150,7 @@ def test_zero_points_all_eight_equal_symmetric(path, M):
     assert bitwise_equal(o1, o2)
 
 
-@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("path", [0, 1, 2])
 def test_one_hot_reads_back_w_hat(path):
     """a = e_k (rows of the identity): fp32 output row k is w_hat[k] exactly;
     k = G-1, G, K-1 sit at group boundaries."""

@@ -576,35 +576,6 @@ void gemv_kernel(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fixed-order reduction of K-slice partials (second kernel of a split call)
-// ---------------------------------------------------------------------------
-template <int OF>
-__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ part, void *__restrict__ out,
-                                                     int M, int N, int Np, int nsplit) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  for (int m = blockIdx.y; m < M; m += gridDim.y) {
-    float s = 0.f;
-    for (int zz = 0; zz < nsplit; ++zz) s += part[((size_t)zz * M + m) * Np + n];
-    const size_t o = (size_t)m * N + n;
-    if constexpr (OF == O_BF16)
-      ((uint16_t *)out)[o] = f32_to_bf16(s);
-    else
-      ((float *)out)[o] = s;
-  }
-}
-
-hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
-                         hipStream_t st) {
-  dim3 grid((N + 255) / 256, M < 65535 ? M : 65535);
-  if (ofmt == O_BF16)
-    reduce_kernel<O_BF16><<<grid, 256, 0, st>>>(partial, out, M, N, Np, nsplit);
-  else
-    reduce_kernel<O_F32><<<grid, 256, 0, st>>>(partial, out, M, N, Np, nsplit);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // launcher: (wfmt, afmt, sfmt, ofmt, zp, mb, G) -> kernel instance
 // ---------------------------------------------------------------------------
 template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G>

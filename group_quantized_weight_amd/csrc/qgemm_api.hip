@@ -148,8 +148,10 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   base = (long long)p.tiles_x * p.tiles_y;  // workgroups without a K-split
 
   // K-split: only when the tiles alone leave compute units idle; then aim at
-  // two workgroups per compute unit.
-  int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((2LL * cus + base - 1) / base));
+  // two workgroups per compute unit (one for the small-M MFMA path, whose
+  // partials grow with M: measured best on MI355X).
+  const long long target = path == QG_PATH_SMALL ? cus : 2LL * cus;
+  int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((target + base - 1) / base));
   ns = balance(p.units, ns);
   if (path == QG_PATH_GEMV)
     while (ns < p.units && gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) ns = balance(p.units, ns + 1);

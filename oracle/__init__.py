@@ -47,6 +47,7 @@ def load(path: str = _LIB):
     lib.oracle_qgemm.argtypes = [c_int] * 8 + [vp] * 5 + [i64p, c_int, i64p, c_int, vp, vp]
     lib.oracle_int_partials.argtypes = [c_int] * 6 + [vp, vp, vp, i64p, c_int, i64p, c_int, vp]
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_quantize_act.argtypes = [c_int, c_int, c_int, vp, vp, vp]
     if path == _LIB:
         _lib = lib
     return lib
@@ -132,6 +133,20 @@ def for_problem(p, rows=None, cols=None, lib=None):
     """Oracle (ref, bound) of a workloads.Problem."""
     return qgemm(p.M, p.N, p.K, p.G, p.wfmt, p.afmt, p.sfmt, p.has_zp, p.A, p.a_scale, p.W, p.S,
                  p.Z, rows=rows, cols=cols, lib=lib)
+
+
+def quantize_act(A, G: int, lib=None):
+    """Dynamic per-group int8 quantization of float32 activations [M, K]:
+    returns (codes int8 [M, K], scales float32 [M, K/G]) (see oracle.c)."""
+    lib = lib or load()
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    M, K = A.shape
+    Aq = np.empty((M, K), np.int8)
+    sc = np.empty((M, K // G if G > 0 else 0), np.float32)
+    st = lib.oracle_quantize_act(M, K, G, _ptr(A), _ptr(Aq), _ptr(sc))
+    if st != 0:
+        raise ValueError("oracle_quantize_act: bad shape")
+    return Aq, sc
 
 
 def num_threads(lib=None) -> int:

@@ -260,6 +260,50 @@ int oracle_int_partials(int M, int N, int K, int G, int wfmt, int has_zp, const 
     return 0;
 }
 
+/*
+ * Dynamic per-group int8 quantization of float32 activations: the absmax ->
+ * scale -> round -> clamp kernel of the page "quantization-and-fused-kernels"
+ * (arganzheng.life), section 四.5 (there for fp8 per token; here with int8
+ * codes per (row, group of G), the activation format that the blockwise
+ * product of the page "04 · 分组量化 GEMM 内核" (developer.aliyun.com),
+ * section 二, consumes). Read as, for every row m and group g, in float32
+ * (the precision the codes are decided in):
+ *     amax        = max_k |a[m,k]|                     (exact)
+ *     a_scale[m,g] = amax / 127, or 1 if amax == 0     (one rounding)
+ *     Aq[m,k]     = clamp(rint(a[m,k] / a_scale[m,g]), -127, 127)
+ * with rint rounding halves to even. A group of zeros gets scale 1 and
+ * codes 0 (the section's guard against dividing by zero).
+ * Returns 0, or -1 on bad shapes.
+ */
+int oracle_quantize_act(int M, int K, int G, const float *A, int8_t *Aq, float *a_scale)
+{
+    if (M < 0 || K <= 0 || G <= 0 || K % G != 0)
+        return -1;
+    const int ng = K / G;
+    for (int m = 0; m < M; ++m) {
+        for (int g = 0; g < ng; ++g) {
+            const float *a = A + (size_t)m * K + (size_t)g * G;
+            float amax = 0.0f;
+            for (int j = 0; j < G; ++j) {
+                float v = fabsf(a[j]);
+                if (v > amax)
+                    amax = v;
+            }
+            const float sc = amax > 0.0f ? amax / 127.0f : 1.0f;
+            a_scale[(size_t)m * ng + g] = sc;
+            for (int j = 0; j < G; ++j) {
+                float q = rintf(a[j] / sc);
+                if (q > 127.0f)
+                    q = 127.0f;
+                if (q < -127.0f)
+                    q = -127.0f;
+                Aq[(size_t)m * K + (size_t)g * G + j] = (int8_t)q;
+            }
+        }
+    }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

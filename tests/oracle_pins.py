@@ -280,6 +280,85 @@ def check_zero_points_all_eight(lib):
     assert np.array_equal(ref, ref2)
 
 
+# --------------------------------------------------------------------------
+# dynamic per-group int8 activation quantization
+# --------------------------------------------------------------------------
+QGOLDEN = os.path.join(os.path.dirname(__file__), "golden", "quantize_cases.json")
+with open(QGOLDEN) as _f:
+    QHAND = json.load(_f)["cases"]
+
+
+def _quantize(lib, A, G):
+    return oracle.quantize_act(np.asarray(A, np.float32), G, lib=lib)
+
+
+def check_quant_hand(lib, case):
+    q, s = _quantize(lib, case["A"], case["G"])
+    assert np.array_equal(q, np.array(case["codes"])), (case["id"], q)
+    assert np.array_equal(s, np.array(case["scales"], np.float32)), (case["id"], s)
+
+
+def _quant_inputs(seed=31, M=5, K=256, G=32):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    A[0, 5] = -40.0                      # a negative maximum
+    A[1, 32:64] = 0.0                    # a group of zeros
+    A[2, 64:96] *= 1e-3                  # a small group
+    return A, G
+
+
+def check_quant_properties(lib):
+    """Facts that hold for any correct quantizer of the definition: codes in
+    [-127, 127]; each group's largest |a| maps to +-127 with its sign; every
+    code is within half a step of a / a_scale (fp64, with the scale the
+    quantizer returned); a group of zeros has scale 1 and codes 0; and the
+    scale is max|a| / 127 up to one float32 rounding."""
+    A, G = _quant_inputs()
+    q, s = _quantize(lib, A, G)
+    M, K = A.shape
+    qi = q.astype(np.int64)
+    assert np.all(np.abs(qi) <= 127)
+    for m in range(M):
+        for g in range(K // G):
+            a = A[m, g * G:(g + 1) * G].astype(np.float64)
+            sc = float(s[m, g])
+            amax = np.abs(a).max()
+            if amax == 0:
+                assert sc == 1.0 and np.all(qi[m, g * G:(g + 1) * G] == 0), (m, g)
+                continue
+            assert abs(sc * 127 - amax) <= amax * 2.0 ** -22, (m, g, sc, amax)
+            j = int(np.argmax(np.abs(a)))
+            assert qi[m, g * G + j] == (127 if a[j] > 0 else -127), (m, g)
+            err = np.abs(qi[m, g * G:(g + 1) * G] - a / sc)
+            assert np.all(err <= 0.5 + 1e-4), (m, g, err.max())
+
+
+def check_quant_power_of_two(lib):
+    """Multiplying the activations by 4 multiplies every scale by 4 and leaves
+    every code unchanged (exact in binary floating point)."""
+    A, G = _quant_inputs(seed=32)
+    q1, s1 = _quantize(lib, A, G)
+    q2, s2 = _quantize(lib, A * np.float32(4), G)
+    assert np.array_equal(q1, q2)
+    zero = np.all(A.reshape(A.shape[0], -1, G) == 0, axis=2)
+    assert np.array_equal(s2[~zero], 4 * s1[~zero])
+
+
+def check_quant_vs_generator(lib):
+    """The input generator quantizes with the same recipe in float64 (an
+    independent route, workloads.quantize_i8): the scales agree, and away from
+    rounding ties so do the codes."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    M, K, G = 4, 512, 32
+    a = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+    q, s = _quantize(lib, a, G)
+    gq, gs = wl.quantize_i8(a, G)
+    ratio = (a.reshape(M, K // G, G).astype(np.float64) / gs[:, :, None].astype(np.float64)).reshape(M, K)
+    away = np.abs(ratio - np.floor(ratio) - 0.5) > 1e-4
+    assert np.array_equal(s, gs)
+    assert np.array_equal(q[away], gq[away])
+
+
 def all_checks():
     """(name, callable(lib)) for every pin."""
     out = [(f"hand_{c['id']}", (lambda c: lambda lib: check_hand_case(lib, c))(c)) for c in HAND]
@@ -293,4 +372,7 @@ def all_checks():
     out += [(f"one_hot_{z}", (lambda z: lambda lib: check_one_hot(lib, z))(z)) for z in (False, True)]
     out += [("q_equal_z", check_q_equal_z), ("scale_doubling", check_scale_doubling),
             ("zero_points_all_eight", check_zero_points_all_eight)]
+    out += [(f"quant_hand_{c['id']}", (lambda c: lambda lib: check_quant_hand(lib, c))(c)) for c in QHAND]
+    out += [("quant_properties", check_quant_properties), ("quant_power_of_two", check_quant_power_of_two),
+            ("quant_vs_generator", check_quant_vs_generator)]
     return out

@@ -40,6 +40,12 @@ MUTANTS = [
     ("zp_row_stride", "Z[(size_t)g * words_per_row + n / 8]", "Z[(size_t)g * 0 + n / 8]"),
     ("i8_activation_unscaled", "return (double)a_scale[(size_t)m * (K / G) + k / G] * (double)",
      "return 1.0 * (double)"),
+    ("quant_divisor_128", "amax / 127.0f", "amax / 128.0f"),
+    ("quant_truncates", "rintf(a[j] / sc)", "truncf(a[j] / sc)"),
+    ("quant_signed_max", "float v = fabsf(a[j]);", "float v = a[j];"),
+    ("quant_zero_group_scale", ": 1.0f;", ": 0.0f;"),
+    ("quant_group_offset", "const float *a = A + (size_t)m * K + (size_t)g * G;",
+     "const float *a = A + (size_t)m * K;"),
 ]
 
 

@@ -158,12 +158,21 @@ def make_activations(rng, M, K, G, afmt, outlier_frac=0.0, outlier_mult=50.0, in
     if afmt == "bf16":
         return f32_to_bf16_bits(a32), None
     if afmt == "i8":
-        ag = a32.reshape(M, K // G, G).astype(np.float64)
-        mx = np.abs(ag).max(axis=2)
-        sc = np.where(mx > 0, mx / 127.0, 1.0).astype(np.float32)
-        q = np.clip(np.rint(ag / sc[:, :, None].astype(np.float64)), -127, 127).astype(np.int8)
-        return q.reshape(M, K), sc
+        return quantize_i8(a32, G)
     raise ValueError(afmt)
+
+
+def quantize_i8(a32, G):
+    """int8 codes and float32 scales for pre-quantized activation inputs:
+    per (row, group) scale = max|a| / 127 (1 for zeros), code =
+    clamp(rint(a / scale), -127, 127), worked in float64 with the scale
+    rounded to float32 (an input recipe; not the kernels' arithmetic)."""
+    M, K = a32.shape
+    ag = np.asarray(a32, np.float32).reshape(M, K // G, G).astype(np.float64)
+    mx = np.abs(ag).max(axis=2)
+    sc = np.where(mx > 0, mx / 127.0, 1.0).astype(np.float32)
+    q = np.clip(np.rint(ag / sc[:, :, None].astype(np.float64)), -127, 127).astype(np.int8)
+    return q.reshape(M, K), sc
 
 
 def make_problem(M, N, K, G, prec, has_zp=False, seed=0, *, scale_lo=1e-3, scale_hi=1e-2,

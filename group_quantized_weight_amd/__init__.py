@@ -23,11 +23,13 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "qgemm.h")
 # status codes, precisions and paths (include/qgemm.h)
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EALIGN, EHIP = 0, -1, -2, -3, -4, -5
 W4_A_BF16, W4_A_F32, W8_A_F32, W4_A_I8, W8_A_I8, W4_A_BF16_OF32 = 1, 2, 3, 4, 5, 6
+W4_A_F32_DQ8, W8_A_F32_DQ8 = 7, 8
 PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SMALL = -1, 0, 1, 2
 
 _PREC_FMT = {1: ("w4", "bf16", "bf16", "bf16"), 2: ("w4", "f32", "f32", "f32"),
              3: ("w8", "f32", "f32", "f32"), 4: ("w4", "i8", "f32", "f32"),
-             5: ("w8", "i8", "f32", "f32"), 6: ("w4", "bf16", "bf16", "f32")}
+             5: ("w8", "i8", "f32", "f32"), 6: ("w4", "bf16", "bf16", "f32"),
+             7: ("w4", "f32", "f32", "f32"), 8: ("w8", "f32", "f32", "f32")}
 
 
 class QGemmError(RuntimeError):
@@ -67,6 +69,8 @@ def lib():
             L.qgemm_run.argtypes = run_args
             L.qgemm_run_ex.restype = c_int
             L.qgemm_run_ex.argtypes = run_args + [c_int, c_int]
+            L.qgemm_quantize_activations.restype = c_int
+            L.qgemm_quantize_activations.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
             L.qgemm_strerror.restype = ctypes.c_char_p
             L.qgemm_strerror.argtypes = [c_int]
             _lib = L
@@ -150,6 +154,22 @@ def workspace(nbytes: int, device):
 def out_dtype(prec: int):
     import torch
     return torch.bfloat16 if _PREC_FMT[prec][3] == "bf16" else torch.float32
+
+
+def quantize_activations(A, G: int, Aq=None, a_scales=None, stream=None):
+    """(Aq int8 [M, K], a_scales float32 [M, K/G]): per-group dynamic int8
+    quantization of float32 activations A [M, K] (see include/qgemm.h)."""
+    import torch
+    M, K = A.shape
+    if Aq is None:
+        Aq = torch.empty((M, K), dtype=torch.int8, device=A.device)
+    if a_scales is None:
+        a_scales = torch.empty((M, K // G if G > 0 else 0), dtype=torch.float32, device=A.device)
+    st = lib().qgemm_quantize_activations(_ptr(A), M, K, G, _ptr(Aq), _ptr(a_scales),
+                                          stream if stream is not None else _stream(A.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_quantize_activations")
+    return Aq, a_scales
 
 
 def run(A, w_packed, scales, *, N: int, G: int, prec: int, zeros=None, a_scales=None, out=None,

@@ -75,6 +75,9 @@ hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, h
 hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np,
                        hipStream_t stream);
+// Aq[m][k], a_scale[m][k / G] = per-group int8 quantization of A[M][K]
+// (float32); G in {32, 128}, K % G == 0, A 16-byte and Aq 4-byte aligned.
+hipError_t launch_quant(const float *A, int8_t *Aq, float *a_scale, int M, int K, int G, hipStream_t stream);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t stream);

@@ -7,7 +7,9 @@
 // float32 partials to the workspace and a reduction kernel adds them in the
 // fixed order z = 0..nsplit-1 (the kernel boundary orders the two; no
 // device-wide fences or atomics are used). The MFMA path adds a pre-pass
-// that writes per-group activation sums to the start of the workspace.
+// that writes per-group activation sums to the workspace; precisions 7 and 8
+// add a pre-pass that quantizes float32 activations to int8 codes and
+// per-group scales in the workspace, which the int8 GEMV then reads.
 //
 // Dispatch follows the roofline argument of the page
 // "quantization-and-fused-kernels" (arganzheng.life), section 三.2: at small
@@ -34,6 +36,7 @@ namespace {
 
 struct Formats {
   int w, a, s, o;
+  bool dq = false;  // float32 activations quantized to int8 per group inside the call
 };
 
 bool prec_formats(int prec, Formats &f) {
@@ -44,6 +47,8 @@ bool prec_formats(int prec, Formats &f) {
     case QG_W4_A_I8: f = {W4, A_I8, S_F32, O_F32}; return true;
     case QG_W8_A_I8: f = {W8, A_I8, S_F32, O_F32}; return true;
     case QG_W4_A_BF16_OF32: f = {W4, A_BF16, S_BF16, O_F32}; return true;
+    case QG_W4_A_F32_DQ8: f = {W4, A_I8, S_F32, O_F32, true}; return true;
+    case QG_W8_A_F32_DQ8: f = {W8, A_I8, S_F32, O_F32, true}; return true;
     default: return false;
   }
 }
@@ -83,9 +88,13 @@ struct Plan {
   int tiles_x = 1, tiles_y = 1;
   int units = 1;          // groups (GEMV) or 128-k chunks (GEMM) along K
   size_t lds = 0;
-  size_t asum = 0;        // MFMA path: bytes of activation sums at the start of the workspace
+  size_t codes = 0;       // in-call activation quantization: bytes of int8 codes, then
+  size_t ascale = 0;      //   of their float32 scales, at the start of the workspace
+  size_t asum = 0;        // MFMA path: bytes of activation sums (after the above)
   size_t ws = 0;
 };
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 size_t padded_rows(int M) { return ((size_t)M + kGemmBM - 1) / kGemmBM * kGemmBM; }
 
@@ -167,7 +176,11 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   }
   p.nsplit = ns;
   p.asum = path == QG_PATH_GEMM ? gemm_asum_bytes(M, K) : 0;
-  p.ws = p.asum + (p.nsplit > 1 ? (size_t)p.nsplit * M * Np * 4 : 0);
+  if (f.dq) {
+    p.codes = round256((size_t)M * K);
+    p.ascale = round256((size_t)M * (K / G) * 4);
+  }
+  p.ws = p.codes + p.ascale + p.asum + (p.nsplit > 1 ? (size_t)p.nsplit * M * Np * 4 : 0);
   return QG_OK;
 }
 
@@ -245,10 +258,11 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
   if (st != QG_OK) return st;
   if (M == 0) return QG_OK;
   if (!A || !w_packed || !scales || !out) return QG_EINVAL;
-  if (f.a == A_I8 && !a_scales) return QG_EINVAL;
+  const bool given_scales = f.a == A_I8 && !f.dq;
+  if (given_scales && !a_scales) return QG_EINVAL;
   if (has_zp && !zeros) return QG_EINVAL;
   if (!aligned16(A) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(out) ||
-      (f.a == A_I8 && !aligned16(a_scales)) || (has_zp && !aligned16(zeros)))
+      (given_scales && !aligned16(a_scales)) || (has_zp && !aligned16(zeros)))
     return QG_EALIGN;
   Plan p;
   st = make_plan(M, N, K, group, f, force_path, force_nsplit, p);
@@ -258,9 +272,17 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     if (!aligned16(workspace)) return QG_EALIGN;
   }
   hipStream_t s = (hipStream_t)stream;
-  float *partial = p.nsplit > 1 ? (float *)((char *)workspace + p.asum) : nullptr;
+  char *ws = (char *)workspace;
+  float *partial = p.nsplit > 1 ? (float *)(ws + p.codes + p.ascale + p.asum) : nullptr;
   const int Np = (int)padded_cols(N);
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  if (f.dq) {
+    // the product then reads the codes and scales this writes
+    e = launch_quant((const float *)A, (int8_t *)ws, (float *)(ws + p.codes), M, K, group, s);
+    if (e != hipSuccess) return QG_EHIP;
+    A = ws;
+    a_scales = ws + p.codes;
+  }
   if (p.path == QG_PATH_GEMV) {
     GemvArgs a;
     a.A = A;
@@ -295,7 +317,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
     a.out = out;
     a.partial = partial;
-    a.asum = (float *)workspace;
+    a.asum = (float *)(ws + p.codes + p.ascale);
     a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np; a.Mp = (int)padded_rows(M);
     a.nchunks = K / kGemmKC;
     a.nsplit = p.nsplit;
@@ -310,6 +332,20 @@ int qgemm_run(int M, int N, int K, int group, int prec, int has_zp, const void *
               void *out, void *workspace, size_t workspace_bytes, void *stream) {
   return qgemm_run_ex(M, N, K, group, prec, has_zp, A, a_scales, w_packed, scales, zeros, out, workspace,
                       workspace_bytes, stream, QG_PATH_AUTO, 0);
+}
+
+int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq, void *a_scales,
+                               void *stream) {
+  if (M < 0 || K <= 0) return QG_EINVAL;
+  if (group != 32 && group != 128) return QG_EUNSUPPORTED;
+  if (K % group != 0) return QG_EINVAL;
+  if ((size_t)M * K / 1024 > (size_t)INT_MAX) return QG_EUNSUPPORTED;  // grid of 256 x 4 elements
+  if (M == 0) return QG_OK;
+  if (!A || !Aq || !a_scales) return QG_EINVAL;
+  if (!aligned16(A) || !aligned16(Aq) || !aligned16(a_scales)) return QG_EALIGN;
+  const hipError_t e = launch_quant((const float *)A, (int8_t *)Aq, (float *)a_scales, M, K, group,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 
 const char *qgemm_strerror(int status) {

@@ -62,8 +62,13 @@ enum {
     QG_W8_A_F32 = 3,       /* int8  | float32               | float32 | float32 */
     QG_W4_A_I8 = 4,        /* int4  | int8 + a_scales f32   | float32 | float32 */
     QG_W8_A_I8 = 5,        /* int8  | int8 + a_scales f32   | float32 | float32 */
-    QG_W4_A_BF16_OF32 = 6  /* int4  | bf16                  | bf16    | float32 */
+    QG_W4_A_BF16_OF32 = 6, /* int4  | bf16                  | bf16    | float32 */
+    QG_W4_A_F32_DQ8 = 7,   /* int4  | float32, quantized    | float32 | float32 */
+    QG_W8_A_F32_DQ8 = 8    /* int8  | float32, quantized    | float32 | float32 */
 };
+/* Precisions 7 and 8 take float32 activations and quantize them inside the
+ * call, exactly as qgemm_quantize_activations does, into the workspace; the
+ * product then runs as precision 4 / 5 on those codes and scales. */
 
 /* Paths (for qgemm_plan / qgemm_run_ex). */
 enum {
@@ -103,9 +108,10 @@ int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, 
 
 /*
  * Device workspace bytes qgemm_run needs for this problem (0: none, and the
- * workspace pointer may be NULL). The workspace holds, on the MFMA path, the
- * float32 activation sums per (group, row) of a pre-pass, and the float32
- * partial sums of a K-split; its contents before a call do not matter. Calls
+ * workspace pointer may be NULL). The workspace holds the int8 codes and
+ * float32 scales of in-call activation quantization (precisions 7 and 8),
+ * on the MFMA path the float32 activation sums per (group, row) of a
+ * pre-pass, and the float32 partial sums of a K-split; its contents before a call do not matter. Calls
  * that share a workspace must not run concurrently.
  */
 size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec);
@@ -125,10 +131,11 @@ int qgemm_plan(int M, int N, int K, int group, int prec, int force_path, int for
  * out = the group-quantized product described at the top of this file.
  * Enqueues one kernel, or two when K is split (nsplit > 1: the partial sums
  * of the K-slices, then their fixed-order reduction); the MFMA path first
- * enqueues a pre-pass that sums each group of activations.
+ * enqueues a pre-pass that sums each group of activations, and precisions 7
+ * and 8 first enqueue the activation quantization.
  *   M >= 0 (M == 0 is a no-op), N >= 1, K >= 1, K % group == 0, group in {32, 128}.
  *   A:         activations [M][K] (bf16 / float32 / int8 by prec)
- *   a_scales:  float32 [M][K/G] for *_A_I8, else NULL
+ *   a_scales:  float32 [M][K/G] for *_A_I8, else NULL (unused)
  *   w_packed:  output of qgemm_pack
  *   scales:    [K/G][N] (bf16 for prec 1 and 6, else float32)
  *   zeros:     uint32 [K/G][N/8] when has_zp (int4 only, N % 8 == 0), else NULL
@@ -147,6 +154,28 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
                  const void *a_scales, const void *w_packed, const void *scales,
                  const void *zeros, void *out, void *workspace, size_t workspace_bytes,
                  void *stream, int force_path, int force_nsplit);
+
+/*
+ * Dynamic per-group int8 quantization of float32 activations: the absmax ->
+ * scale -> round -> saturate step that precedes an int8-activation product,
+ * as in the per-token dynamic quantization kernel of the page
+ * "quantization-and-fused-kernels" (arganzheng.life), section 四.5, here per
+ * (row, group of G consecutive k) with int8 codes, the activation format of
+ * the page "04 · 分组量化 GEMM 内核" (developer.aliyun.com), section 二.
+ * For every row m < M and group g < K/G, in float32:
+ *     a_scales[m][g] = max_{k in g} |A[m][k]| / 127, or 1 when that max is 0
+ *     Aq[m][k]       = clamp(rint(A[m][k] / a_scales[m][g]), -127, 127)
+ * with the division correctly rounded and rint rounding halves to even.
+ *   A:        float32 [M][K] (device, read)
+ *   Aq:       int8 [M][K] (device, written)
+ *   a_scales: float32 [M][K/G] (device, written)
+ * Its outputs are the A and a_scales of a QG_W4_A_I8 / QG_W8_A_I8 call.
+ * M >= 0 (0 is a no-op), K >= 1, K % group == 0, group in {32, 128}; all three
+ * pointers 16-byte aligned; non-finite inputs give unspecified codes. One
+ * kernel, enqueued on `stream`; nothing is allocated.
+ */
+int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq, void *a_scales,
+                               void *stream);
 
 /* Human-readable text of a status code. */
 const char *qgemm_strerror(int status);

@@ -130,7 +130,13 @@ def int_partials(M, N, K, G, wfmt, has_zp, Aq, W, Z, rows=None, cols=None, lib=N
 
 
 def for_problem(p, rows=None, cols=None, lib=None):
-    """Oracle (ref, bound) of a workloads.Problem."""
+    """Oracle (ref, bound) of a workloads.Problem. For a problem whose float32
+    activations are quantized inside the call (p.dq), the product is that of
+    the int8 codes and scales quantize_act gives."""
+    if getattr(p, "dq", False):
+        Aq, sc = quantize_act(p.A, p.G, lib=lib)
+        return qgemm(p.M, p.N, p.K, p.G, p.wfmt, "i8", p.sfmt, p.has_zp, Aq, sc, p.W, p.S, p.Z,
+                     rows=rows, cols=cols, lib=lib)
     return qgemm(p.M, p.N, p.K, p.G, p.wfmt, p.afmt, p.sfmt, p.has_zp, p.A, p.a_scale, p.W, p.S,
                  p.Z, rows=rows, cols=cols, lib=lib)
 

@@ -38,7 +38,13 @@ def test_layout_and_sizes():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(prec=0), qg.EUNSUPPORTED),
-    (dict(prec=7), qg.EUNSUPPORTED),
+    (dict(prec=9), qg.EUNSUPPORTED),
+    (dict(prec=qg.W4_A_F32_DQ8, zp=1, Z=P, N=250), qg.EUNSUPPORTED),
+    (dict(prec=qg.W8_A_F32_DQ8, zp=1, Z=P), qg.EUNSUPPORTED),
+    (dict(prec=qg.W4_A_F32_DQ8, A=MIS), qg.EALIGN),
+    (dict(prec=qg.W8_A_F32_DQ8, K=100), qg.EINVAL),
+    (dict(prec=qg.W4_A_F32_DQ8, path=qg.PATH_GEMM, M=300, G=128), qg.EUNSUPPORTED),
+    (dict(prec=qg.W4_A_F32_DQ8), qg.EWORKSPACE),      # its codes and scales live in the workspace
     (dict(M=-1), qg.EINVAL),
     (dict(N=0), qg.EINVAL),
     (dict(K=0), qg.EINVAL),
@@ -92,6 +98,23 @@ def test_workspace_checked_before_launch():
     assert qg.plan(1, 28672, 4096, 128, qg.W4_A_BF16)[1:] == (1, 0)
 
 
+def test_quantize_validation():
+    L = qg.lib()
+    q = lambda A=P, M=4, K=256, G=32, Aq=P2, s=P: L.qgemm_quantize_activations(A, M, K, G, Aq, s, None)
+    assert q(M=0, A=None, Aq=None, s=None) == qg.OK       # no-op
+    assert q(M=-1) == qg.EINVAL
+    assert q(K=0) == qg.EINVAL
+    assert q(G=64) == qg.EUNSUPPORTED
+    assert q(K=160, G=128) == qg.EINVAL                   # K % G != 0
+    assert q(A=None) == qg.EINVAL
+    assert q(Aq=None) == qg.EINVAL
+    assert q(s=None) == qg.EINVAL
+    assert q(A=MIS) == qg.EALIGN
+    assert q(Aq=MIS) == qg.EALIGN
+    assert q(s=MIS) == qg.EALIGN
+    assert q(M=1 << 30, K=1 << 12, G=128) == qg.EUNSUPPORTED   # beyond one grid
+
+
 def test_pack_validation():
     L = qg.lib()
     assert L.qgemm_pack(None, P, 64, 8, qg.W4_A_BF16, None) == qg.EINVAL
@@ -101,7 +124,9 @@ def test_pack_validation():
 
 
 CASES = [(1, 28672, 4096, 128, 1), (8, 28672, 8192, 128, 1), (1, 128256, 4096, 128, 1),
-         (32, 11264, 2048, 32, 2), (32, 11000, 2048, 32, 5), (1, 256, 256, 32, 2)]
+         (32, 11264, 2048, 32, 2), (32, 11000, 2048, 32, 5), (1, 256, 256, 32, 2),
+         (1, 11264, 2048, 32, 7), (32, 11264, 2048, 32, 8), (32, 11000, 2048, 32, 7),
+         (300, 4096, 4096, 128, 8)]
 CASES += [(M, 4096, 4096, 128, 1) for M in (1, 16, 64, 256, 1024, 4096)]
 
 
@@ -113,6 +138,14 @@ def test_plan_is_pure_and_consistent(M, N, K, G, prec):
     path, ns, ws = a
     assert 1 <= ns <= K // G
     assert ws == qg.lib().qgemm_workspace_bytes(M, N, K, G, prec)
+    if prec in (7, 8):
+        # int8 codes [M][K] and float32 scales [M][K/G] (each rounded up to 256
+        # bytes), then the plan of the same product on int8 activations
+        assert (path, ns) == qg.plan(M, N, K, G, prec - 3)[:2]
+        pre = -(-M * K // 256) * 256 + -(-M * (K // G) * 4 // 256) * 256
+        assert ws == pre + qg.plan(M, N, K, G, prec - 3)[2]
+        assert path == qg.PATH_GEMV
+        return
     if path in (qg.PATH_GEMV, qg.PATH_SMALL):
         assert (ws == 0) == (ns == 1)
         assert ws == (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)

@@ -26,7 +26,7 @@ def _gpu():
 
 
 PREC_ZP = [(1, False), (1, True), (2, False), (2, True), (3, False), (4, False), (4, True),
-           (5, False), (6, False), (6, True)]
+           (5, False), (6, False), (6, True), (7, False), (7, True), (8, False)]
 
 
 # ---------------------------------------------------------------------------

@@ -37,9 +37,13 @@ PREC = {
     4: ("w4", "i8", "f32", "f32"),       # QG_W4_A_I8
     5: ("w8", "i8", "f32", "f32"),       # QG_W8_A_I8
     6: ("w4", "bf16", "bf16", "f32"),    # QG_W4_A_BF16_OF32
+    7: ("w4", "f32", "f32", "f32"),      # QG_W4_A_F32_DQ8: float32 activations, quantized in the call
+    8: ("w8", "f32", "f32", "f32"),      # QG_W8_A_F32_DQ8
 }
 PREC_NAME = {1: "W4_A_BF16", 2: "W4_A_F32", 3: "W8_A_F32", 4: "W4_A_I8",
-             5: "W8_A_I8", 6: "W4_A_BF16_OF32"}
+             5: "W8_A_I8", 6: "W4_A_BF16_OF32", 7: "W4_A_F32_DQ8", 8: "W8_A_F32_DQ8"}
+# precisions whose float32 activations the library quantizes to int8 itself
+DQ8_PRECS = (7, 8)
 
 
 # ----------------------------------------------------------------------------
@@ -134,6 +138,11 @@ class Problem:
     def ofmt(self):
         return PREC[self.prec][3]
 
+    @property
+    def dq(self):
+        """True when the product runs on int8 codes of the float32 A."""
+        return self.prec in DQ8_PRECS
+
 
 def make_activations(rng, M, K, G, afmt, outlier_frac=0.0, outlier_mult=50.0, integer_range=None):
     """Activations ~ N(0,1) (or integers uniform in [-r, r]).
@@ -215,12 +224,19 @@ _register(_cfg("decode_w4a16_g128", 1, 28672, 4096, 128, 1, False, 1020,
                outlier_frac=1e-3, outlier_mult=50.0))
 # Q8_0 / Q4_0-style group GEMM, G=32, K=2048
 _seed = 1030
-for wname, prec_f, prec_i in (("q8_0", 3, 5), ("q4_0", 2, 4)):
+for wname, prec_f, prec_i, prec_d in (("q8_0", 3, 5, 8), ("q4_0", 2, 4, 7)):
     for N in (11264, 11000):
         for M in (1, 32):
             for aname, prec in (("f32", prec_f), ("i8", prec_i)):
                 _register(_cfg(f"{wname}_m{M}_n{N}_a{aname}", M, N, 2048, 32, prec, False, _seed))
                 _seed += 1
+# the same layers with float32 activations that the call quantizes to int8
+_seed = 1090
+for wname, prec in (("q8_0", 8), ("q4_0", 7)):
+    for N in (11264, 11000):
+        for M in (1, 32):
+            _register(_cfg(f"{wname}_m{M}_n{N}_adq8", M, N, 2048, 32, prec, False, _seed))
+            _seed += 1
 # prefill crossover sweep, W4A16 g128 symmetric, K = N = 4096
 for i, M in enumerate((1, 16, 64, 256, 1024, 4096)):
     _register(_cfg(f"prefill_w4a16_m{M}", M, 4096, 4096, 128, 1, False, 1060 + i))

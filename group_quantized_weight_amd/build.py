@@ -14,8 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemm.so")
-SOURCES = ["qgemm_api.hip", "pack.hip", "gemv.hip", "gemm.hip", "gemm_small.hip", "reduce.hip",
-           "quant.hip"]
+SOURCES = ["qgemm_api.hip", "pack.hip", "gemv.hip", "gemv_i8.hip", "gemm.hip", "gemm_small.hip",
+           "reduce.hip", "quant.hip"]
 ARCH = "gfx950"
 
 

@@ -70,6 +70,9 @@ struct SmallArgs {
 // launch status; the dispatcher has validated every argument before.
 hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, const GemvArgs &a,
                        dim3 grid, size_t lds_bytes, hipStream_t stream);
+// int8 activations (float32 scales and output)
+hipError_t launch_gemv_i8(int wfmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds_bytes,
+                          hipStream_t stream);
 hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t stream);
 // mb = ceil(M / 16) row blocks; grid (Np / 64, nsplit)
 hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t stream);

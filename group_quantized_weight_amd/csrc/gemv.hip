@@ -1,4 +1,5 @@
-// GEMV path of the group-quantized GEMM: vector-ALU kernel for small M.
+// GEMV path of the group-quantized GEMM: vector-ALU kernel for small M with
+// bf16 or float32 activations (int8 activations have their own kernel).
 //
 // Mapping (one workgroup = 4 waves = one 64-column tile of the packed layout):
 //   lane l       : columns 4 (l % 16) .. +3 of the tile and word-rows
@@ -28,12 +29,6 @@
 //   float32 activations: codes are split into bytes and converted with
 //     v_cvt_f32_ubyte (b = 0 for int4; b = 128 for int8 codes flipped to
 //     unsigned by xor 0x80).
-//   int8 activations: v_dot4_i32_i8 on byte codes, exact int32 per group
-//     (b = 0); the four lanes that share a column add their integer partials,
-//     so the whole group's integer dot is formed before it is scaled by
-//     a_scale * b_scale (the blockwise formula of developer.aliyun.com,
-//     section 二, and its remark that the group's integer dot must be finished
-//     before the scales are applied).
 // Then acc += s[g,n] * dot in float32 (the per-group scale of the teaching
 // GEMV, arganzheng.life section 九.4).
 //
@@ -93,7 +88,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 template <int WF, int AF>
 struct Stage {
   static constexpr int kpw = WF == W4 ? 8 : 4;  // k per packed word
-  static constexpr int bytes = AF == A_I8 ? kpw : (AF == A_BF16 ? 2 * kpw : 4 * kpw);
+  static constexpr int bytes = AF == A_BF16 ? 2 * kpw : 4 * kpw;
 };
 
 // Global -> registers: the activations of one word-row (kpw values). The
@@ -108,14 +103,8 @@ __device__ __forceinline__ void load_row(const void *A, size_t k, u32x4_v &c0, u
   } else if constexpr (AF == A_F32 && WF == W4) {
     c0 = *(const u32x4_v *)((const float *)A + k);
     c1 = *(const u32x4_v *)((const float *)A + k + 4);
-  } else if constexpr (AF == A_F32) {
-    c0 = *(const u32x4_v *)((const float *)A + k);
-  } else if constexpr (WF == W4) {
-    const u32x2_v v = *(const u32x2_v *)((const int8_t *)A + k);
-    c0[0] = v[0];
-    c0[1] = v[1];
   } else {
-    c0[0] = *(const uint32_t *)((const int8_t *)A + k);
+    c0 = *(const u32x4_v *)((const float *)A + k);
   }
 }
 
@@ -128,7 +117,7 @@ __device__ __forceinline__ void mask_row(bool ok, u32x4_v &c0, u32x4_v &c1) {
 }
 
 // Registers -> LDS in the order the dot products consume; returns the row's
-// activation sum (float bits, or int bits for int8 codes), summed in k order.
+// activation sum (float bits), summed in k order.
 template <int WF, int AF>
 __device__ __forceinline__ uint32_t store_row(unsigned char *dst, const u32x4_v &c0, const u32x4_v &c1) {
   if constexpr (AF == A_BF16) {
@@ -148,29 +137,12 @@ __device__ __forceinline__ uint32_t store_row(unsigned char *dst, const u32x4_v 
 #pragma unroll
     for (int j = 0; j < 4; ++j) s += __uint_as_float(c1[j]);
     return __float_as_uint(s);
-  } else if constexpr (AF == A_F32) {
+  } else {
     *(u32x4_v *)dst = c0;
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) s += __uint_as_float(c0[j]);
     return __float_as_uint(s);
-  } else if constexpr (WF == W4) {
-    // bytes k + {0,4,1,5} and k + {2,6,3,7}
-    const uint32_t lo = __builtin_amdgcn_perm(c0[1], c0[0], 0x05010400u);
-    const uint32_t hi = __builtin_amdgcn_perm(c0[1], c0[0], 0x07030602u);
-    *(uint2 *)dst = make_uint2(lo, hi);
-    int s = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += (int)(int8_t)(c0[0] >> (8 * j));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += (int)(int8_t)(c0[1] >> (8 * j));
-    return (uint32_t)s;
-  } else {
-    *(uint32_t *)dst = c0[0];
-    int s = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += (int)(int8_t)(c0[0] >> (8 * j));
-    return (uint32_t)s;
   }
 }
 
@@ -202,7 +174,7 @@ void gemv_kernel(GemvArgs a) {
   constexpr int IPB = GPB * IPG;                      // wave loads per batch
   constexpr int NB = kSmallBatches ? 2 : 1;           // batch slots in registers
   constexpr int SMAX = 2;                             // activation rows staged per thread up front
-  constexpr bool INT = AF == A_I8;
+  static_assert(AF == A_BF16 || AF == A_F32, "int8 activations use gemv_i8_kernel");
   constexpr int bias = AF == A_BF16 ? 128 : ((AF == A_F32 && WF == W8) ? 128 : 0);
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -365,16 +337,12 @@ void gemv_kernel(GemvArgs a) {
         if (gg + gi >= wgc) break;
         const int gl = wg0 + gg + gi;
         float pf[MB][4];
-        int pi[MB][4];
-        uint32_t cs[MB];  // this lane's share of the group's activation sum
+        float cs[MB];  // this lane's share of the group's activation sum
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-          cs[m] = 0;
+          cs[m] = 0.f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            pf[m][c] = 0.f;
-            pi[m][c] = 0;
-          }
+          for (int c = 0; c < 4; ++c) pf[m][c] = 0.f;
         }
 #pragma unroll
         for (int i = 0; i < IPG; ++i) {
@@ -382,8 +350,7 @@ void gemv_kernel(GemvArgs a) {
           const int lr = gl * RPG + 4 * i + lk;  // local word-row
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
-            const uint32_t rs = s_rsum[m * rows + lr];
-            cs[m] = INT ? (uint32_t)((int)cs[m] + (int)rs) : __float_as_uint(__uint_as_float(cs[m]) + __uint_as_float(rs));
+            cs[m] += __uint_as_float(s_rsum[m * rows + lr]);
           }
           const unsigned char *arow = s_act + (size_t)lr * AB;
           if constexpr (AF == A_BF16) {
@@ -454,31 +421,6 @@ void gemv_kernel(GemvArgs a) {
                 pf[m][c] = p;
               }
             }
-          } else if constexpr (AF == A_I8 && WF == W4) {
-            uint32_t lo[4], hi[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              lo[c] = wq[c] & 0x0F0F0F0Fu;
-              hi[c] = (wq[c] >> 4) & 0x0F0F0F0Fu;
-            }
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-              const uint2 av = *(const uint2 *)(arow + (size_t)m * rows * AB);
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                int p = pi[m][c];
-                p = __builtin_amdgcn_sdot4((int)lo[c], (int)av.x, p, false);
-                p = __builtin_amdgcn_sdot4((int)hi[c], (int)av.y, p, false);
-                pi[m][c] = p;
-              }
-            }
-          } else {  // A_I8, W8
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-              const uint32_t av = *(const uint32_t *)(arow + (size_t)m * rows * AB);
-#pragma unroll
-              for (int c = 0; c < 4; ++c) pi[m][c] = __builtin_amdgcn_sdot4((int)wq[c], (int)av, pi[m][c], false);
-            }
           }
         }
 
@@ -492,42 +434,13 @@ void gemv_kernel(GemvArgs a) {
           if constexpr (ZP) zz = (int)((zv[u][gi] >> (4 * ((ncol & 7) + c))) & 0xFu);
           zc[c] = bias + zz;
         }
-        if constexpr (INT) {
-          // the whole group's integer dot: add the 4 lanes (rows mod 4) sharing these columns
 #pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            int t = (int)cs[m];
-            t += __shfl_xor(t, 16);
-            t += __shfl_xor(t, 32);
-            cs[m] = (uint32_t)t;
+        for (int m = 0; m < MB; ++m)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              int v = pi[m][c];
-              v += __shfl_xor(v, 16);
-              v += __shfl_xor(v, 32);
-              pi[m][c] = v;
-            }
+          for (int c = 0; c < 4; ++c) {
+            const float d = pf[m][c] - (float)zc[c] * cs[m];
+            acc[m][c] = __builtin_fmaf(s[c], d, acc[m][c]);
           }
-          if (lk == 0) {
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-              const float asc = (m0 + m < a.M) ? a.a_scale[(size_t)(m0 + m) * a.ngroups + gb + gl] : 0.f;
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                const int d = pi[m][c] - zc[c] * (int)cs[m];
-                acc[m][c] = __builtin_fmaf(asc * s[c], (float)d, acc[m][c]);
-              }
-            }
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float d = pf[m][c] - (float)zc[c] * __uint_as_float(cs[m]);
-              acc[m][c] = __builtin_fmaf(s[c], d, acc[m][c]);
-            }
-        }
       }
     }
   }
@@ -613,11 +526,6 @@ hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, 
               : go_mb<W4, A_F32, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
   if (wfmt == W8 && afmt == A_F32)
     return go_mb<W8, A_F32, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
-  if (wfmt == W4 && afmt == A_I8)
-    return zp ? go_mb<W4, A_I8, S_F32, O_F32, true>(mb, G, a, grid, lds, st)
-              : go_mb<W4, A_I8, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
-  if (wfmt == W8 && afmt == A_I8)
-    return go_mb<W8, A_I8, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
   return hipErrorInvalidValue;
 }
 

@@ -295,8 +295,9 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np;
     a.ngroups = K / group;
     a.nsplit = p.nsplit;
-    e = launch_gemv(f.w, f.a, f.s, f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.mblocks, p.nsplit),
-                    p.lds, s);
+    const dim3 grid(p.tiles_x, p.mblocks, p.nsplit);
+    e = f.a == A_I8 ? launch_gemv_i8(f.w, has_zp != 0, p.mb, a, grid, p.lds, s)
+                    : launch_gemv(f.w, f.a, f.s, f.o, has_zp != 0, p.mb, a, grid, p.lds, s);
   } else if (p.path == QG_PATH_SMALL) {
     SmallArgs a;
     a.A = (const uint16_t *)A;

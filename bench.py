@@ -274,15 +274,16 @@ def bench(args):
     head, p = run_workload(args.workload, args.steps, args.warmup, args.mode)
     log(f"bench: {args.workload}: {head['ms'] * 1e3:.2f} us/step, {head['gbs']:.0f} GB/s")
 
-    gemm, _ = run_workload("prefill_w4a16_m1024", max(20, args.steps // 4), max(5, args.warmup // 2), args.mode)
+    # long enough runs (milliseconds) that the clocks have settled under MFMA load
+    gemm, _ = run_workload("prefill_w4a16_m1024", max(200, args.steps), max(20, args.warmup), args.mode)
     log(f"bench: prefill M=1024: {gemm['ms'] * 1e3:.1f} us, {gemm['tflops']:.1f} TFLOP/s")
 
     sweep = []
     if not args.no_sweep:
         for M in (1, 16, 64, 256, 1024, 4096):
-            st = 50 if M <= 256 else 20
-            r, _ = run_workload(f"prefill_w4a16_m{M}", st, 5, args.mode)
-            d_ms = dense_bf16(M, 4096, 4096, st, 5, args.mode)
+            st = 200 if M <= 1024 else 100
+            r, _ = run_workload(f"prefill_w4a16_m{M}", st, 20, args.mode)
+            d_ms = dense_bf16(M, 4096, 4096, st, 20, args.mode)
             sweep.append(dict(M=M, w4_us=r["ms"] * 1e3, bf16_us=d_ms * 1e3, w4_path=r["path"],
                               w4_nsplit=r["nsplit"], w4_tflops=r["tflops"], w4_gbs=r["gbs"],
                               bf16_tflops=2 * M * 4096 * 4096 / (d_ms * 1e-3) / 1e12,

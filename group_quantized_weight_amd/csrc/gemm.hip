@@ -6,20 +6,19 @@
 // (arganzheng.life), section 三.1: int4 tile -> unpack in registers -> matrix
 // instruction in bf16 with float32 accumulation; and the multi-stage
 // global-to-shared pipeline of its section 三.3, item 2):
-//   - workgroup tile 128 x 128, K in chunks of 128 = one group; 8 waves in
-//     two halves of 4 (each wave 128 rows x 32 columns = 8 x 2 tiles of
+//   - workgroup tile 128 x 128, K in chunks of 128 = one group; 4 waves, one
+//     per SIMD, each owning all 128 rows and 32 columns (8 x 2 tiles of
 //     v_mfma_f32_16x16x32_bf16, so each dequantized weight fragment feeds 8
-//     MFMAs). The halves take alternate chunks of the workgroup's K-range,
-//     so each SIMD runs two waves; at the end half 1 hands its accumulators
-//     to half 0 through LDS;
+//     MFMAs);
 //   - the chunk's activation tile, scales, zero-points and activation sums
 //     are copied by buffer loads straight into LDS (no registers on the way),
-//     into a ring of 4 stages (two chunks in use, two in flight). Each wave
+//     into a ring of 3 stages (one chunk in use, two in flight). Each wave
 //     waits for its own copies, then a barrier makes every wave's copies
 //     visible;
 //   - the activation tile's 16-byte pieces are XOR-swizzled with the row
 //     index, so the MFMA fragment reads of 16 rows hit 16 different 4-bank
-//     groups; rows past M are clamped to row M-1 (their results are dropped);
+//     groups; rows past M read zeros through the buffer's range check (their
+//     results are not written);
 //   - weights: each lane loads 8 bytes of packed words (2 adjacent columns x
 //     8 k) into registers one chunk ahead, and turns each word into four bf16
 //     pairs (128 + q) with one and-or per pair (bf16 magic number 0x4300,

@@ -48,6 +48,10 @@ def load(path: str = _LIB):
     lib.oracle_int_partials.argtypes = [c_int] * 6 + [vp, vp, vp, i64p, c_int, i64p, c_int, vp]
     lib.oracle_num_threads.argtypes = []
     lib.oracle_quantize_act.argtypes = [c_int, c_int, c_int, vp, vp, vp]
+    lib.oracle_fp8_value.argtypes = [c_int]
+    lib.oracle_fp8_value.restype = ctypes.c_double
+    lib.oracle_fp8_quantize.argtypes = [c_int, c_int, c_int, vp, vp, vp]
+    lib.oracle_fp8_gemm.argtypes = [c_int] * 4 + [vp] * 4 + [i64p, c_int, i64p, c_int, vp, vp]
     if path == _LIB:
         _lib = lib
     return lib
@@ -153,6 +157,43 @@ def quantize_act(A, G: int, lib=None):
     if st != 0:
         raise ValueError("oracle_quantize_act: bad shape")
     return Aq, sc
+
+
+def fp8_value(code: int, lib=None) -> float:
+    """Value of an 8-bit E4M3 ("fn") code (NaN for 0x7F and 0xFF)."""
+    return float((lib or load()).oracle_fp8_value(int(code)))
+
+
+def fp8_quantize(A_bf16_bits, block: int, lib=None):
+    """Dynamic FP8 quantization of bf16 activations (uint16 bits [M, K]):
+    returns (codes uint8 [M, K], scales float32 [M] for block 0 or [M, K/128]
+    for block 128) (see oracle.c)."""
+    lib = lib or load()
+    A = np.ascontiguousarray(A_bf16_bits, dtype=np.uint16)
+    M, K = A.shape
+    Aq = np.empty((M, K), np.uint8)
+    sc = np.empty((M,) if block == 0 else (M, K // 128 if block else 0), np.float32)
+    if lib.oracle_fp8_quantize(M, K, block, _ptr(A), _ptr(Aq), _ptr(sc)) != 0:
+        raise ValueError("oracle_fp8_quantize: bad shape")
+    return Aq, sc
+
+
+def fp8_gemm(M, N, K, scaling, Aq, a_scale, Wq, w_scale, rows=None, cols=None, lib=None):
+    """(ref, bound) float64 [len(rows), len(cols)] of the FP8 GEMM (see oracle.c)."""
+    lib = lib or load()
+    Aq, Wq = _c(Aq, np.uint8), _c(Wq, np.uint8)
+    a_scale, w_scale = _c(a_scale, np.float32), _c(w_scale, np.float32)
+    rows, nr = _idx(rows)
+    cols, nc = _idx(cols)
+    nr = M if rows is None else nr
+    nc = N if cols is None else nc
+    ref = np.zeros((nr, nc), dtype=np.float64)
+    bound = np.zeros((nr, nc), dtype=np.float64)
+    rc = lib.oracle_fp8_gemm(M, N, K, scaling, _ptr(Aq), _ptr(a_scale), _ptr(Wq), _ptr(w_scale),
+                             _ptr(rows), nr, _ptr(cols), nc, _ptr(ref), _ptr(bound))
+    if rc != 0:
+        raise ValueError(f"oracle_fp8_gemm rejected its arguments (rc={rc})")
+    return ref, bound
 
 
 def num_threads(lib=None) -> int:

@@ -304,6 +304,143 @@ int oracle_quantize_act(int M, int K, int G, const float *A, int8_t *Aq, float *
     return 0;
 }
 
+/*
+ * ---------------------------------------------------------------------------
+ * FP8 W8A8 (E4M3, "fn" variant), the variant the page
+ * "quantization-and-fused-kernels" (arganzheng.life) contrasts with W4A16 in
+ * section 四: both operands in FP8, products accumulated in float32, scales
+ * either outside the K sum (section 四.2) or per 128-wide K block inside it
+ * (section 四.3).
+ * ---------------------------------------------------------------------------
+ *
+ * Value of an 8-bit E4M3 code, from the format's definition (same page,
+ * section 二.1: 1 sign bit, 4 exponent bits, 3 mantissa bits, largest finite
+ * value 448, no infinities, and the pattern with exponent and mantissa all
+ * ones is NaN). Exponent bias 7; exponent field 0 holds the subnormals:
+ *   e == 0:  (-1)^s * (f / 8) * 2^(1 - 7)
+ *   e  > 0:  (-1)^s * (1 + f / 8) * 2^(e - 7)
+ * Returns NaN for 0x7F and 0xFF.
+ */
+double oracle_fp8_value(int code)
+{
+    const int s = (code >> 7) & 1, e = (code >> 3) & 0xF, f = code & 7;
+    if (e == 0xF && f == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)f / 8.0, 1 - 7) : ldexp(1.0 + (double)f / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/*
+ * A float32 value x with |x| <= 448 rounded to the nearest E4M3 code, ties to
+ * the code whose mantissa (lowest bit) is even; the sign is kept, so values
+ * that round to zero from below give negative zero (0x80). Found by comparing
+ * x with every finite non-negative code.
+ */
+static int fp8_round(float x)
+{
+    const int neg = signbit(x) != 0;
+    const double ax = fabs((double)x);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double d = fabs(oracle_fp8_value(c) - ax);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best | (neg << 7);
+}
+
+/*
+ * Dynamic FP8 quantization of bf16 activations A[M][K], after the per-token
+ * kernel of the same page, section 四.5 (absmax reduction, scale = max / 448,
+ * divide, saturate to +-448, round to FP8): with block == 0 one scale per row
+ * (per token, a_scale[M]); with block == 128 one scale per 128 consecutive
+ * elements of a row (the 1 x 128 activation blocks of section 四.3,
+ * a_scale[M][K/128]). In float32 (the precision the codes are decided in):
+ *   amax    = max |a| over the row or block         (exact)
+ *   a_scale = amax / 448, or 1 when amax == 0       (one rounding)
+ *   x       = a / a_scale                           (one rounding)
+ *   code    = fp8_round(clamp(x, -448, 448))
+ * The section's optional upper bound on the scale is not used, and its
+ * minimum scale (whose value the page does not give) is read as the guard of
+ * an all-zero row or block. Returns 0, or -1 on bad shapes.
+ */
+int oracle_fp8_quantize(int M, int K, int block, const uint16_t *A, uint8_t *Aq, float *a_scale)
+{
+    if (M < 0 || K <= 0 || !(block == 0 || block == 128) || (block && K % block != 0))
+        return -1;
+    const int len = block ? block : K;
+    const int nb = K / len;
+    for (int m = 0; m < M; ++m) {
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t *a = A + (size_t)m * K + (size_t)b * len;
+            float amax = 0.0f;
+            for (int j = 0; j < len; ++j) {
+                const float v = fabsf((float)bf16_to_double(a[j]));
+                if (v > amax)
+                    amax = v;
+            }
+            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            a_scale[(size_t)m * nb + b] = sc;
+            for (int j = 0; j < len; ++j) {
+                float x = (float)bf16_to_double(a[j]) / sc;
+                if (x > 448.0f)
+                    x = 448.0f;
+                if (x < -448.0f)
+                    x = -448.0f;
+                Aq[(size_t)m * K + (size_t)b * len + j] = (uint8_t)fp8_round(x);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * FP8 GEMM reference, fp64. Aq: E4M3 codes [M][K]; Wq: E4M3 codes [N][K]
+ * (each output channel's K codes contiguous). With v() = oracle_fp8_value:
+ *   scaling 0 (per-token x per-channel, section 四.2; a_scale[M], w_scale[N]):
+ *     ref[m,n] = a_scale[m] * w_scale[n] * sum_k v(Aq[m,k]) * v(Wq[n,k])
+ *   scaling 1 (per-block, section 四.3; a_scale[M][K/128], w_scale[N/128][K/128]):
+ *     ref[m,n] = sum_b a_scale[m,b] * w_scale[n/128,b] * sum_{k in b} v(Aq[m,k]) * v(Wq[n,k])
+ * bound[m,n] = the same sums of absolute values of the terms. k ascending;
+ * rows / cols select outputs (NULL: all). Returns 0, or -1 on bad arguments.
+ */
+int oracle_fp8_gemm(int M, int N, int K, int scaling, const uint8_t *Aq, const float *a_scale,
+                    const uint8_t *Wq, const float *w_scale, const int64_t *rows, int nrows,
+                    const int64_t *cols, int ncols, double *ref, double *bound)
+{
+    if (M < 0 || N <= 0 || K <= 0 || !(scaling == 0 || scaling == 1))
+        return -1;
+    if (scaling == 1 && (K % 128 != 0 || N % 128 != 0))
+        return -1;
+    if (check_indices(rows, nrows, M) || check_indices(cols, ncols, N))
+        return -1;
+    const int nb = K / 128;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int j = 0; j < ncols; ++j) {
+        const int n = col_index(cols, j);
+        for (int i = 0; i < nrows; ++i) {
+            const int m = row_index(rows, i);
+            double sum = 0.0, mag = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double sc;
+                if (scaling == 0)
+                    sc = (double)a_scale[m] * (double)w_scale[n];
+                else
+                    sc = (double)a_scale[(size_t)m * nb + k / 128] * (double)w_scale[(size_t)(n / 128) * nb + k / 128];
+                const double term = sc * oracle_fp8_value(Aq[(size_t)m * K + k]) * oracle_fp8_value(Wq[(size_t)n * K + k]);
+                sum += term;
+                mag += fabs(term);
+            }
+            ref[(size_t)i * ncols + j] = sum;
+            bound[(size_t)i * ncols + j] = mag;
+        }
+    }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -359,6 +359,162 @@ def check_quant_vs_generator(lib):
     assert np.array_equal(q[away], gq[away])
 
 
+# --------------------------------------------------------------------------
+# FP8 (E4M3) W8A8: format, dynamic quantization and GEMM
+# --------------------------------------------------------------------------
+FGOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fp8_cases.json")
+with open(FGOLDEN) as _f:
+    FP8 = json.load(_f)
+
+
+def _bf16_bits(x):
+    """float values that are exact in bf16 -> their bf16 bit patterns."""
+    b = np.asarray(x, np.float32).view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0), "value not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def check_fp8_decode_hand(lib):
+    for c in FP8["decode"]:
+        v = oracle.fp8_value(int(c["code"], 16), lib=lib)
+        assert v == c["value"] and np.signbit(v) == np.signbit(c["value"]), (c, v)
+    for c in FP8["nan_codes"]:
+        assert np.isnan(oracle.fp8_value(int(c, 16), lib=lib)), c
+
+
+def check_fp8_decode_vs_torch(lib):
+    """Every code against torch's float8_e4m3fn (a library routine)."""
+    import torch
+    t = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        v = oracle.fp8_value(c, lib=lib)
+        assert (np.isnan(v) and np.isnan(t[c])) or (v == t[c] and np.signbit(v) == np.signbit(t[c])), (c, v, t[c])
+
+
+def check_fp8_quant_hand(lib):
+    for case in FP8["quantize"]:
+        q, s = oracle.fp8_quantize(_bf16_bits(case["A"]), case["block"], lib=lib)
+        assert np.array_equal(q, np.array(case["codes"], np.uint8)), (case["id"], q)
+        assert np.array_equal(s, np.array(case["scales"], np.float32)), (case["id"], s)
+
+
+def check_fp8_round_vs_torch(lib):
+    """With a row maximum of 448 the scale is exactly 1, so the codes are the
+    round-to-nearest-even FP8 casts of the inputs themselves: compared with
+    torch's float32 -> float8_e4m3fn cast on every midpoint between adjacent
+    codes (each a tie), on their negatives, and on random bf16 values."""
+    import torch
+    vals = np.array([oracle.fp8_value(c, lib=lib) for c in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.Generator(np.random.PCG64(41))
+    rnd = rng.uniform(-448, 448, 2000)
+    rnd = np.concatenate([rnd, rng.uniform(-0.05, 0.05, 1000)])
+    x = np.concatenate([mids, -mids, rnd]).astype(np.float32)
+    x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)   # exact in bf16
+    row = np.concatenate([[448.0], x]).astype(np.float32)
+    q, s = oracle.fp8_quantize(_bf16_bits(row)[None, :], 0, lib=lib)
+    assert s[0] == 1.0
+    t = torch.from_numpy(row).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(q[0] != t)[0]
+    assert bad.size == 0, (bad[:5], row[bad[:5]], q[0][bad[:5]], t[bad[:5]])
+
+
+def check_fp8_quant_properties(lib):
+    """For per-token and 1 x 128 blocks: the scale is max|a| / 448 up to one
+    float32 rounding (1 for a zero row or block); the element of largest
+    magnitude maps to +-448 (0x7E / 0xFE); every decoded code times the scale
+    is within half a step of the input (a relative 2^-4 for normal values, an
+    absolute 2^-10 * scale below 2^-6)."""
+    rng = np.random.Generator(np.random.PCG64(43))
+    a = rng.standard_normal((4, 512)).astype(np.float32)
+    a[0, 7] = -60.0
+    a[1, 128:256] = 0.0
+    a[2] *= 1e-3
+    a = (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    dec = np.array([oracle.fp8_value(c, lib=lib) for c in range(256)])
+    for block in (0, 128):
+        q, s = oracle.fp8_quantize(_bf16_bits(a), block, lib=lib)
+        L = 512 if block == 0 else 128
+        s2 = s.reshape(4, -1)
+        for m in range(4):
+            for b in range(512 // L):
+                seg = a[m, b * L:(b + 1) * L].astype(np.float64)
+                sc = float(s2[m, b])
+                qs = q[m, b * L:(b + 1) * L]
+                amax = np.abs(seg).max()
+                if amax == 0:
+                    assert sc == 1.0 and np.all((qs & 0x7F) == 0), (block, m, b)
+                    continue
+                assert abs(sc * 448 - amax) <= amax * 2.0 ** -22, (block, m, b)
+                j = int(np.argmax(np.abs(seg)))
+                assert qs[j] == (0x7E if seg[j] > 0 else 0xFE), (block, m, b, qs[j])
+                x = seg / sc
+                err = np.abs(dec[qs] - x)
+                lim = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10)
+                assert np.all(err <= lim * (1 + 1e-6)), (block, m, b, float((err / lim).max()))
+
+
+def _fp8_frac(code):
+    """E4M3 code -> exact Fraction, through torch's decode (not the oracle's)."""
+    import torch
+    v = torch.tensor([code], dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).item()
+    return Fraction(v)
+
+
+def _fp8_codes(rng, shape):
+    """Random finite E4M3 codes (every code but the two NaNs)."""
+    c = rng.integers(0, 254, size=shape)
+    return np.where(c >= 0x7F, c + 1, c).astype(np.uint8)
+
+
+def check_fp8_gemm_brute(lib, scaling):
+    """Exact rational brute force of both scalings on small inputs, written
+    blockwise: out = sum_b sa * sb * sum_{k in b} a_k w_k."""
+    rng = np.random.Generator(np.random.PCG64(47 + scaling))
+    M, N, K = 3, 128 if scaling else 5, 256
+    Aq = _fp8_codes(rng, (M, K))
+    Wq = _fp8_codes(rng, (N, K))
+    if scaling == 0:
+        sa = rng.uniform(0.5, 2, M).astype(np.float32)
+        sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    else:
+        sa = rng.uniform(0.5, 2, (M, K // 128)).astype(np.float32)
+        sw = rng.uniform(1e-3, 1e-2, (N // 128, K // 128)).astype(np.float32)
+    cols = [0, 1, N - 1] if scaling else list(range(N))
+    ref, bound = oracle.fp8_gemm(M, N, K, scaling, Aq, sa, Wq, sw, cols=cols, lib=lib)
+    table = [_fp8_frac(c) if c not in (0x7F, 0xFF) else None for c in range(256)]
+    for i in range(M):
+        for jj, n in enumerate(cols):
+            tot = Fraction(0)
+            mag = Fraction(0)
+            for b in range(K // 128):
+                part = sum(table[Aq[i, k]] * table[Wq[n, k]] for k in range(128 * b, 128 * (b + 1)))
+                pmag = sum(abs(table[Aq[i, k]] * table[Wq[n, k]]) for k in range(128 * b, 128 * (b + 1)))
+                if scaling == 0:
+                    f = Fraction(float(sa[i])) * Fraction(float(sw[n]))
+                else:
+                    f = Fraction(float(sa[i, b])) * Fraction(float(sw[n // 128, b]))
+                tot += f * part
+                mag += f * pmag
+            assert abs(ref[i, jj] - float(tot)) <= 1e-12 * float(mag) + 1e-300, (scaling, i, n, ref[i, jj], float(tot))
+            assert abs(bound[i, jj] - float(mag)) <= 1e-12 * float(mag), (scaling, i, n)
+
+
+def check_fp8_blockwise_uniform(lib):
+    """Per-block scales that are the same in every block equal the per-token x
+    per-channel scaling with those scales (bitwise: the same fp64 terms)."""
+    rng = np.random.Generator(np.random.PCG64(53))
+    M, N, K = 4, 256, 384
+    Aq = _fp8_codes(rng, (M, K))
+    Wq = _fp8_codes(rng, (N, K))
+    sa = rng.uniform(0.5, 2, M).astype(np.float32)
+    sw_blk = rng.uniform(1e-3, 1e-2, N // 128).astype(np.float32)
+    r0, _ = oracle.fp8_gemm(M, N, K, 0, Aq, sa, Wq, np.repeat(sw_blk, 128), lib=lib)
+    r1, _ = oracle.fp8_gemm(M, N, K, 1, Aq, np.repeat(sa[:, None], K // 128, 1), Wq,
+                            np.repeat(sw_blk[:, None], K // 128, 1), lib=lib)
+    assert np.array_equal(r0, r1)
+
+
 def all_checks():
     """(name, callable(lib)) for every pin."""
     out = [(f"hand_{c['id']}", (lambda c: lambda lib: check_hand_case(lib, c))(c)) for c in HAND]
@@ -375,4 +531,10 @@ def all_checks():
     out += [(f"quant_hand_{c['id']}", (lambda c: lambda lib: check_quant_hand(lib, c))(c)) for c in QHAND]
     out += [("quant_properties", check_quant_properties), ("quant_power_of_two", check_quant_power_of_two),
             ("quant_vs_generator", check_quant_vs_generator)]
+    out += [("fp8_decode_hand", check_fp8_decode_hand), ("fp8_decode_vs_torch", check_fp8_decode_vs_torch),
+            ("fp8_quant_hand", check_fp8_quant_hand), ("fp8_round_vs_torch", check_fp8_round_vs_torch),
+            ("fp8_quant_properties", check_fp8_quant_properties),
+            ("fp8_gemm_brute_0", lambda lib: check_fp8_gemm_brute(lib, 0)),
+            ("fp8_gemm_brute_1", lambda lib: check_fp8_gemm_brute(lib, 1)),
+            ("fp8_blockwise_uniform", check_fp8_blockwise_uniform)]
     return out

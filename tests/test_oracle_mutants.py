@@ -46,6 +46,16 @@ MUTANTS = [
     ("quant_zero_group_scale", ": 1.0f;", ": 0.0f;"),
     ("quant_group_offset", "const float *a = A + (size_t)m * K + (size_t)g * G;",
      "const float *a = A + (size_t)m * K;"),
+    ("fp8_bias_6", "ldexp(1.0 + (double)f / 8.0, e - 7)", "ldexp(1.0 + (double)f / 8.0, e - 6)"),
+    ("fp8_subnormal_as_normal", "e == 0 ? ldexp((double)f / 8.0, 1 - 7)", "e == 0 ? ldexp(1.0 + (double)f / 8.0, 1 - 7)"),
+    ("fp8_ties_to_odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    ("fp8_sign_dropped", "return best | (neg << 7);", "return best;"),
+    ("fp8_divisor_240", "amax / 448.0f", "amax / 240.0f"),
+    ("fp8_block_offset", "const uint16_t *a = A + (size_t)m * K + (size_t)b * len;",
+     "const uint16_t *a = A + (size_t)m * K;"),
+    ("fp8_wscale_row", "(double)a_scale[m] * (double)w_scale[n]", "(double)a_scale[m] * (double)w_scale[m]"),
+    ("fp8_block_scale_k", "(double)w_scale[(size_t)(n / 128) * nb + k / 128]", "(double)w_scale[(size_t)(n / 128) * nb]"),
+    ("fp8_weight_transposed", "oracle_fp8_value(Wq[(size_t)n * K + k])", "oracle_fp8_value(Wq[(size_t)k * N + n])"),
 ]
 
 

@@ -423,19 +423,19 @@ int oracle_fp8_gemm(int M, int N, int K, int scaling, const uint8_t *Aq, const f
         const int n = col_index(cols, j);
         for (int i = 0; i < nrows; ++i) {
             const int m = row_index(rows, i);
-            double sum = 0.0, mag = 0.0;
+            double total = 0.0, total_abs = 0.0;
             for (int k = 0; k < K; ++k) {
                 double sc;
                 if (scaling == 0)
                     sc = (double)a_scale[m] * (double)w_scale[n];
                 else
                     sc = (double)a_scale[(size_t)m * nb + k / 128] * (double)w_scale[(size_t)(n / 128) * nb + k / 128];
-                const double term = sc * oracle_fp8_value(Aq[(size_t)m * K + k]) * oracle_fp8_value(Wq[(size_t)n * K + k]);
-                sum += term;
-                mag += fabs(term);
+                const double prod = sc * oracle_fp8_value(Aq[(size_t)m * K + k]) * oracle_fp8_value(Wq[(size_t)n * K + k]);
+                total += prod;
+                total_abs += fabs(prod);
             }
-            ref[(size_t)i * ncols + j] = sum;
-            bound[(size_t)i * ncols + j] = mag;
+            ref[(size_t)i * ncols + j] = total;
+            bound[(size_t)i * ncols + j] = total_abs;
         }
     }
     return 0;

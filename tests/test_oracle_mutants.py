@@ -43,7 +43,7 @@ MUTANTS = [
     ("quant_divisor_128", "amax / 127.0f", "amax / 128.0f"),
     ("quant_truncates", "rintf(a[j] / sc)", "truncf(a[j] / sc)"),
     ("quant_signed_max", "float v = fabsf(a[j]);", "float v = a[j];"),
-    ("quant_zero_group_scale", ": 1.0f;", ": 0.0f;"),
+    ("quant_zero_group_scale", "amax / 127.0f : 1.0f;", "amax / 127.0f : 0.0f;"),
     ("quant_group_offset", "const float *a = A + (size_t)m * K + (size_t)g * G;",
      "const float *a = A + (size_t)m * K;"),
     ("fp8_bias_6", "ldexp(1.0 + (double)f / 8.0, e - 7)", "ldexp(1.0 + (double)f / 8.0, e - 6)"),
@@ -56,6 +56,9 @@ MUTANTS = [
     ("fp8_wscale_row", "(double)a_scale[m] * (double)w_scale[n]", "(double)a_scale[m] * (double)w_scale[m]"),
     ("fp8_block_scale_k", "(double)w_scale[(size_t)(n / 128) * nb + k / 128]", "(double)w_scale[(size_t)(n / 128) * nb]"),
     ("fp8_weight_transposed", "oracle_fp8_value(Wq[(size_t)n * K + k])", "oracle_fp8_value(Wq[(size_t)k * N + n])"),
+    ("fp8_sum_sign", "total += prod;", "total -= prod;"),
+    ("fp8_zero_row_scale", "amax / 448.0f : 1.0f;", "amax / 448.0f : 0.0f;"),
+    ("fp8_bound_not_abs", "total_abs += fabs(prod);", "total_abs += prod;"),
 ]
 
 

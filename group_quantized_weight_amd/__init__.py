@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "qgemm.h")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EALIGN, EHIP = 0, -1, -2, -3, -4, -5
 W4_A_BF16, W4_A_F32, W8_A_F32, W4_A_I8, W8_A_I8, W4_A_BF16_OF32 = 1, 2, 3, 4, 5, 6
 W4_A_F32_DQ8, W8_A_F32_DQ8 = 7, 8
+FP8_PER_TOKEN, FP8_BLOCKWISE = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SMALL = -1, 0, 1, 2
 
 _PREC_FMT = {1: ("w4", "bf16", "bf16", "bf16"), 2: ("w4", "f32", "f32", "f32"),
@@ -69,6 +70,10 @@ def lib():
             L.qgemm_run.argtypes = run_args
             L.qgemm_run_ex.restype = c_int
             L.qgemm_run_ex.argtypes = run_args + [c_int, c_int]
+            L.qgemm_fp8_quantize.restype = c_int
+            L.qgemm_fp8_quantize.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
+            L.qgemm_fp8_gemm.restype = c_int
+            L.qgemm_fp8_gemm.argtypes = [c_int] * 4 + [vp] * 6
             L.qgemm_quantize_activations.restype = c_int
             L.qgemm_quantize_activations.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
             L.qgemm_strerror.restype = ctypes.c_char_p
@@ -170,6 +175,35 @@ def quantize_activations(A, G: int, Aq=None, a_scales=None, stream=None):
     if st != OK:
         raise QGemmError(st, "qgemm_quantize_activations")
     return Aq, a_scales
+
+
+def fp8_quantize(A, block: int = FP8_PER_TOKEN, stream=None):
+    """(codes uint8 [M, K], scales float32 [M] or [M, K/128]): dynamic E4M3
+    quantization of bf16 activations A [M, K] (see include/qgemm.h)."""
+    import torch
+    M, K = A.shape
+    Aq = torch.empty((M, K), dtype=torch.uint8, device=A.device)
+    sc = torch.empty((M,) if block == FP8_PER_TOKEN else (M, K // 128), dtype=torch.float32, device=A.device)
+    st = lib().qgemm_fp8_quantize(_ptr(A), M, K, block, _ptr(Aq), _ptr(sc),
+                                  stream if stream is not None else _stream(A.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_fp8_quantize")
+    return Aq, sc
+
+
+def fp8_gemm(Aq, a_scales, Wq, w_scales, scaling: int = FP8_PER_TOKEN, out=None, stream=None):
+    """bf16 [M, N] = FP8 GEMM of E4M3 codes Aq [M, K] and Wq [N, K] with
+    float32 scales (see include/qgemm.h)."""
+    import torch
+    M, K = Aq.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=Aq.device)
+    st = lib().qgemm_fp8_gemm(M, N, K, scaling, _ptr(Aq), _ptr(a_scales), _ptr(Wq), _ptr(w_scales), _ptr(out),
+                              stream if stream is not None else _stream(Aq.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_fp8_gemm")
+    return out
 
 
 def run(A, w_packed, scales, *, N: int, G: int, prec: int, zeros=None, a_scales=None, out=None,

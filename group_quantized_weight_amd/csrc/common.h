@@ -81,6 +81,12 @@ hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, i
 // Aq[m][k], a_scale[m][k / G] = per-group int8 quantization of A[M][K]
 // (float32); G in {32, 128}, K % G == 0, A 16-byte and Aq 4-byte aligned.
 hipError_t launch_quant(const float *A, int8_t *Aq, float *a_scale, int M, int K, int G, hipStream_t stream);
+// FP8 (E4M3) W8A8: dynamic quantization of bf16 activations (block 0: one
+// scale per row; 128: one per 128 elements) and the GEMM (scaling 0: per
+// token x per channel; 1: per 128 x 128 block).
+hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int M, int K, int block, hipStream_t stream);
+hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
+                           const float *w_scale, uint16_t *out, int M, int N, int K, hipStream_t stream);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t stream);

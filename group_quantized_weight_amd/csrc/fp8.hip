@@ -1,0 +1,269 @@
+// FP8 (E4M3) W8A8 path: dynamic activation quantization and the FP8 GEMM,
+// the variant the page "quantization-and-fused-kernels" (arganzheng.life)
+// contrasts with W4A16 in section 四: weights and activations both in FP8,
+// products accumulated in float32 on the matrix cores, scales either outside
+// the K sum (per token x per output channel, section 四.2) or per 128-wide K
+// block inside it, promoted into a float32 accumulator once per block
+// (section 四.3).
+//
+// E4M3 here is the OCP "fn" variant (bias 7, largest finite 448, no
+// infinities), the format gfx950's FP8 conversions and matrix instructions
+// use.
+#include "common.h"
+
+namespace qg {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_v;
+typedef __attribute__((ext_vector_type(8))) int i32x8_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(2))) float f32x2_v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kBufWord3 = 0x00020000;   // raw buffer: 32-bit data, no swizzle
+constexpr int kDead = (int)0x80000000u; // out-of-range buffer offset: zero result, no access
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// float32 -> E4M3 after the saturation of the page's conversion (section
+// 二.3: values are first clamped to +-448), rounded to nearest even by
+// v_cvt_pk_fp8_f32. Returns the two codes in the low 16 bits.
+__device__ __forceinline__ uint32_t to_fp8x2(float x0, float x1) {
+  x0 = fminf(fmaxf(x0, -448.f), 448.f);
+  x1 = fminf(fmaxf(x1, -448.f), 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
+}
+
+// 8 bf16 values (one 16-byte load) divided by the scale -> 8 codes (8 bytes).
+__device__ __forceinline__ uint2 quant8(u32x4_v v, float sc) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = to_fp8x2(bf16_lo(v[j]) / sc, bf16_hi(v[j]) / sc);
+  return make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+}
+
+__device__ __forceinline__ float absmax8(u32x4_v v) {
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[j])), fabsf(bf16_hi(v[j]))));
+  return m;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Dynamic quantization (section 四.5): scale = max|a| / 448 (1 for an all-zero
+// row or block), code = E4M3(clamp(a / scale, -448, 448)), all in float32
+// with the division correctly rounded.
+// ---------------------------------------------------------------------------
+
+// One 128-element block per 16 lanes (8 values per lane); the 16 lanes
+// combine their maxima with lane exchanges (max is exact in any order).
+__global__ __launch_bounds__(256) void fp8_quant_block_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aq,
+                                                             float *__restrict__ a_scale, size_t total) {
+  const size_t e = 8 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (e >= total) return;  // total % 128 == 0: a block's 16 lanes are all in range or all out
+  const u32x4_v v = *(const u32x4_v *)(A + e);
+  float amax = absmax8(v);
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  *(uint2 *)(Aq + e) = quant8(v, sc);
+  if ((threadIdx.x & 15) == 0) a_scale[e / 128] = sc;
+}
+
+// One workgroup per row (per-token scale): the row's maximum over the
+// workgroup (lane exchanges, then LDS), then a second pass over the row.
+__global__ __launch_bounds__(256) void fp8_quant_row_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aq,
+                                                           float *__restrict__ a_scale, int K) {
+  __shared__ float s_max[4];
+  const uint16_t *row = A + (size_t)blockIdx.x * K;
+  uint8_t *qrow = Aq + (size_t)blockIdx.x * K;
+  float amax = 0.f;
+  for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) amax = fmaxf(amax, absmax8(*(const u32x4_v *)(row + k)));
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) *(uint2 *)(qrow + k) = quant8(*(const u32x4_v *)(row + k), sc);
+  if (threadIdx.x == 0) a_scale[blockIdx.x] = sc;
+}
+
+hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int M, int K, int block,
+                            hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  if (block == 128) {
+    const size_t total = (size_t)M * K;
+    fp8_quant_block_kernel<<<(unsigned)((total / 8 + 255) / 256), 256, 0, st>>>(A, Aq, a_scale, total);
+  } else {
+    fp8_quant_row_kernel<<<M, 256, 0, st>>>(A, Aq, a_scale, K);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// FP8 GEMM: out[m][n] (bf16) from Aq [M][K] and Wq [N][K] (E4M3 codes).
+//   per-token scaling:  out = a_scale[m] * (w_scale[n] * sum_k a w)  (the
+//                       epilogue order of section 四.2: weight scale first)
+//   blockwise scaling:  out = sum_b (a_scale[m][b] * w_scale[n/128][b]) * P_b,
+//                       P_b = sum_{k in block b} a w, promoted in float32 per
+//                       block (section 四.3); a_scale [M][K/128],
+//                       w_scale [N/128][K/128].
+//
+// Workgroup tile 128 x 128, 4 waves (2 x 2), each 64 x 64 = 4 x 4 tiles of
+// v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3, float32 accumulate): one
+// instruction per tile per 128-wide K step, which is one scale block. The
+// K step's operand tiles (128 rows x 128 bytes each) are copied by buffer
+// loads straight into LDS, into a ring of 3 stages; the 16-byte pieces of a
+// row are XOR-swizzled with the row index (mod 8), so the fragment reads of
+// 8 consecutive rows hit 8 different bank groups. A lane's fragment is 32
+// consecutive bytes of k (k = 32 (lane / 16) .. +31) of row lane % 16, the
+// same k for both operands, so the instruction's sum runs over all 128 k.
+// ---------------------------------------------------------------------------
+constexpr int kF8Tile = 128;
+constexpr int kF8Row = 128;                       // bytes per operand row per K step
+constexpr int kF8OpBytes = kF8Tile * kF8Row;      // 16 KiB
+constexpr int kF8Stage = 2 * kF8OpBytes + 512;    // A, B, and the block's 128 activation scales
+constexpr int kF8Stages = 3;
+
+template <bool BLOCKWISE>
+__global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict__ Aq, const float *__restrict__ a_scale,
+                                                      const uint8_t *__restrict__ Wq, const float *__restrict__ w_scale,
+                                                      uint16_t *__restrict__ out, int M, int N, int K) {
+  __shared__ __align__(16) unsigned char s_ring[kF8Stages * kF8Stage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int m0 = blockIdx.y * kF8Tile, n0 = blockIdx.x * kF8Tile;
+  const int nsteps = K / 128;
+
+  // operand resources start at the tile's first row; rows past M (or N) fall
+  // outside num_records and read zeros
+  const int a_rows = M - m0 < kF8Tile ? M - m0 : kF8Tile;
+  const int b_rows = N - n0 < kF8Tile ? N - n0 : kF8Tile;
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(Aq + (size_t)m0 * K), (short)0, a_rows * K, kBufWord3);
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(Wq + (size_t)n0 * K), (short)0, b_rows * K, kBufWord3);
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(BLOCKWISE ? a_scale + (size_t)m0 * nsteps : a_scale), (short)0, BLOCKWISE ? a_rows * nsteps * 4 : 0,
+      kBufWord3);
+
+  // Copy j (0..3) of wave w moves LDS bytes 1 KiB * (4 j + w) of an operand
+  // tile: piece p = 64 (4 j + w) + lane of 16 bytes, row p / 8, physical slot
+  // p % 8 = lane % 8 holding logical piece (lane % 8) ^ (row % 8).
+  const int crow0 = 8 * wave + (lane >> 3);                      // + 32 j
+  const int cpiece = (lane & 7) ^ (crow0 & 7);
+  const int c_voff = crow0 * K + 16 * cpiece;                     // + 32 K j, + 128 step (SGPR)
+  auto copy_step = [&](int step, int stage, int dead) {
+    unsigned char *sb = s_ring + stage * kF8Stage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(sb + 1024 * (4 * j + wave)), 16,
+                                               (c_voff + 32 * K * j) | dead, step * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_void *)(sb + kF8OpBytes + 1024 * (4 * j + wave)), 16,
+                                               (c_voff + 32 * K * j) | dead, step * 128, 0, 0);
+    }
+    if constexpr (BLOCKWISE) {
+      // the step's 128 activation scales a_scale[m0 + r][step], 4 bytes per
+      // lane, by waves 0 and 1 (issued last: waiting for the 8 operand copies
+      // of a later step also waits for this one)
+      if (wave < 2) {
+        const int r = 64 * wave + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(q_rsrc, (lds_void *)(sb + 2 * kF8OpBytes + 256 * wave), 4,
+                                                 ((r * nsteps + step) * 4) | dead, 0, 0, 0);
+      }
+    }
+  };
+  // At the top of step i at most the next step's copies may be in flight:
+  // 8 operand copies per wave (waves 0 and 1 add one scale copy after them,
+  // which vmcnt(8) then also waits for).
+  constexpr int kCopies = 8;
+
+  auto frag = [&](const unsigned char *op, int row) {   // 32 bytes: pieces 2 lk, 2 lk + 1 of the row
+    const u32x4_v lo = *(const u32x4_v *)(op + row * kF8Row + 16 * ((2 * lk) ^ (row & 7)));
+    const u32x4_v hi = *(const u32x4_v *)(op + row * kF8Row + 16 * ((2 * lk + 1) ^ (row & 7)));
+    return (i32x8_v){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  f32x4_v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
+
+  copy_step(0, 0, 0);
+  copy_step(1, 1, nsteps > 1 ? 0 : kDead);
+  for (int i = 0; i < nsteps; ++i) {
+    // this step's copies are done when at most the next step's remain in flight
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
+    // every wave is past step i - 1: its stage takes step i + 2
+    copy_step(i + 2, (i + 2) % kF8Stages, i + 2 < nsteps ? 0 : kDead);
+    const unsigned char *sb = s_ring + (i % kF8Stages) * kF8Stage;
+    i32x8_v af[4], bfr[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      af[f] = frag(sb, 64 * wr + 16 * f + li);
+      bfr[f] = frag(sb + kF8OpBytes, 64 * wc + 16 * f + li);
+    }
+    if constexpr (BLOCKWISE) {
+      const float sb_w = w_scale[(size_t)(n0 / 128) * nsteps + i];   // one per workgroup tile and block
+      const float *sa = (const float *)(sb + 2 * kF8OpBytes);
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) {
+        const f32x4_v s4 = *(const f32x4_v *)(sa + 64 * wr + 16 * fm + 4 * lk) * sb_w;
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+          const f32x4_v p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[fm], bfr[fn], (f32x4_v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(s4[r], p[r], acc[fm][fn][r]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0, 127,
+                                                                         0, 127);
+    }
+  }
+
+  // ---- epilogue: tile (fm, fn) element r is row 16 fm + 4 lk + r, column 16 fn + li ----
+#pragma unroll
+  for (int fn = 0; fn < 4; ++fn) {
+    const int n = n0 + 64 * wc + 16 * fn + li;
+    if (n >= N) continue;
+    const float ws = BLOCKWISE ? 1.f : w_scale[n];
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 64 * wr + 16 * fm + 4 * lk + r;
+        if (m >= M) continue;
+        const float v = BLOCKWISE ? acc[fm][fn][r] : a_scale[m] * (ws * acc[fm][fn][r]);
+        const f32x2_v two = {v, 0.f};
+        out[(size_t)m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_v)) & 0xFFFFu);
+      }
+  }
+}
+
+hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
+                           const float *w_scale, uint16_t *out, int M, int N, int K, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid((N + kF8Tile - 1) / kF8Tile, (M + kF8Tile - 1) / kF8Tile);
+  if (scaling == 1)
+    fp8_gemm_kernel<true><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+  else
+    fp8_gemm_kernel<false><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace qg

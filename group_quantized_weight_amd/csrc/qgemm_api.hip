@@ -349,6 +349,37 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 
+int qgemm_fp8_quantize(const void *A, int M, int K, int block, void *Aq, void *a_scales, void *stream) {
+  if (M < 0 || K <= 0) return QG_EINVAL;
+  if (block != QG_FP8_PER_TOKEN && block != 128) return QG_EUNSUPPORTED;
+  if (K % (block ? block : 8) != 0) return QG_EINVAL;
+  if ((size_t)M * K / 2048 > (size_t)INT_MAX) return QG_EUNSUPPORTED;  // grid of 256 x 8 elements
+  if (M == 0) return QG_OK;
+  if (!A || !Aq || !a_scales) return QG_EINVAL;
+  if (!aligned16(A) || !aligned16(Aq) || !aligned16(a_scales)) return QG_EALIGN;
+  const hipError_t e = launch_fp8_quant((const uint16_t *)A, (uint8_t *)Aq, (float *)a_scales, M, K, block,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void *a_scales, const void *Wq,
+                   const void *w_scales, void *out, void *stream) {
+  if (M < 0 || N <= 0 || K <= 0) return QG_EINVAL;
+  if (scaling != QG_FP8_PER_TOKEN && scaling != QG_FP8_BLOCKWISE) return QG_EUNSUPPORTED;
+  if (K % 128 != 0) return QG_EINVAL;
+  if (scaling == QG_FP8_BLOCKWISE && N % 128 != 0) return QG_EUNSUPPORTED;
+  // buffer resources address 128 rows of K bytes, and 128 rows of K / 128 scales,
+  // with 32-bit offsets; the grid has ceil(M / 128) rows of workgroups
+  if ((size_t)128 * K > (size_t)INT_MAX || (M + 127) / 128 > 65535) return QG_EUNSUPPORTED;
+  if (M == 0) return QG_OK;
+  if (!Aq || !a_scales || !Wq || !w_scales || !out) return QG_EINVAL;
+  if (!aligned16(Aq) || !aligned16(a_scales) || !aligned16(Wq) || !aligned16(w_scales) || !aligned16(out))
+    return QG_EALIGN;
+  const hipError_t e = launch_fp8_gemm(scaling, (const uint8_t *)Aq, (const float *)a_scales, (const uint8_t *)Wq,
+                                       (const float *)w_scales, (uint16_t *)out, M, N, K, (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
 const char *qgemm_strerror(int status) {
   switch (status) {
     case QG_OK: return "ok";

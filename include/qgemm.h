@@ -177,6 +177,51 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
 int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq, void *a_scales,
                                void *stream);
 
+/*
+ * FP8 (E4M3) W8A8 -- the variant the page "quantization-and-fused-kernels"
+ * (arganzheng.life) contrasts with W4A16 in section 四: weights and
+ * activations both in FP8, products accumulated in float32 on the matrix
+ * cores. E4M3 is the OCP "fn" variant of section 二.1 (1 sign, 4 exponent,
+ * 3 mantissa bits, bias 7, largest finite 448, no infinities; 0x7F and 0xFF
+ * are NaN). Codes are stored one per byte.
+ */
+enum {
+    QG_FP8_PER_TOKEN = 0,  /* scales outside the K sum: a_scales [M], w_scales [N]   */
+    QG_FP8_BLOCKWISE = 1   /* per 128-wide K block: a_scales [M][K/128] (1 x 128 of
+                              the activations), w_scales [N/128][K/128] (128 x 128
+                              of the weights)                                         */
+};
+
+/*
+ * Dynamic FP8 quantization of bf16 activations (section 四.5): for every row
+ * (block == QG_FP8_PER_TOKEN, a_scales float32 [M]) or every 128 consecutive
+ * elements of a row (block == 128, a_scales float32 [M][K/128]), in float32:
+ *     a_scale = max |a| / 448, or 1 when that max is 0
+ *     code    = E4M3(clamp(a / a_scale, -448, 448)), rounded to nearest even
+ * with the division correctly rounded. The page's optional upper bound on the
+ * scale is not applied.
+ *   A:  bf16 [M][K] (device, read); Aq: E4M3 codes [M][K] (device, written).
+ * M >= 0 (0 is a no-op), K >= 1 with K % 8 == 0 (K % 128 == 0 for block 128);
+ * all pointers 16-byte aligned. One kernel on `stream`; nothing allocated.
+ */
+int qgemm_fp8_quantize(const void *A, int M, int K, int block, void *Aq, void *a_scales, void *stream);
+
+/*
+ * FP8 GEMM, out (bf16 [M][N], rounded once to nearest even) from
+ *   Aq: E4M3 codes [M][K]; Wq: E4M3 codes [N][K] (each output channel's K
+ *   codes contiguous); float32 scales as `scaling` says:
+ *   QG_FP8_PER_TOKEN (section 四.2): out[m][n] = a_scales[m] * (w_scales[n] * acc),
+ *       acc = sum_k a[m][k] w[n][k] accumulated in float32;
+ *   QG_FP8_BLOCKWISE (section 四.3): out[m][n] = sum_b (a_scales[m][b] *
+ *       w_scales[n/128][b]) * P_b with P_b the float32 sum over K block b,
+ *       promoted into a float32 accumulator once per block.
+ * M >= 0 (0 is a no-op), N >= 1, K % 128 == 0; N % 128 == 0 for
+ * QG_FP8_BLOCKWISE; all pointers device pointers, 16-byte aligned. One
+ * kernel on `stream`; nothing allocated; bitwise reproducible.
+ */
+int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void *a_scales, const void *Wq,
+                   const void *w_scales, void *out, void *stream);
+
 /* Human-readable text of a status code. */
 const char *qgemm_strerror(int status);
 

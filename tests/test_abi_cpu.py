@@ -115,6 +115,30 @@ def test_quantize_validation():
     assert q(M=1 << 30, K=1 << 12, G=128) == qg.EUNSUPPORTED   # beyond one grid
 
 
+def test_fp8_validation():
+    L = qg.lib()
+    q = lambda A=P, M=4, K=256, b=0, Aq=P2, s=P: L.qgemm_fp8_quantize(A, M, K, b, Aq, s, None)
+    assert q(M=0, A=None, Aq=None, s=None) == qg.OK
+    assert q(M=-1) == qg.EINVAL
+    assert q(K=0) == qg.EINVAL
+    assert q(b=64) == qg.EUNSUPPORTED
+    assert q(K=100) == qg.EINVAL                         # K % 8
+    assert q(K=264, b=128) == qg.EINVAL                  # K % 128 for blocks of 128
+    assert q(A=None) == qg.EINVAL and q(Aq=None) == qg.EINVAL and q(s=None) == qg.EINVAL
+    assert q(A=MIS) == qg.EALIGN and q(Aq=MIS) == qg.EALIGN and q(s=MIS) == qg.EALIGN
+    g = lambda M=4, N=256, K=256, sc=0, Aq=P, sa=P, W=P, sw=P, out=P2: L.qgemm_fp8_gemm(
+        M, N, K, sc, Aq, sa, W, sw, out, None)
+    assert g(M=0, Aq=None, sa=None, W=None, sw=None, out=None) == qg.OK
+    assert g(M=-1) == qg.EINVAL and g(N=0) == qg.EINVAL and g(K=0) == qg.EINVAL
+    assert g(sc=2) == qg.EUNSUPPORTED
+    assert g(K=200) == qg.EINVAL                          # K % 128
+    assert g(sc=1, N=200) == qg.EUNSUPPORTED              # blockwise needs N % 128
+    assert g(M=65536 * 128) == qg.EUNSUPPORTED            # grid rows
+    for kw in ("Aq", "sa", "W", "sw", "out"):
+        assert g(**{kw: None}) == qg.EINVAL, kw
+        assert g(**{kw: MIS}) == qg.EALIGN, kw
+
+
 def test_pack_validation():
     L = qg.lib()
     assert L.qgemm_pack(None, P, 64, 8, qg.W4_A_BF16, None) == qg.EINVAL

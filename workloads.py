@@ -246,6 +246,51 @@ _register(_cfg("asym_w4a16_zp_m8", 8, 28672, 8192, 128, 1, True, 1071))
 _register(_cfg("lm_head_w4a16_zp", 1, 128256, 4096, 128, 1, True, 1072))
 
 
+@dataclasses.dataclass
+class Fp8Problem:
+    """FP8 W8A8 inputs: bf16 activations (quantized by the method itself),
+    E4M3 weight codes [N, K] and float32 weight scales ([N] per channel, or
+    [N/128, K/128] per block)."""
+    M: int
+    N: int
+    K: int
+    scaling: int                  # 0 per token x per channel, 1 per 128 x 128 block
+    A: np.ndarray                 # uint16 bf16 bits [M, K]
+    Wq: np.ndarray                # uint8 E4M3 codes [N, K]
+    w_scale: np.ndarray           # float32 [N] or [N/128, K/128]
+    name: str = ""
+
+
+def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniformly random finite E4M3 codes (all 256 patterns but the NaNs 0x7F, 0xFF)."""
+    c = rng.integers(0, 254, size=shape)
+    return np.where(c >= 0x7F, c + 1, c).astype(np.uint8)
+
+
+def make_fp8_problem(M, N, K, scaling, seed=0, outlier_frac=1e-3, outlier_mult=50.0, name="") -> Fp8Problem:
+    """Activations ~ N(0,1) with per-row outliers (as make_activations), cast
+    to bf16; weight codes uniform over the finite E4M3 codes; weight scales
+    log-uniform in [1e-4, 1e-3] (the codes span +-448)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a, _ = make_activations(rng, M, K, 128, "f32", outlier_frac, outlier_mult)
+    A = f32_to_bf16_bits(a)
+    Wq = fp8_codes(rng, (N, K))
+    shape = (N,) if scaling == 0 else (N // 128, K // 128)
+    w_scale = log_uniform(rng, 1e-4, 1e-3, shape).astype(np.float32)
+    return Fp8Problem(M, N, K, scaling, A, Wq, w_scale, name=name)
+
+
+# FP8 W8A8 layers, K = N = 4096 (the prefill sweep's shape), both scalings
+FP8_CONFIGS = {}
+for _i, _M in enumerate((16, 256, 1024, 4096)):
+    for _sc, _sn in ((0, "tok"), (1, "blk")):
+        FP8_CONFIGS[f"fp8_{_sn}_m{_M}"] = dict(M=_M, N=4096, K=4096, scaling=_sc, seed=1100 + 10 * _i + _sc)
+
+
+def make_fp8_config(name: str) -> Fp8Problem:
+    return make_fp8_problem(name=name, **FP8_CONFIGS[name])
+
+
 def make_config(name: str, M: Optional[int] = None) -> Problem:
     c = dict(CONFIGS[name])
     c.pop("name")

@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 g128 GEMV HBM GB/s at M=1; GEMM TFLOPS at M=1024; % of roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 ROTATE_BYTES = 640 << 20
 
 
@@ -176,6 +177,63 @@ def dense_bf16(M, N, K, steps, warmup, mode):
     return ms
 
 
+def run_fp8(name, steps, warmup, mode):
+    """FP8 W8A8 layer: one step = dynamic quantization of the bf16 activations
+    plus the FP8 GEMM (weights rotated like the W4 runs); also the GEMM alone
+    and, where this torch build supports it, torch._scaled_mm on the same
+    codes and scales."""
+    import torch
+    import group_quantized_weight_amd as qg
+    import workloads as wl
+    vp = ctypes.c_void_p
+    p = wl.make_fp8_config(name)
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / (p.N * p.K))))
+    A = torch.from_numpy(p.A.view("int16")).view(torch.bfloat16).cuda()
+    W0 = torch.from_numpy(p.Wq).cuda()
+    ws0 = torch.from_numpy(p.w_scale).cuda()
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    block = 0 if p.scaling == 0 else 128
+    Aq, sc = qg.fp8_quantize(A, block)
+    out = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+    L = qg.lib()
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+
+    def gemm(i):
+        st = L.qgemm_fp8_gemm(p.M, p.N, p.K, p.scaling, vp(Aq.data_ptr()), vp(sc.data_ptr()),
+                              vp(Ws[i % copies].data_ptr()), vp(ws0.data_ptr()), vp(out.data_ptr()), stream)
+        assert st == 0, st
+
+    def step(i):
+        st = L.qgemm_fp8_quantize(vp(A.data_ptr()), p.M, p.K, block, vp(Aq.data_ptr()), vp(sc.data_ptr()), stream)
+        assert st == 0, st
+        gemm(i)
+
+    ms_gemm = time_steps(gemm, steps, warmup, mode)
+    ms_step = time_steps(step, steps, warmup, mode)
+    flops = 2 * p.M * p.N * p.K
+    res = dict(workload=name, M=p.M, N=p.N, K=p.K, scaling=["per_token", "blockwise"][p.scaling],
+               gemm_us=round(ms_gemm * 1e3, 2), step_us=round(ms_step * 1e3, 2),
+               gemm_tflops=round(flops / (ms_gemm * 1e-3) / 1e12, 1),
+               frac_fp8_peak=round(flops / (ms_gemm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4), scaled_mm_us=None)
+    if p.scaling == 0:
+        try:
+            a8 = Aq.view(torch.float8_e4m3fn)
+            b8 = [w.view(torch.float8_e4m3fn).t() for w in Ws]      # [K, N], column-major
+            sa, sb = sc.view(-1, 1), ws0.view(1, -1)
+
+            def sm(i):
+                torch._scaled_mm(a8, b8[i % copies], scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+
+            sm(0)
+            torch.cuda.synchronize()
+            res["scaled_mm_us"] = round(time_steps(sm, steps, warmup, "eager") * 1e3, 2)
+        except Exception as e:   # not every torch build has row-wise FP8 scaling on this GPU
+            log(f"bench: torch._scaled_mm unavailable here ({type(e).__name__})")
+    del A, Ws, Aq, sc, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(p, seconds=10.0):
     import numpy as np
     import oracle
@@ -202,6 +260,7 @@ def main():
     ap.add_argument("--workload", default="decode_w4a16_g128")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--only", default=None, help="run one named workload only (profiling)")
     ap.add_argument("--force-path", type=int, default=-1, help="with --only: QG_PATH_* to force")
     ap.add_argument("--force-nsplit", type=int, default=0, help="with --only: K-split to force")
@@ -265,6 +324,10 @@ def bench(args):
         copy_calibration(args.copy_mib, args.steps, args.warmup)
         return
     if args.only:
+        import workloads as wl
+        if args.only in wl.FP8_CONFIGS:
+            log(json.dumps(run_fp8(args.only, args.steps, args.warmup, args.mode)))
+            return
         r, _ = run_workload(args.only, args.steps, args.warmup, args.mode, force_path=args.force_path,
                             force_nsplit=args.force_nsplit)
         log(json.dumps(r))
@@ -289,6 +352,14 @@ def bench(args):
                               bf16_tflops=2 * M * 4096 * 4096 / (d_ms * 1e-3) / 1e12,
                               w4_speedup=d_ms / r["ms"]))
             log(f"bench: sweep M={M}: w4 {r['ms'] * 1e3:.1f} us ({r['path']}), bf16 {d_ms * 1e3:.1f} us")
+
+    fp8 = []
+    if not args.no_fp8:
+        for name in ("fp8_tok_m1024", "fp8_blk_m1024", "fp8_tok_m4096", "fp8_blk_m4096"):
+            r = run_fp8(name, 100, 20, args.mode)
+            fp8.append(r)
+            log(f"bench: {name}: gemm {r['gemm_us']} us ({r['gemm_tflops']} TFLOP/s), with quantization "
+                f"{r['step_us']} us, torch._scaled_mm {r['scaled_mm_us']}")
 
     cpu = None
     if not args.no_cpu:
@@ -319,6 +390,7 @@ def bench(args):
                        "tflops": round(gemm["tflops"], 2), "peak_tflops": BF16_PEAK_TFLOPS,
                        "frac": round(gemm["tflops"] / BF16_PEAK_TFLOPS, 4), "nsplit": gemm["nsplit"]},
         "crossover": sweep,
+        "fp8_w8a8": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -86,7 +86,7 @@ hipError_t launch_quant(const float *A, int8_t *Aq, float *a_scale, int M, int K
 // token x per channel; 1: per 128 x 128 block).
 hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int M, int K, int block, hipStream_t stream);
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
-                           const float *w_scale, uint16_t *out, int M, int N, int K, hipStream_t stream);
+                           const float *w_scale, uint16_t *out, int M, int N, int K, int cus, hipStream_t stream);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t stream);

@@ -119,7 +119,12 @@ hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int 
 // v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3, float32 accumulate): one
 // instruction per tile per 128-wide K step, which is one scale block. The
 // K step's operand tiles (128 rows x 128 bytes each) are copied by buffer
-// loads straight into LDS, into a ring of 3 stages; the 16-byte pieces of a
+// loads straight into LDS, into a ring of STAGES stages: 3 (two steps in
+// flight) when the grid is about one workgroup per compute unit, 2 (67 KiB,
+// so two workgroups share a compute unit and hide each other's waits) when
+// there are at least two tiles per compute unit (measured on MI355X: M = 4096,
+// K = N = 4096 per token 116 -> 85 us; M = 1024 prefers 3 stages, 32 vs
+// 38 us). The 16-byte pieces of a
 // row are XOR-swizzled with the row index (mod 8), so the fragment reads of
 // 8 consecutive rows hit 8 different bank groups. A lane's fragment is 32
 // consecutive bytes of k (k = 32 (lane / 16) .. +31) of row lane % 16, the
@@ -129,13 +134,13 @@ constexpr int kF8Tile = 128;
 constexpr int kF8Row = 128;                       // bytes per operand row per K step
 constexpr int kF8OpBytes = kF8Tile * kF8Row;      // 16 KiB
 constexpr int kF8Stage = 2 * kF8OpBytes + 512;    // A, B, and the block's 128 activation scales
-constexpr int kF8Stages = 3;
 
-template <bool BLOCKWISE>
+template <bool BLOCKWISE, int STAGES>
 __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict__ Aq, const float *__restrict__ a_scale,
                                                       const uint8_t *__restrict__ Wq, const float *__restrict__ w_scale,
                                                       uint16_t *__restrict__ out, int M, int N, int K) {
-  __shared__ __align__(16) unsigned char s_ring[kF8Stages * kF8Stage];
+  static_assert(STAGES == 2 || STAGES == 3, "ring depth");
+  __shared__ __align__(16) unsigned char s_ring[STAGES * kF8Stage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lk = lane >> 4;
@@ -181,10 +186,10 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
       }
     }
   };
-  // At the top of step i at most the next step's copies may be in flight:
-  // 8 operand copies per wave (waves 0 and 1 add one scale copy after them,
-  // which vmcnt(8) then also waits for).
-  constexpr int kCopies = 8;
+  // At the top of step i at most the next step's copies may be in flight
+  // (3 stages): 8 operand copies per wave (waves 0 and 1 add one scale copy
+  // after them, which vmcnt(8) then also waits for); with 2 stages none.
+  constexpr int kInFlight = STAGES == 3 ? 8 : 0;
 
   auto frag = [&](const unsigned char *op, int row) {   // 32 bytes: pieces 2 lk, 2 lk + 1 of the row
     const u32x4_v lo = *(const u32x4_v *)(op + row * kF8Row + 16 * ((2 * lk) ^ (row & 7)));
@@ -199,13 +204,14 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
 
   copy_step(0, 0, 0);
-  copy_step(1, 1, nsteps > 1 ? 0 : kDead);
+  if constexpr (STAGES == 3) copy_step(1, 1, nsteps > 1 ? 0 : kDead);
   for (int i = 0; i < nsteps; ++i) {
     // this step's copies are done when at most the next step's remain in flight
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
-    // every wave is past step i - 1: its stage takes step i + 2
-    copy_step(i + 2, (i + 2) % kF8Stages, i + 2 < nsteps ? 0 : kDead);
-    const unsigned char *sb = s_ring + (i % kF8Stages) * kF8Stage;
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
+    // every wave is past step i - 1: its stage takes step i + STAGES - 1
+    const int nx = i + STAGES - 1;
+    copy_step(nx, nx % STAGES, nx < nsteps ? 0 : kDead);
+    const unsigned char *sb = s_ring + (i % STAGES) * kF8Stage;
     i32x8_v af[4], bfr[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -255,14 +261,24 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
   }
 }
 
+template <bool BLOCKWISE>
+static void go_fp8(int stages, dim3 grid, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
+                   const float *w_scale, uint16_t *out, int M, int N, int K, hipStream_t st) {
+  if (stages == 2)
+    fp8_gemm_kernel<BLOCKWISE, 2><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+  else
+    fp8_gemm_kernel<BLOCKWISE, 3><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+}
+
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
-                           const float *w_scale, uint16_t *out, int M, int N, int K, hipStream_t st) {
+                           const float *w_scale, uint16_t *out, int M, int N, int K, int cus, hipStream_t st) {
   if (M == 0) return hipSuccess;
   const dim3 grid((N + kF8Tile - 1) / kF8Tile, (M + kF8Tile - 1) / kF8Tile);
+  const int stages = (long long)grid.x * grid.y >= 2LL * cus ? 2 : 3;
   if (scaling == 1)
-    fp8_gemm_kernel<true><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+    go_fp8<true>(stages, grid, Aq, a_scale, Wq, w_scale, out, M, N, K, st);
   else
-    fp8_gemm_kernel<false><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+    go_fp8<false>(stages, grid, Aq, a_scale, Wq, w_scale, out, M, N, K, st);
   return hipGetLastError();
 }
 

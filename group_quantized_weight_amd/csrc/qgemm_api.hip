@@ -376,7 +376,8 @@ int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void 
   if (!aligned16(Aq) || !aligned16(a_scales) || !aligned16(Wq) || !aligned16(w_scales) || !aligned16(out))
     return QG_EALIGN;
   const hipError_t e = launch_fp8_gemm(scaling, (const uint8_t *)Aq, (const float *)a_scales, (const uint8_t *)Wq,
-                                       (const float *)w_scales, (uint16_t *)out, M, N, K, (hipStream_t)stream);
+                                       (const float *)w_scales, (uint16_t *)out, M, N, K, device_cus(),
+                                       (hipStream_t)stream);
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 

@@ -117,6 +117,28 @@ def test_gemm_small(scaling, M, N, K):
     check(out, ref, bound, f"fp8 scaling={scaling} M={M} N={N} K={K}", bf16_out=True)
 
 
+@pytest.mark.parametrize("scaling", [0, 1])
+def test_gemm_two_stage_ring(scaling):
+    """At least two 128 x 128 tiles per compute unit select the 2-stage LDS
+    ring (M = 1024, N = 8192: 512 tiles); sampled columns against the oracle,
+    all rows, and bitwise agreement with the same rows computed through the
+    3-stage ring (a 128-row slice of the problem: 64 tiles)."""
+    import torch
+    M, N, K = 1024, 8192, 256
+    p = wl.make_fp8_problem(M, N, K, scaling, seed=1600 + scaling)
+    block = 0 if scaling == 0 else 128
+    Aq, sc = _quant_same(p.A, block, "two-stage inputs")
+    Wq, ws = _u8_dev(p.Wq), _f32_dev(p.w_scale)
+    out = qg.fp8_gemm(Aq, sc, Wq, ws, scaling)
+    part = qg.fp8_gemm(Aq[:128].contiguous(), sc[:128].contiguous(), Wq, ws, scaling)
+    torch.cuda.synchronize()
+    assert bitwise_equal(out[:128].contiguous(), part), "2-stage and 3-stage rings differ"
+    cols = sample_indices(N, 256, 5)
+    ref, bound = oracle.fp8_gemm(M, N, K, scaling, Aq.cpu().numpy(), sc.cpu().numpy(), p.Wq, p.w_scale, cols=cols)
+    check(out.float().cpu().numpy().astype(np.float64)[:, cols], ref, bound, f"two-stage scaling={scaling}",
+          bf16_out=True)
+
+
 @pytest.mark.parametrize("M,N", [(3, 300), (130, 1000), (64, 8)])
 def test_gemm_ragged_n_per_token(M, N):
     """Per-token scaling allows any N: the weight rows past N read zeros and

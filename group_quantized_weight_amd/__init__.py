@@ -70,6 +70,14 @@ def lib():
             L.qgemm_run.argtypes = run_args
             L.qgemm_run_ex.restype = c_int
             L.qgemm_run_ex.argtypes = run_args + [c_int, c_int]
+            L.qgemm_moe_max_tiles.restype = c_int
+            L.qgemm_moe_max_tiles.argtypes = [c_int] * 3
+            L.qgemm_moe_align.restype = c_int
+            L.qgemm_moe_align.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp, vp]
+            L.qgemm_moe_workspace_bytes.restype = c_size
+            L.qgemm_moe_workspace_bytes.argtypes = [c_int] * 8
+            L.qgemm_moe_run.restype = c_int
+            L.qgemm_moe_run.argtypes = [c_int] * 9 + [vp] * 8 + [c_size, vp]
             L.qgemm_fp8_quantize.restype = c_int
             L.qgemm_fp8_quantize.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
             L.qgemm_fp8_gemm.restype = c_int
@@ -175,6 +183,47 @@ def quantize_activations(A, G: int, Aq=None, a_scales=None, stream=None):
     if st != OK:
         raise QGemmError(st, "qgemm_quantize_activations")
     return Aq, a_scales
+
+
+def moe_align(topk_ids, E: int, block: int, stream=None):
+    """(sorted_ids, tile_experts, num_post_pad) int32 device tensors for the
+    grouped GEMV (see include/qgemm.h); topk_ids: int32 [T, topk] or flat."""
+    import torch
+    ids = topk_ids.reshape(-1)
+    numel = ids.numel()
+    mt = int(lib().qgemm_moe_max_tiles(numel, E, block))
+    if mt == 0:
+        raise QGemmError(EUNSUPPORTED, "qgemm_moe_max_tiles")
+    dev = topk_ids.device
+    sorted_ids = torch.empty(mt * block, dtype=torch.int32, device=dev)
+    tile_experts = torch.empty(mt, dtype=torch.int32, device=dev)
+    npp = torch.empty(4, dtype=torch.int32, device=dev)
+    st = lib().qgemm_moe_align(_ptr(ids), numel, E, block, _ptr(sorted_ids), _ptr(tile_experts), _ptr(npp),
+                               stream if stream is not None else _stream(dev))
+    if st != OK:
+        raise QGemmError(st, "qgemm_moe_align")
+    return sorted_ids, tile_experts, npp
+
+
+def moe_run(A, w_packed, scales, routing, *, topk: int, N: int, G: int, E: int, block: int, prec: int = W4_A_BF16,
+            zeros=None, out=None, stream=None):
+    """Grouped W4A16 GEMV: out [T*topk, N], row i = A[i // topk] times the
+    weights of slot i's expert (see include/qgemm.h). routing: moe_align's
+    result; w_packed: the E packed weights one after another."""
+    import torch
+    T, K = A.shape
+    sorted_ids, tile_experts, npp = routing
+    if out is None:
+        out = torch.empty((T * topk, N), dtype=out_dtype(prec), device=A.device)
+    need = int(lib().qgemm_moe_workspace_bytes(T, topk, N, K, G, prec, E, block))
+    ws = workspace(need, A.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().qgemm_moe_run(T, topk, N, K, G, prec, int(zeros is not None), E, block, _ptr(A), _ptr(w_packed),
+                             _ptr(scales), _ptr(zeros), _ptr(sorted_ids), _ptr(tile_experts), _ptr(npp), _ptr(out),
+                             _ptr(ws), ws_bytes, stream if stream is not None else _stream(A.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_moe_run")
+    return out
 
 
 def fp8_quantize(A, block: int = FP8_PER_TOKEN, stream=None):

@@ -41,6 +41,13 @@ struct GemvArgs {
   float *partial;          // [nsplit][M][Np] (nsplit > 1)
   int M, N, K, G, Np;
   int ngroups, nsplit;
+  // grouped (MoE) launches only: routed rows per row block, each block's
+  // expert, the padded routed-row count, and each expert's weight stride
+  const int *sorted_ids;   // [row blocks * MB] slot ids (>= M: padding)
+  const int *tile_experts; // [row blocks] expert of the block, or -1
+  const int *num_post_pad; // padded routed rows (device scalar)
+  int topk;                // activation row = slot / topk
+  size_t w_expert_words, s_expert_bytes, z_expert_words;
 };
 
 struct GemmArgs {
@@ -70,6 +77,12 @@ struct SmallArgs {
 // launch status; the dispatcher has validated every argument before.
 hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, const GemvArgs &a,
                        dim3 grid, size_t lds_bytes, hipStream_t stream);
+// grouped (MoE) W4A16 GEMV: rows gathered through GemvArgs::sorted_ids
+hipError_t launch_gemv_grouped(int ofmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds_bytes,
+                               hipStream_t stream);
+// routing metadata for the grouped GEMV (counting sort by expert)
+hipError_t launch_moe_align(const int *topk_ids, int numel, int E, int block, int max_tiles, int *sorted_ids,
+                            int *tile_experts, int *num_post_pad, hipStream_t stream);
 // int8 activations (float32 scales and output)
 hipError_t launch_gemv_i8(int wfmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds_bytes,
                           hipStream_t stream);

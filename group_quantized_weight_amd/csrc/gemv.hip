@@ -151,7 +151,7 @@ struct BatchRows {  // weight load instructions issued together, by register bud
   static constexpr int value = MB <= 2 ? 16 : (MB == 4 ? 8 : 4);
 };
 
-template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G>
+template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G, bool GR>
 __global__ __launch_bounds__(gemv_waves(MB) * kWave)
 void gemv_kernel(GemvArgs a) {
   constexpr int kGemvWaves = gemv_waves(MB);
@@ -187,6 +187,42 @@ void gemv_kernel(GemvArgs a) {
   const int z = blockIdx.z;
   const int R = a.K / KPW;                            // word-rows of the whole matrix
 
+  // Grouped (MoE) row blocks: block y holds the routed rows (slots)
+  // sorted_ids[m0 .. m0 + MB - 1] of one expert; their activations are the
+  // token rows slot / topk, the expert's weights, scales and zero-points
+  // follow one another, and row `slot` of the output is written. Blocks past
+  // the padded row count, or without an expert, have nothing to do.
+  const uint32_t *Wb = a.W;
+  const char *Sb = (const char *)a.S;
+  const uint32_t *Zb = a.Z;
+  int slot[MB];
+  if constexpr (GR) {
+    if (m0 >= *a.num_post_pad) return;
+    const int e = a.tile_experts[blockIdx.y];
+    if (e < 0) return;
+    Wb += (size_t)e * a.w_expert_words;
+    Sb += (size_t)e * a.s_expert_bytes;
+    if constexpr (ZP) Zb += (size_t)e * a.z_expert_words;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) slot[m] = a.sorted_ids[m0 + m];
+  } else {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) slot[m] = m0 + m;
+  }
+  // output row of block row m (valid when < M) and its activation row
+  auto out_row = [&](int m) {
+    if constexpr (GR) {
+      int r = slot[0];
+#pragma unroll
+      for (int j = 1; j < MB; ++j) r = m == j ? slot[j] : r;
+      return r;
+    } else {
+      return m0 + m;
+    }
+  };
+  auto act_row = [&](int m) { return GR ? out_row(m) / a.topk : m0 + m; };
+  const int act_row0 = GR ? 0 : m0;                   // a valid row for lanes without one
+
   int gb, gcount;
   split_range(a.ngroups, a.nsplit, z, gb, gcount);
   int wg0, wgc;  // this wave's groups, local to the slice
@@ -204,7 +240,7 @@ void gemv_kernel(GemvArgs a) {
   // adds one fixed byte offset, so issuing a load costs no vector arithmetic.
   // (A buffer load past num_records returns 0 instead of faulting.)
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.W + (size_t)tile * R * kTileCols), (short)0, R * kTileCols * 4, kBufferWord3);
+      (void *)(Wb + (size_t)tile * R * kTileCols), (short)0, R * kTileCols * 4, kBufferWord3);
   const int w_voff = (lk * kTileCols + 4 * c4) * 4;
 
   // Scale and zero-point prefetch goes to registers with no divergent control
@@ -214,10 +250,10 @@ void gemv_kernel(GemvArgs a) {
   const int scol = col_ok ? ncol : 0;
   constexpr int SB = SF == S_BF16 ? 2 : 4;          // bytes per scale
   const __amdgpu_buffer_rsrc_t s_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.S, (short)0, a.ngroups * a.N * SB, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)Sb, (short)0, a.ngroups * a.N * SB, kBufferWord3);
   const int s_voff = vec_s ? scol * SB : 0;
   const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)a.Z, (short)0, ZP ? a.ngroups * (a.N >> 3) * 4 : 0, kBufferWord3);
+      (void *)Zb, (short)0, ZP ? a.ngroups * (a.N >> 3) * 4 : 0, kBufferWord3);
   const int z_voff = (scol >> 3) * 4;
   using SRaw = typename std::conditional<SF == S_BF16, u32x2_v, u32x4_v>::type;
   u32x4_v wv[NB][IPB];
@@ -269,9 +305,9 @@ void gemv_kernel(GemvArgs a) {
         s[c] = 0.f;
         if (ncol + c < a.N) {
           if constexpr (SF == S_BF16)
-            s[c] = __uint_as_float((uint32_t)((const uint16_t *)a.S)[si + c] << 16);
+            s[c] = __uint_as_float((uint32_t)((const uint16_t *)Sb)[si + c] << 16);
           else
-            s[c] = ((const float *)a.S)[si + c];
+            s[c] = ((const float *)Sb)[si + c];
         }
       }
     }
@@ -286,8 +322,8 @@ void gemv_kernel(GemvArgs a) {
   for (int s = 0; s < SMAX; ++s) {
     const int idx = threadIdx.x + kGemvThreads * s;
     const int m = idx / rows, r = idx - (idx / rows) * rows;
-    st_ok[s] = idx < nstage && m0 + m < a.M;
-    const size_t k = st_ok[s] ? (size_t)(m0 + m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)m0 * a.K;
+    st_ok[s] = idx < nstage && out_row(m) < a.M;
+    const size_t k = st_ok[s] ? (size_t)act_row(m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)act_row0 * a.K;
     load_row<WF, AF>(a.A, k, st0[s], st1[s]);
   }
   // the first batch (NB - 1 batches with NB > 1); a wave without groups
@@ -303,9 +339,10 @@ void gemv_kernel(GemvArgs a) {
   }
   for (int idx = threadIdx.x + kGemvThreads * SMAX; idx < nstage; idx += kGemvThreads) {
     const int m = idx / rows, r = idx - (idx / rows) * rows;
-    const bool ok = m0 + m < a.M;
+    const bool ok = out_row(m) < a.M;
     u32x4_v c0, c1;
-    load_row<WF, AF>(a.A, ok ? (size_t)(m0 + m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)m0 * a.K, c0, c1);
+    load_row<WF, AF>(a.A, ok ? (size_t)act_row(m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)act_row0 * a.K,
+                     c0, c1);
     mask_row(ok, c0, c1);
     s_rsum[idx] = store_row<WF, AF>(s_act + (size_t)idx * AB, c0, c1);
   }
@@ -471,15 +508,16 @@ void gemv_kernel(GemvArgs a) {
 
   for (int t = threadIdx.x; t < MB * kTileCols; t += kGemvThreads) {
     const int m = t / kTileCols, col = t % kTileCols;
-    if (m0 + m >= a.M) continue;
+    const int orow = out_row(m);
+    if (orow >= a.M) continue;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kGemvWaves; ++w) v += s_red[((size_t)w * MB + m) * kTileCols + col];
     const int n = tile * kTileCols + col;
     if (a.nsplit > 1) {
-      a.partial[((size_t)z * a.M + m0 + m) * a.Np + n] = v;
+      a.partial[((size_t)z * a.M + orow) * a.Np + n] = v;
     } else if (n < a.N) {
-      const size_t o = (size_t)(m0 + m) * a.N + n;
+      const size_t o = (size_t)orow * a.N + n;
       if constexpr (OF == O_BF16)
         ((uint16_t *)a.out)[o] = f32_to_bf16(v);
       else
@@ -491,17 +529,17 @@ void gemv_kernel(GemvArgs a) {
 // ---------------------------------------------------------------------------
 // launcher: (wfmt, afmt, sfmt, ofmt, zp, mb, G) -> kernel instance
 // ---------------------------------------------------------------------------
-template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G>
+template <int WF, int AF, int SF, int OF, bool ZP, int MB, int G, bool GR>
 static hipError_t go(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  gemv_kernel<WF, AF, SF, OF, ZP, MB, G><<<grid, gemv_waves(MB) * kWave, lds, st>>>(a);
+  gemv_kernel<WF, AF, SF, OF, ZP, MB, G, GR><<<grid, gemv_waves(MB) * kWave, lds, st>>>(a);
   return hipGetLastError();
 }
 
-template <int WF, int AF, int SF, int OF, bool ZP>
+template <int WF, int AF, int SF, int OF, bool ZP, bool GR = false>
 static hipError_t go_mb(int mb, int G, const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-#define QG_G(MBV)                                                   \
-  return G == 32 ? go<WF, AF, SF, OF, ZP, MBV, 32>(a, grid, lds, st) \
-                 : go<WF, AF, SF, OF, ZP, MBV, 128>(a, grid, lds, st)
+#define QG_G(MBV)                                                       \
+  return G == 32 ? go<WF, AF, SF, OF, ZP, MBV, 32, GR>(a, grid, lds, st) \
+                 : go<WF, AF, SF, OF, ZP, MBV, 128, GR>(a, grid, lds, st)
   switch (mb) {
     case 1: QG_G(1);
     case 2: QG_G(2);
@@ -527,6 +565,17 @@ hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, 
   if (wfmt == W8 && afmt == A_F32)
     return go_mb<W8, A_F32, S_F32, O_F32, false>(mb, G, a, grid, lds, st);
   return hipErrorInvalidValue;
+}
+
+// Grouped (MoE) W4A16: bf16 activations and scales; bf16 or float32 output.
+hipError_t launch_gemv_grouped(int ofmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds,
+                               hipStream_t st) {
+  const int G = a.G;
+  if (ofmt == O_BF16)
+    return zp ? go_mb<W4, A_BF16, S_BF16, O_BF16, true, true>(mb, G, a, grid, lds, st)
+              : go_mb<W4, A_BF16, S_BF16, O_BF16, false, true>(mb, G, a, grid, lds, st);
+  return zp ? go_mb<W4, A_BF16, S_BF16, O_F32, true, true>(mb, G, a, grid, lds, st)
+            : go_mb<W4, A_BF16, S_BF16, O_F32, false, true>(mb, G, a, grid, lds, st);
 }
 
 }  // namespace qg

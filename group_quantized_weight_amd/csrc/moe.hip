@@ -1,0 +1,80 @@
+// Routing metadata for the grouped (MoE) GEMV: the align step of the fused
+// MoE pipeline on the page "quantization-and-fused-kernels"
+// (arganzheng.life), section 六.3. From the expert of every routed slot
+// (topk_ids, slot i = token * topk + j) it writes
+//   sorted_ids:   the slots grouped by expert, each expert's segment padded
+//                 to a multiple of `block` rows with the sentinel numel;
+//   tile_experts: the expert of each block of `block` rows (-1 past the end);
+//   num_post_pad: the padded row count.
+// It is a counting sort in one workgroup: per-expert counts (LDS atomics),
+// an exclusive sum of the padded counts, then each slot takes the next free
+// position of its expert's segment. As on the page, the order of slots
+// within an expert follows the atomics' arrival; the grouped GEMV computes
+// every row on its own, so its output does not depend on that order. Slots
+// whose expert is outside [0, E) are skipped (their output rows are not
+// written).
+#include "common.h"
+
+namespace qg {
+
+__global__ __launch_bounds__(1024) void moe_align_kernel(const int *__restrict__ topk_ids, int numel, int E, int block,
+                                                        int max_tiles, int *__restrict__ sorted_ids,
+                                                        int *__restrict__ tile_experts, int *__restrict__ num_post_pad) {
+  extern __shared__ int sh[];
+  int *cnt = sh;             // [E]
+  int *off = sh + E;         // [E + 1] padded segment starts
+  int *cur = off + E + 1;    // [E] next free position per expert
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int e = tid; e < E; e += nt) {
+    cnt[e] = 0;
+    cur[e] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < numel; i += nt) {
+    const int e = topk_ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = acc;
+      acc += (cnt[e] + block - 1) / block * block;
+    }
+    off[E] = acc;
+    *num_post_pad = acc;
+  }
+  __syncthreads();
+  const int total = off[E];
+  for (int p = tid; p < max_tiles * block; p += nt) sorted_ids[p] = numel;
+  for (int t = tid; t < max_tiles; t += nt) {
+    int e = -1;
+    if (t * block < total) {  // the expert whose segment holds row t * block: off[e] <= x < off[e + 1]
+      const int x = t * block;
+      int lo = 0, hi = E;     // first j in [0, E] with off[j] > x is in (lo, hi]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (off[mid] <= x)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      e = lo;
+    }
+    tile_experts[t] = e;
+  }
+  __syncthreads();  // the sentinel fill above is ordered before the placement below
+  for (int i = tid; i < numel; i += nt) {
+    const int e = topk_ids[i];
+    if (e >= 0 && e < E) sorted_ids[off[e] + atomicAdd(&cur[e], 1)] = i;
+  }
+}
+
+hipError_t launch_moe_align(const int *topk_ids, int numel, int E, int block, int max_tiles, int *sorted_ids,
+                            int *tile_experts, int *num_post_pad, hipStream_t st) {
+  moe_align_kernel<<<1, 1024, (size_t)(3 * E + 1) * sizeof(int), st>>>(topk_ids, numel, E, block, max_tiles,
+                                                                       sorted_ids, tile_experts, num_post_pad);
+  return hipGetLastError();
+}
+
+}  // namespace qg

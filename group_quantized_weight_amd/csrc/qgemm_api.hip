@@ -80,6 +80,7 @@ size_t padded_cols(int N) { return ((size_t)N + kColAlign - 1) / kColAlign * kCo
 constexpr size_t kPartialCap = 256ull << 20;  // bytes of float32 partials at most
 constexpr int kSmallMaxM = 64;                // rows the small-M MFMA path takes (4 blocks of 16)
 constexpr size_t kGemvLdsCap = 60 * 1024;     // dynamic LDS per workgroup (static LDS comes on top)
+constexpr int kMoeMaxExperts = 1024;          // experts the align step's LDS counters hold
 
 struct Plan {
   int path = QG_PATH_GEMV;
@@ -346,6 +347,120 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
   if (!aligned16(A) || !aligned16(Aq) || !aligned16(a_scales)) return QG_EALIGN;
   const hipError_t e = launch_quant((const float *)A, (int8_t *)Aq, (float *)a_scales, M, K, group,
                                     (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_moe_max_tiles(int numel, int E, int block) {
+  if (numel < 0 || E < 1 || E > kMoeMaxExperts || !(block == 1 || block == 2 || block == 4 || block == 8)) return 0;
+  const long long t = ((long long)numel + (long long)E * (block - 1)) / block;
+  return t > 65535 ? 0 : (int)(t > 0 ? t : 1);
+}
+
+int qgemm_moe_align(const int *topk_ids, int numel, int E, int block, int *sorted_ids, int *tile_experts,
+                    int *num_post_pad, void *stream) {
+  if (numel < 0) return QG_EINVAL;
+  const int max_tiles = qgemm_moe_max_tiles(numel, E, block);
+  if (max_tiles == 0) return QG_EUNSUPPORTED;
+  if (!sorted_ids || !tile_experts || !num_post_pad || (numel > 0 && !topk_ids)) return QG_EINVAL;
+  if ((numel > 0 && !aligned16(topk_ids)) || !aligned16(sorted_ids) || !aligned16(tile_experts) ||
+      !aligned16(num_post_pad))
+    return QG_EALIGN;
+  const hipError_t e = launch_moe_align(topk_ids, numel, E, block, max_tiles, sorted_ids, tile_experts,
+                                        num_post_pad, (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+namespace {
+
+// Plan of the grouped GEMV: one row block per possible tile, a K-split when
+// the column tiles times the tiles that are surely used (numel / block)
+// leave compute units idle; the same rules as the dense GEMV.
+int moe_plan(int numel, int N, int K, int G, const Formats &f, int E, int block, int force_nsplit, Plan &p) {
+  const int cus = device_cus();
+  const size_t Np = padded_cols(N);
+  p.path = QG_PATH_GEMV;
+  p.mb = block;
+  p.mblocks = qgemm_moe_max_tiles(numel, E, block);
+  p.tiles_x = (int)(Np / kTileCols);
+  p.units = K / G;
+  const long long used = (numel + block - 1) / block;
+  const long long base = (long long)p.tiles_x * (used > 0 ? used : 1);
+  int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((2LL * cus + base - 1) / base));
+  ns = balance(p.units, ns);
+  while (ns < p.units && gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) ns = balance(p.units, ns + 1);
+  if (force_nsplit <= 0)
+    while (ns > 1 && (size_t)ns * numel * Np * 4 > kPartialCap) {
+      const int lower = balance(p.units, ns - 1);
+      if (gemv_lds(f, p.mb, G, p.units, lower) > kGemvLdsCap) break;
+      ns = lower;
+    }
+  if (gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) return QG_EUNSUPPORTED;
+  p.lds = gemv_lds(f, p.mb, G, p.units, ns);
+  p.nsplit = ns;
+  p.ws = ns > 1 ? (size_t)ns * numel * Np * 4 : 0;
+  return QG_OK;
+}
+
+int check_moe(int T, int topk, int N, int K, int G, int prec, int has_zp, int E, int block, Formats &f) {
+  if (prec != QG_W4_A_BF16 && prec != QG_W4_A_BF16_OF32) return QG_EUNSUPPORTED;
+  if (T < 0 || topk < 1) return QG_EINVAL;
+  if ((long long)T * topk > INT_MAX / 2) return QG_EUNSUPPORTED;
+  const int numel = T * topk;
+  if (qgemm_moe_max_tiles(numel, E, block) == 0) return QG_EUNSUPPORTED;
+  return check_shape(numel > 0 ? numel : 1, N, K, G, prec, has_zp, f);
+}
+
+}  // namespace
+
+size_t qgemm_moe_workspace_bytes(int T, int topk, int N, int K, int group, int prec, int E, int block) {
+  Formats f;
+  if (check_moe(T, topk, N, K, group, prec, 0, E, block, f) != QG_OK || T == 0) return 0;
+  Plan p;
+  if (moe_plan(T * topk, N, K, group, f, E, block, 0, p) != QG_OK) return 0;
+  return p.ws;
+}
+
+int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp, int E, int block, const void *A,
+                  const void *w_packed, const void *scales, const void *zeros, const int *sorted_ids,
+                  const int *tile_experts, const int *num_post_pad, void *out, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  Formats f;
+  int st = check_moe(T, topk, N, K, group, prec, has_zp, E, block, f);
+  if (st != QG_OK) return st;
+  if (T == 0) return QG_OK;
+  if (!A || !w_packed || !scales || !out || !sorted_ids || !tile_experts || !num_post_pad) return QG_EINVAL;
+  if (has_zp && !zeros) return QG_EINVAL;
+  if (!aligned16(A) || !aligned16(w_packed) || !aligned16(scales) || !aligned16(out) || !aligned16(sorted_ids) ||
+      !aligned16(tile_experts) || !aligned16(num_post_pad) || (has_zp && !aligned16(zeros)))
+    return QG_EALIGN;
+  const int numel = T * topk;
+  Plan p;
+  st = moe_plan(numel, N, K, group, f, E, block, 0, p);
+  if (st != QG_OK) return st;
+  if (p.ws > 0) {
+    if (!workspace || workspace_bytes < p.ws) return QG_EWORKSPACE;
+    if (!aligned16(workspace)) return QG_EALIGN;
+  }
+  GemvArgs a = {};
+  a.A = A;
+  a.W = (const uint32_t *)w_packed;
+  a.S = scales;
+  a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
+  a.out = out;
+  a.partial = p.nsplit > 1 ? (float *)workspace : nullptr;
+  a.M = numel; a.N = N; a.K = K; a.G = group; a.Np = (int)padded_cols(N);
+  a.ngroups = K / group;
+  a.nsplit = p.nsplit;
+  a.sorted_ids = sorted_ids;
+  a.tile_experts = tile_experts;
+  a.num_post_pad = num_post_pad;
+  a.topk = topk;
+  a.w_expert_words = qgemm_packed_bytes(K, N, prec) / 4;
+  a.s_expert_bytes = (size_t)(K / group) * N * 2;
+  a.z_expert_words = (size_t)(K / group) * (N / 8);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_gemv_grouped(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.mblocks, p.nsplit), p.lds, s);
+  if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, a.partial, out, numel, N, a.Np, p.nsplit, s);
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 

@@ -178,6 +178,57 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
                                void *stream);
 
 /*
+ * Grouped (MoE) W4A16 GEMV -- grouped GEMM #1 of the fused MoE pipeline on
+ * the page "quantization-and-fused-kernels" (arganzheng.life), section 六:
+ * each of T tokens is routed to topk experts (slot i = t * topk + j holds
+ * expert topk_ids[i]); every slot's output row is its token's activations
+ * times its expert's weights,
+ *     out[i][n] = sum_g s_e[g,n] * sum_{k in g} A[i / topk][k] * (q_e[k,n] - z_e[g,n]),
+ * e = topk_ids[i]. Rows of one expert are gathered into blocks of `block`
+ * rows (1, 2, 4 or 8) by the align step (section 六.3), so each block reads
+ * its expert's weights once.
+ *
+ * qgemm_moe_max_tiles: row blocks the align step may produce for numel
+ * routed slots (0 if the arguments are invalid); sorted_ids holds
+ * max_tiles * block ints and tile_experts max_tiles ints.
+ */
+int qgemm_moe_max_tiles(int numel, int E, int block);
+
+/*
+ * Align (section 六.3), one kernel on `stream`: from topk_ids (int32
+ * [numel], experts in [0, E); slots with other values are skipped and their
+ * output rows are not written) write sorted_ids (the slots grouped by
+ * expert, each expert's segment padded to a multiple of `block` with the
+ * value numel), tile_experts (each block's expert, -1 past the padded rows)
+ * and num_post_pad (one int: the padded row count). The order of slots
+ * within an expert follows atomic arrival, as on the page; the grouped GEMV's
+ * output does not depend on it. 1 <= E <= 1024; device pointers, 16-byte
+ * aligned.
+ */
+int qgemm_moe_align(const int *topk_ids, int numel, int E, int block, int *sorted_ids, int *tile_experts,
+                    int *num_post_pad, void *stream);
+
+/* Workspace bytes of qgemm_moe_run (float32 K-split partials; 0: none). */
+size_t qgemm_moe_workspace_bytes(int T, int topk, int N, int K, int group, int prec, int E, int block);
+
+/*
+ * The grouped GEMV on the align step's metadata (device pointers, 16-byte
+ * aligned; enqueued on `stream` after the align step):
+ *   prec:      QG_W4_A_BF16 (bf16 out) or QG_W4_A_BF16_OF32 (float32 out)
+ *   A:         bf16 [T][K] token activations
+ *   w_packed:  E packed weights one after another, each qgemm_packed_bytes(K, N, prec)
+ *   scales:    bf16 [E][K/G][N]; zeros: uint32 [E][K/G][N/8] when has_zp (N % 8 == 0)
+ *   out:       [T * topk][N], row i for slot i
+ *   workspace: qgemm_moe_workspace_bytes() bytes (float32 partials of a K-split)
+ * T >= 0 (0 is a no-op), topk >= 1, group 32 or 128, K % group == 0.
+ * Bitwise reproducible (each row is computed on its own, in a fixed order).
+ */
+int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp, int E, int block,
+                  const void *A, const void *w_packed, const void *scales, const void *zeros,
+                  const int *sorted_ids, const int *tile_experts, const int *num_post_pad, void *out,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * FP8 (E4M3) W8A8 -- the variant the page "quantization-and-fused-kernels"
  * (arganzheng.life) contrasts with W4A16 in section 四: weights and
  * activations both in FP8, products accumulated in float32 on the matrix

@@ -159,6 +159,61 @@ def quantize_act(A, G: int, lib=None):
     return Aq, sc
 
 
+def moe_align(topk_ids, E: int, block: int):
+    """The align step of the fused MoE pipeline (page "quantization-and-fused-
+    kernels", section 六.3), as a plain counting sort: per-expert counts, each
+    padded up to a multiple of `block`, their exclusive sum, and the slots of
+    each expert in ascending order followed by the sentinel numel. Returns
+    (sorted_ids, tile_experts, num_post_pad) with tile_experts[t] the expert
+    of rows [t*block, (t+1)*block). Slots whose expert is outside [0, E) are
+    left out."""
+    ids = [int(x) for x in np.asarray(topk_ids).reshape(-1)]
+    numel = len(ids)
+    counts = [0] * E
+    for e in ids:
+        if 0 <= e < E:
+            counts[e] += 1
+    starts, total = [], 0
+    for e in range(E):
+        starts.append(total)
+        total += -(-counts[e] // block) * block
+    sorted_ids = [numel] * total
+    fill = list(starts)
+    for i, e in enumerate(ids):
+        if 0 <= e < E:
+            sorted_ids[fill[e]] = i
+            fill[e] += 1
+    tile_experts = []
+    for e in range(E):
+        tile_experts += [e] * (-(-counts[e] // block))
+    return np.array(sorted_ids, np.int64), np.array(tile_experts, np.int64), total
+
+
+def moe(T, topk, N, K, G, wfmt, afmt, sfmt, has_zp, A, topk_ids, W, S, Z, slots=None, cols=None, lib=None):
+    """Grouped (MoE) reference: row i of the output (slot i = token * topk + j)
+    is the product of token i // topk's activations with the weights of
+    expert topk_ids[i] (section 六.3: A rows gathered as slot // topk, B the
+    expert's weights), each computed by qgemm above. W, S, Z hold the E
+    experts' canonical arrays stacked on a leading axis. Returns (ref, bound)
+    [len(slots), len(cols)]; rows of slots with an expert outside the stack
+    are NaN."""
+    ids = np.asarray(topk_ids).reshape(-1)
+    slots = np.arange(T * topk) if slots is None else np.asarray(slots)
+    nc = N if cols is None else len(cols)
+    ref = np.full((len(slots), nc), np.nan)
+    bound = np.full((len(slots), nc), np.nan)
+    for e in range(W.shape[0]):
+        pick = np.nonzero(ids[slots] == e)[0]
+        if pick.size == 0:
+            continue
+        tokens = slots[pick] // topk
+        r, b = qgemm(T, N, K, G, wfmt, afmt, sfmt, has_zp, A, None, W[e], S[e], None if Z is None else Z[e],
+                     rows=tokens, cols=cols, lib=lib)
+        ref[pick] = r
+        bound[pick] = b
+    return ref, bound
+
+
 def fp8_value(code: int, lib=None) -> float:
     """Value of an 8-bit E4M3 ("fn") code (NaN for 0x7F and 0xFF)."""
     return float((lib or load()).oracle_fp8_value(int(code)))

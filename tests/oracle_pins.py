@@ -515,6 +515,60 @@ def check_fp8_blockwise_uniform(lib):
     assert np.array_equal(r0, r1)
 
 
+# --------------------------------------------------------------------------
+# grouped (MoE) GEMV: align step and per-slot products
+# --------------------------------------------------------------------------
+MGOLDEN = os.path.join(os.path.dirname(__file__), "golden", "moe_cases.json")
+with open(MGOLDEN) as _f:
+    MOE = json.load(_f)["cases"]
+
+
+def check_moe_align_hand(lib, orc=oracle):
+    """The page's worked example: counts, padded cumulative sum, padded row
+    count, tile experts, and the tokens tiles 1 and 3 read."""
+    for c in MOE:
+        srt, tiles, total = orc.moe_align(c["topk_ids"], c["E"], c["block"])
+        numel = c["T"] * c["topk"]
+        assert total == c["num_post_pad"], (c["id"], total)
+        assert list(tiles) == c["tile_experts"], (c["id"], tiles)
+        assert list(srt) == c["sorted_ids_ascending"], (c["id"], srt)
+        b = c["block"]
+        counts = [int(np.sum(np.array(c["topk_ids"]) == e)) for e in range(c["E"])]
+        assert counts == c["counts"]
+        # segment starts: the first row of each expert's tiles (an expert
+        # without tiles starts where the next one does)
+        starts = [total] * (c["E"] + 1)
+        for e in range(c["E"] - 1, -1, -1):
+            own = np.nonzero(tiles == e)[0]
+            starts[e] = int(own[0]) * b if own.size else starts[e + 1]
+        assert starts == c["cumsum"], starts
+        if "tile1_valid_tokens" in c:
+            t1 = [int(x) // c["topk"] for x in srt[b:2 * b] if x < numel]
+            t3 = sorted(int(x) // c["topk"] for x in srt[3 * b:4 * b] if x < numel)
+            assert t1 == c["tile1_valid_tokens"] and t3 == c["tile3_tokens"], (t1, t3)
+
+
+def check_moe_vs_brute(lib, orc=oracle):
+    """Each slot's row of the grouped reference equals the exact rational
+    brute force of its token's activations with its expert's weights."""
+    rng = np.random.Generator(np.random.PCG64(61))
+    E, T, topk, K, N, G = 3, 5, 2, 64, 8, 32
+    wfmt, afmt, sfmt, has_zp = "w4", "bf16", "bf16", True
+    experts = [arrays_any_format(T, N, K, G, wfmt, afmt, sfmt, has_zp, seed=62 + e) for e in range(E)]
+    A = experts[0].A                                   # one activation matrix for all experts
+    W = np.stack([x.W for x in experts])
+    S = np.stack([x.S for x in experts])
+    Z = np.stack([x.Z for x in experts])
+    ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)]).reshape(-1)
+    ref, _ = orc.moe(T, topk, N, K, G, wfmt, afmt, sfmt, has_zp, A, ids, W, S, Z, lib=lib)
+    for i in range(T * topk):
+        e, t = int(ids[i]), i // topk
+        p = SimpleNamespace(**vars(experts[e]))
+        p.A, p.M = A[t:t + 1], 1
+        exact = np.array([float(x) for x in brute_force(p)[0][0]])
+        assert np.allclose(ref[i], exact, rtol=1e-12, atol=1e-15), (i, e, t)
+
+
 def all_checks():
     """(name, callable(lib)) for every pin."""
     out = [(f"hand_{c['id']}", (lambda c: lambda lib: check_hand_case(lib, c))(c)) for c in HAND]
@@ -537,4 +591,5 @@ def all_checks():
             ("fp8_gemm_brute_0", lambda lib: check_fp8_gemm_brute(lib, 0)),
             ("fp8_gemm_brute_1", lambda lib: check_fp8_gemm_brute(lib, 1)),
             ("fp8_blockwise_uniform", check_fp8_blockwise_uniform)]
+    out += [("moe_align_hand", check_moe_align_hand), ("moe_vs_brute", check_moe_vs_brute)]
     return out

@@ -85,3 +85,36 @@ def test_mutant_is_caught(tmp_path, source, name, orig, mut):
         except (AssertionError, ValueError):
             caught.append(check_name)
     assert caught, f"mutant {name} passed every pin"
+
+
+# Planted mistakes in the Python half of the oracle (the MoE composition in
+# oracle/__init__.py): a mutated copy of the module is loaded under another
+# name and run through the MoE pins.
+PY_MUTANTS = [
+    ("moe_token_index", "tokens = slots[pick] // topk", "tokens = slots[pick] % topk"),
+    ("moe_pad_down", "total += -(-counts[e] // block) * block", "total += (counts[e] // block) * block"),
+    ("moe_tile_count", "tile_experts += [e] * (-(-counts[e] // block))", "tile_experts += [e] * (counts[e] // block + 1)"),
+    ("moe_sentinel", "sorted_ids = [numel] * total", "sorted_ids = [0] * total"),
+    ("moe_expert_shift", "pick = np.nonzero(ids[slots] == e)[0]", "pick = np.nonzero(ids[slots] == (e + 1) % W.shape[0])[0]"),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_is_caught(name, orig, mut):
+    import importlib.util
+    path = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+    with open(path) as f:
+        src = f.read()
+    assert src.count(orig) == 1, f"mutation site for {name} must be unique"
+    spec = importlib.util.spec_from_loader(f"oracle_mut_{name}", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__file__ = path
+    exec(compile(src.replace(orig, mut), path, "exec"), mod.__dict__)
+    lib = oracle.load()
+    caught = []
+    for check in (pins.check_moe_align_hand, pins.check_moe_vs_brute):
+        try:
+            check(lib, orc=mod)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+    assert caught, f"mutant {name} passed every MoE pin"

@@ -77,7 +77,7 @@ def lib():
             L.qgemm_moe_workspace_bytes.restype = c_size
             L.qgemm_moe_workspace_bytes.argtypes = [c_int] * 8
             L.qgemm_moe_run.restype = c_int
-            L.qgemm_moe_run.argtypes = [c_int] * 9 + [vp] * 8 + [c_size, vp]
+            L.qgemm_moe_run.argtypes = [c_int] * 9 + [vp] * 9 + [c_size, vp]
             L.qgemm_fp8_quantize.restype = c_int
             L.qgemm_fp8_quantize.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
             L.qgemm_fp8_gemm.restype = c_int

@@ -11,8 +11,8 @@
 // position of its expert's segment. As on the page, the order of slots
 // within an expert follows the atomics' arrival; the grouped GEMV computes
 // every row on its own, so its output does not depend on that order. Slots
-// whose expert is outside [0, E) are skipped (their output rows are not
-// written).
+// whose expert is outside [0, E) are skipped (their output rows are left
+// unspecified).
 #include "common.h"
 
 namespace qg {

@@ -196,11 +196,12 @@ int qgemm_moe_max_tiles(int numel, int E, int block);
 
 /*
  * Align (section 六.3), one kernel on `stream`: from topk_ids (int32
- * [numel], experts in [0, E); slots with other values are skipped and their
- * output rows are not written) write sorted_ids (the slots grouped by
+ * [numel], experts in [0, E); slots with other values are skipped) write
+ * sorted_ids (the slots grouped by
  * expert, each expert's segment padded to a multiple of `block` with the
  * value numel), tile_experts (each block's expert, -1 past the padded rows)
- * and num_post_pad (one int: the padded row count). The order of slots
+ * and num_post_pad (one int: the padded row count); the output rows of
+ * skipped slots are unspecified. The order of slots
  * within an expert follows atomic arrival, as on the page; the grouped GEMV's
  * output does not depend on it. 1 <= E <= 1024; device pointers, 16-byte
  * aligned.

@@ -139,6 +139,34 @@ def test_fp8_validation():
         assert g(**{kw: MIS}) == qg.EALIGN, kw
 
 
+def test_moe_validation():
+    L = qg.lib()
+    assert L.qgemm_moe_max_tiles(10, 3, 4) == 4            # (10 + 3 * 3) // 4
+    assert L.qgemm_moe_max_tiles(0, 3, 4) == 2            # (0 + 3 * 3) // 4
+    assert L.qgemm_moe_max_tiles(10, 0, 4) == 0            # no experts
+    assert L.qgemm_moe_max_tiles(10, 2000, 4) == 0         # more experts than the align step holds
+    assert L.qgemm_moe_max_tiles(10, 3, 3) == 0            # block not 1, 2, 4, 8
+    a = lambda ids=P, n=10, E=3, b=4, s=P2, t=P, npp=P: L.qgemm_moe_align(ids, n, E, b, s, t, npp, None)
+    assert a(n=-1) == qg.EINVAL
+    assert a(b=3) == qg.EUNSUPPORTED
+    assert a(ids=None) == qg.EINVAL and a(s=None) == qg.EINVAL and a(t=None) == qg.EINVAL and a(npp=None) == qg.EINVAL
+    assert a(ids=MIS) == qg.EALIGN and a(s=MIS) == qg.EALIGN
+    r = lambda T=4, topk=2, N=256, K=256, G=128, prec=1, zp=0, E=8, b=4, A=P, W=P, S=P, Z=None, srt=P, te=P, npp=P, \
+        out=P2, ws=None, wsb=0: L.qgemm_moe_run(T, topk, N, K, G, prec, zp, E, b, A, W, S, Z, srt, te, npp, out, ws,
+                                                  wsb, None)
+    assert r(T=0, A=None, W=None, S=None, srt=None, te=None, npp=None, out=None) == qg.OK
+    assert r(prec=2) == qg.EUNSUPPORTED                   # bf16 activations only
+    assert r(topk=0) == qg.EINVAL and r(T=-1) == qg.EINVAL
+    assert r(G=64) == qg.EUNSUPPORTED and r(K=200) == qg.EINVAL
+    assert r(zp=1, N=250, Z=P) == qg.EUNSUPPORTED and r(zp=1, Z=None) == qg.EINVAL
+    for kw in ("A", "W", "S", "srt", "te", "npp", "out"):
+        assert r(**{kw: None}) == qg.EINVAL, kw
+        assert r(**{kw: MIS}) == qg.EALIGN, kw
+    need = L.qgemm_moe_workspace_bytes(4, 2, 256, 1024, 128, 1, 8, 4)
+    assert need > 0                                        # a narrow shape is split along K
+    assert r(K=1024, ws=None, wsb=0) == qg.EWORKSPACE and r(K=1024, ws=P, wsb=need - 1) == qg.EWORKSPACE
+
+
 def test_pack_validation():
     L = qg.lib()
     assert L.qgemm_pack(None, P, 64, 8, qg.W4_A_BF16, None) == qg.EINVAL

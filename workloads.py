@@ -291,6 +291,56 @@ def make_fp8_config(name: str) -> Fp8Problem:
     return make_fp8_problem(name=name, **FP8_CONFIGS[name])
 
 
+@dataclasses.dataclass
+class MoeProblem:
+    """Grouped (MoE) W4A16 inputs: bf16 token activations, each token routed
+    to topk distinct experts, and E experts' int4 weights, bf16 scales and
+    optional zero-points stacked on a leading axis."""
+    T: int
+    topk: int
+    E: int
+    N: int
+    K: int
+    G: int
+    has_zp: bool
+    A: np.ndarray          # uint16 bf16 bits [T, K]
+    topk_ids: np.ndarray   # int32 [T, topk]
+    W: np.ndarray          # uint32 [E, K/8, N]
+    S: np.ndarray          # uint16 bf16 bits [E, K/G, N]
+    Z: Optional[np.ndarray]  # uint32 [E, K/G, N/8]
+    name: str = ""
+
+
+def make_moe_problem(T, topk, E, N, K, G, has_zp=False, seed=0, name="") -> MoeProblem:
+    """Activations ~ N(0,1) with per-row outliers; each token's topk experts
+    drawn uniformly without replacement; weights, scales and zero-points per
+    expert as make_problem draws them."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a, _ = make_activations(rng, T, K, G, "f32", 1e-3, 50.0)
+    A = f32_to_bf16_bits(a)
+    ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)]).astype(np.int32)
+    W = np.stack([random_words(rng, (K // 8, N)) for _ in range(E)])
+    S = np.stack([f32_to_bf16_bits(log_uniform(rng, 1e-3, 1e-2, (K // G, N)).astype(np.float32))
+                  for _ in range(E)])
+    Z = np.stack([random_words(rng, (K // G, N // 8)) for _ in range(E)]) if has_zp else None
+    return MoeProblem(T, topk, E, N, K, G, has_zp, A, ids, W, S, Z, name=name)
+
+
+# MoE layers: a Mixtral-8x7B-like fused gate+up (E = 8, top-2, K = 4096,
+# N = 2 x 14336) and a 64-expert top-6 layer with small experts (K = 2048,
+# N = 2 x 1408), at decode batch sizes
+MOE_CONFIGS = {
+    "moe_e8_top2_t1": dict(T=1, topk=2, E=8, N=28672, K=4096, G=128, seed=1200),
+    "moe_e8_top2_t16": dict(T=16, topk=2, E=8, N=28672, K=4096, G=128, seed=1201),
+    "moe_e64_top6_t16": dict(T=16, topk=6, E=64, N=2816, K=2048, G=128, seed=1202),
+    "moe_e64_top6_t64": dict(T=64, topk=6, E=64, N=2816, K=2048, G=128, seed=1203),
+}
+
+
+def make_moe_config(name: str) -> MoeProblem:
+    return make_moe_problem(name=name, **MOE_CONFIGS[name])
+
+
 def make_config(name: str, M: Optional[int] = None) -> Problem:
     c = dict(CONFIGS[name])
     c.pop("name")

@@ -234,6 +234,61 @@ def run_fp8(name, steps, warmup, mode):
     return res
 
 
+def run_moe(name, steps, warmup, mode, block=None):
+    """Grouped (MoE) W4A16 layer: one step = the align step plus the grouped
+    GEMV, over resident activations and routing ids; the expert stacks are
+    rotated like the dense weights. Algorithmic bytes count the weights,
+    scales and zero-points of the experts the routing uses, the activations
+    and the output."""
+    import numpy as np
+    import torch
+    import group_quantized_weight_amd as qg
+    import workloads as wl
+    vp = ctypes.c_void_p
+    p = wl.make_moe_config(name)
+    prec = qg.W4_A_BF16
+    if block is None:
+        block = qg.moe_default_block(p.T, p.topk, p.E, p.G, p.N)
+    per_expert = qg.packed_bytes(p.K, p.N, prec) + (p.K // p.G) * p.N * 2 + ((p.K // p.G) * p.N // 2 if p.has_zp else 0)
+    copies = max(1, min(16, math.ceil(ROTATE_BYTES / (p.E * per_expert))))
+    A = torch.from_numpy(p.A.view("int16")).view(torch.bfloat16).cuda()
+    packed = [qg.pack(torch.from_numpy(np.ascontiguousarray(p.W[e]).view(np.int32)).cuda(), p.K, p.N, prec)
+              for e in range(p.E)]
+    W0 = torch.stack(packed).contiguous()
+    del packed
+    S0 = torch.from_numpy(np.ascontiguousarray(p.S).view(np.int16)).view(torch.bfloat16).cuda()
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    Ss = [S0] + [S0.clone() for _ in range(copies - 1)]
+    ids = torch.from_numpy(p.topk_ids.reshape(-1).astype(np.int32)).cuda()
+    numel = p.T * p.topk
+    srt, tiles, npp = qg.moe_align(ids, p.E, block)
+    out = torch.empty((numel, p.N), dtype=torch.bfloat16, device="cuda")
+    need = int(qg.lib().qgemm_moe_workspace_bytes(p.T, p.topk, p.N, p.K, p.G, prec, p.E, block))
+    ws = qg.workspace(need, A.device)
+    L = qg.lib()
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+
+    def step(i):
+        st = L.qgemm_moe_align(vp(ids.data_ptr()), numel, p.E, block, vp(srt.data_ptr()), vp(tiles.data_ptr()),
+                               vp(npp.data_ptr()), stream)
+        assert st == 0, st
+        st = L.qgemm_moe_run(p.T, p.topk, p.N, p.K, p.G, prec, 0, p.E, block, vp(A.data_ptr()),
+                             vp(Ws[i % copies].data_ptr()), vp(Ss[i % copies].data_ptr()), None, vp(srt.data_ptr()),
+                             vp(tiles.data_ptr()), vp(npp.data_ptr()), vp(out.data_ptr()),
+                             vp(ws.data_ptr()) if ws is not None else None, need, stream)
+        assert st == 0, st
+
+    ms = time_steps(step, steps, warmup, mode)
+    used = len(np.unique(p.topk_ids))
+    nbytes = used * per_expert + p.T * p.K * 2 + numel * p.N * 2
+    res = dict(workload=name, T=p.T, topk=p.topk, E=p.E, experts_used=used, N=p.N, K=p.K, group=p.G, block=block,
+               us=round(ms * 1e3, 2), bytes=nbytes, gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+               frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), copies=copies)
+    del A, W0, S0, Ws, Ss, ids, srt, tiles, npp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(p, seconds=10.0):
     import numpy as np
     import oracle
@@ -261,6 +316,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--only", default=None, help="run one named workload only (profiling)")
     ap.add_argument("--force-path", type=int, default=-1, help="with --only: QG_PATH_* to force")
     ap.add_argument("--force-nsplit", type=int, default=0, help="with --only: K-split to force")
@@ -328,6 +384,9 @@ def bench(args):
         if args.only in wl.FP8_CONFIGS:
             log(json.dumps(run_fp8(args.only, args.steps, args.warmup, args.mode)))
             return
+        if args.only in wl.MOE_CONFIGS:
+            log(json.dumps(run_moe(args.only, args.steps, args.warmup, args.mode)))
+            return
         r, _ = run_workload(args.only, args.steps, args.warmup, args.mode, force_path=args.force_path,
                             force_nsplit=args.force_nsplit)
         log(json.dumps(r))
@@ -361,6 +420,13 @@ def bench(args):
             log(f"bench: {name}: gemm {r['gemm_us']} us ({r['gemm_tflops']} TFLOP/s), with quantization "
                 f"{r['step_us']} us, torch._scaled_mm {r['scaled_mm_us']}")
 
+    moe = []
+    if not args.no_moe:
+        for name in ("moe_e8_top2_t1", "moe_e8_top2_t16", "moe_e64_top6_t16", "moe_e64_top6_t64"):
+            r = run_moe(name, 100, 20, args.mode)
+            moe.append(r)
+            log(f"bench: {name}: {r['us']} us, {r['gbs']} GB/s over {r['experts_used']} experts")
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(p)
@@ -391,6 +457,7 @@ def bench(args):
                        "frac": round(gemm["tflops"] / BF16_PEAK_TFLOPS, 4), "nsplit": gemm["nsplit"]},
         "crossover": sweep,
         "fp8_w8a8": fp8,
+        "moe_grouped_gemv": moe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

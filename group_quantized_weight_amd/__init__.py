@@ -72,6 +72,8 @@ def lib():
             L.qgemm_run_ex.argtypes = run_args + [c_int, c_int]
             L.qgemm_moe_max_tiles.restype = c_int
             L.qgemm_moe_max_tiles.argtypes = [c_int] * 3
+            L.qgemm_moe_default_block.restype = c_int
+            L.qgemm_moe_default_block.argtypes = [c_int] * 5
             L.qgemm_moe_align.restype = c_int
             L.qgemm_moe_align.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp, vp]
             L.qgemm_moe_workspace_bytes.restype = c_size
@@ -183,6 +185,11 @@ def quantize_activations(A, G: int, Aq=None, a_scales=None, stream=None):
     if st != OK:
         raise QGemmError(st, "qgemm_quantize_activations")
     return Aq, a_scales
+
+
+def moe_default_block(T: int, topk: int, E: int, G: int, N: int) -> int:
+    """Rows per grouped block this library recommends (see include/qgemm.h)."""
+    return int(lib().qgemm_moe_default_block(T, topk, E, G, N))
 
 
 def moe_align(topk_ids, E: int, block: int, stream=None):

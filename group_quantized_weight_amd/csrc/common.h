@@ -71,6 +71,10 @@ struct SmallArgs {
   float *partial;          // [nsplit][M][Np] (nsplit > 1)
   int M, N, K, Np;
   int ngroups, nsplit;     // K / 128 groups split into nsplit slices
+  // grouped (MoE) launches only (see GemvArgs)
+  const int *sorted_ids, *tile_experts, *num_post_pad;
+  int topk, arows;         // activation row = slot / topk, of arows rows
+  size_t w_expert_words, s_expert_elems, z_expert_words;
 };
 
 // Host-side launchers (defined next to their kernels). They return the HIP
@@ -80,6 +84,8 @@ hipError_t launch_gemv(int wfmt, int afmt, int sfmt, int ofmt, bool zp, int mb, 
 // grouped (MoE) W4A16 GEMV: rows gathered through GemvArgs::sorted_ids
 hipError_t launch_gemv_grouped(int ofmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds_bytes,
                                hipStream_t stream);
+// grouped (MoE) small-M MFMA path: blocks of 16 mb routed rows
+hipError_t launch_gemm_small_grouped(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t stream);
 // routing metadata for the grouped GEMV (counting sort by expert)
 hipError_t launch_moe_align(const int *topk_ids, int numel, int E, int block, int max_tiles, int *sorted_ids,
                             int *tile_experts, int *num_post_pad, hipStream_t stream);

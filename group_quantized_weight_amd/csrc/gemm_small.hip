@@ -25,6 +25,11 @@
 //   - the 4 waves' results are added in wave order (waves 1..3 through LDS),
 //     then written to the output (nsplit == 1) or to float32 partials that a
 //     second kernel adds in the order z = 0..nsplit-1.
+// Grouped (MoE) mode: blockIdx.z is a block of 16 MB routed rows of one
+// expert (the align step's sorted_ids); row i of the block gathers the
+// activations of token sorted_ids[.] / topk (padding rows read zeros), the
+// expert's weights, scales and zero-points are offset by its index, and the
+// row is written to output row sorted_ids[.].
 #include "common.h"
 
 namespace qg {
@@ -71,7 +76,7 @@ __device__ __forceinline__ bf16x8_s bias_operand(int z) {
 
 }  // namespace
 
-template <int MB, int OF, bool ZP>
+template <int MB, int OF, bool ZP, bool GR>
 __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a) {
   extern __shared__ __align__(16) unsigned char s_red[];   // [waves - 1][MB * 16][64] float32
 
@@ -86,8 +91,24 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
   split_range(a.ngroups, a.nsplit, z, gb, gcount);
   split_range(gcount, kWaves, wave, wg0, wgc);
 
+  // grouped row blocks: this block's expert, or nothing to do
+  const uint32_t *Wb = a.W;
+  const uint16_t *Sb = a.S;
+  const uint32_t *Zb = a.Z;
+  const int r0 = GR ? blockIdx.z * 16 * MB : 0;   // first routed row of the block
+  if constexpr (GR) {
+    if (r0 >= *a.num_post_pad) return;
+    const int e = a.tile_experts[blockIdx.z];
+    if (e < 0) return;
+    Wb += (size_t)e * a.w_expert_words;
+    Sb += (size_t)e * a.s_expert_elems;
+    if constexpr (ZP) Zb += (size_t)e * a.z_expert_words;
+  }
+  // output row of block row `row` (>= M: not written)
+  auto out_row = [&](int row) { return GR ? a.sorted_ids[r0 + row] : row; };
+
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.W + (size_t)tile * R * kTileCols), (short)0, R * kTileCols * 4, kBufWord3s);
+      (void *)(Wb + (size_t)tile * R * kTileCols), (short)0, R * kTileCols * 4, kBufWord3s);
   const int w_voff = (lk * kTileCols + 4 * li) * 4;
   // scales and zero-points of the lane's 4 columns (N % 8 == 0: all 4 are
   // in or all out; a lane past N reads column 0's and its results are
@@ -95,14 +116,26 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
   const int ncol = tile * kTileCols + 4 * li;
   const int scol = ncol < a.N ? ncol : 0;
   const __amdgpu_buffer_rsrc_t s_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.S, (short)0, a.ngroups * a.N * 2, kBufWord3s);
+      __builtin_amdgcn_make_buffer_rsrc((void *)Sb, (short)0, a.ngroups * a.N * 2, kBufWord3s);
   const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)a.Z, (short)0, ZP ? a.ngroups * (a.N >> 3) * 4 : 0, kBufWord3s);
+      (void *)Zb, (short)0, ZP ? a.ngroups * (a.N >> 3) * 4 : 0, kBufWord3s);
   // activations: fragment (fm, s) of lane (li, lk) is row 16 fm + li,
   // k = 128 g + 32 s + 8 lk .. +7; rows past M read zeros (range check of
   // the VGPR offset; the group offset in the SGPR operand stays in the row)
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.A, (short)0, a.M * a.K * 2, kBufWord3s);
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.A, (short)0, (GR ? a.arows : a.M) * a.K * 2, kBufWord3s);
+  // byte offset of each fragment row's activations (a padding row of a
+  // grouped block gets an out-of-range offset: zeros, no memory access)
+  int a_off[MB];
+#pragma unroll
+  for (int fm = 0; fm < MB; ++fm) {
+    if constexpr (GR) {
+      const int slot = out_row(16 * fm + li);
+      a_off[fm] = slot < a.M ? (slot / a.topk) * a.K * 2 : (int)0x80000000u;
+    } else {
+      a_off[fm] = (16 * fm + li) * a.K * 2;
+    }
+  }
 
   const uint32_t magic = magic_pair();
   f32x4_s acc[MB][4];
@@ -133,7 +166,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
       for (int s = 0; s < 4; ++s)
         L.af[fm][s] = __builtin_bit_cast(
             bf16x8_s, __builtin_amdgcn_raw_buffer_load_b128(
-                          a_rsrc, ((16 * fm + li) * a.K + 32 * s + 8 * lk) * 2, g * 256, 0));
+                          a_rsrc, a_off[fm] | ((32 * s + 8 * lk) * 2), g * 256, 0));
     L.sv = __builtin_bit_cast(u32x2_s, __builtin_amdgcn_raw_buffer_load_b64(s_rsrc, scol * 2, g * a.N * 2, 0));
     L.zw = 0x88888888u;
     if constexpr (ZP)
@@ -202,7 +235,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
   for (int fm = 0; fm < MB; ++fm)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 16 * fm + 4 * lk + r;
+      const int row = out_row(16 * fm + 4 * lk + r);
       f32x4_s v = (f32x4_s){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) v += *(const f32x4_s *)&red[(((w - 1) * MB + fm) * 16 + 4 * lk + r) * 64 + 4 * li];
@@ -219,20 +252,20 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
     }
 }
 
-template <int MB, int OF, bool ZP>
+template <int MB, int OF, bool ZP, bool GR>
 static hipError_t go_small(const SmallArgs &a, dim3 grid, hipStream_t st) {
   const size_t lds = (size_t)(kWaves - 1) * MB * 16 * 64 * 4;
-  gemm_small_kernel<MB, OF, ZP><<<grid, kWaves * kWave, lds, st>>>(a);
+  gemm_small_kernel<MB, OF, ZP, GR><<<grid, kWaves * kWave, lds, st>>>(a);
   return hipGetLastError();
 }
 
-template <int OF, bool ZP>
+template <int OF, bool ZP, bool GR>
 static hipError_t go_small_mb(int mb, const SmallArgs &a, dim3 grid, hipStream_t st) {
   switch (mb) {
-    case 1: return go_small<1, OF, ZP>(a, grid, st);
-    case 2: return go_small<2, OF, ZP>(a, grid, st);
-    case 3: return go_small<3, OF, ZP>(a, grid, st);
-    case 4: return go_small<4, OF, ZP>(a, grid, st);
+    case 1: return go_small<1, OF, ZP, GR>(a, grid, st);
+    case 2: return go_small<2, OF, ZP, GR>(a, grid, st);
+    case 3: return go_small<3, OF, ZP, GR>(a, grid, st);
+    case 4: return go_small<4, OF, ZP, GR>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -241,8 +274,17 @@ static hipError_t go_small_mb(int mb, const SmallArgs &a, dim3 grid, hipStream_t
 // M <= 64 here (mb = ceil(M / 16) row blocks of 16).
 hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t st) {
   if (a.N % 8 != 0 || a.K % 128 != 0 || mb < 1 || mb > 4 || a.M > 16 * mb) return hipErrorInvalidValue;
-  if (ofmt == O_BF16) return zp ? go_small_mb<O_BF16, true>(mb, a, grid, st) : go_small_mb<O_BF16, false>(mb, a, grid, st);
-  return zp ? go_small_mb<O_F32, true>(mb, a, grid, st) : go_small_mb<O_F32, false>(mb, a, grid, st);
+  if (ofmt == O_BF16)
+    return zp ? go_small_mb<O_BF16, true, false>(mb, a, grid, st) : go_small_mb<O_BF16, false, false>(mb, a, grid, st);
+  return zp ? go_small_mb<O_F32, true, false>(mb, a, grid, st) : go_small_mb<O_F32, false, false>(mb, a, grid, st);
+}
+
+// Grouped (MoE) blocks of 16 mb routed rows; grid (Np / 64, nsplit, row blocks).
+hipError_t launch_gemm_small_grouped(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t st) {
+  if (a.N % 8 != 0 || a.K % 128 != 0 || (mb != 1 && mb != 2 && mb != 4)) return hipErrorInvalidValue;
+  if (ofmt == O_BF16)
+    return zp ? go_small_mb<O_BF16, true, true>(mb, a, grid, st) : go_small_mb<O_BF16, false, true>(mb, a, grid, st);
+  return zp ? go_small_mb<O_F32, true, true>(mb, a, grid, st) : go_small_mb<O_F32, false, true>(mb, a, grid, st);
 }
 
 }  // namespace qg

@@ -350,8 +350,12 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 
+bool moe_block_ok(int block) {
+  return block == 1 || block == 2 || block == 4 || block == 8 || block == 16 || block == 32 || block == 64;
+}
+
 int qgemm_moe_max_tiles(int numel, int E, int block) {
-  if (numel < 0 || E < 1 || E > kMoeMaxExperts || !(block == 1 || block == 2 || block == 4 || block == 8)) return 0;
+  if (numel < 0 || E < 1 || E > kMoeMaxExperts || !moe_block_ok(block)) return 0;
   const long long t = ((long long)numel + (long long)E * (block - 1)) / block;
   return t > 65535 ? 0 : (int)(t > 0 ? t : 1);
 }
@@ -375,27 +379,35 @@ namespace {
 // Plan of the grouped GEMV: one row block per possible tile, a K-split when
 // the column tiles times the tiles that are surely used (numel / block)
 // leave compute units idle; the same rules as the dense GEMV.
+// Blocks of 1..8 rows run on the grouped GEMV, blocks of 16, 32 or 64 rows
+// on the grouped small-M MFMA path (groups of 128, N % 8 == 0).
 int moe_plan(int numel, int N, int K, int G, const Formats &f, int E, int block, int force_nsplit, Plan &p) {
   const int cus = device_cus();
   const size_t Np = padded_cols(N);
-  p.path = QG_PATH_GEMV;
-  p.mb = block;
+  const bool mfma = block >= 16;
+  if (mfma && (G != 128 || N % 8 != 0)) return QG_EUNSUPPORTED;
+  p.path = mfma ? QG_PATH_SMALL : QG_PATH_GEMV;
+  p.mb = mfma ? block / 16 : block;
   p.mblocks = qgemm_moe_max_tiles(numel, E, block);
   p.tiles_x = (int)(Np / kTileCols);
   p.units = K / G;
   const long long used = (numel + block - 1) / block;
   const long long base = (long long)p.tiles_x * (used > 0 ? used : 1);
-  int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((2LL * cus + base - 1) / base));
+  const long long target = mfma ? cus : 2LL * cus;
+  int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((target + base - 1) / base));
   ns = balance(p.units, ns);
-  while (ns < p.units && gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) ns = balance(p.units, ns + 1);
+  if (!mfma)
+    while (ns < p.units && gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) ns = balance(p.units, ns + 1);
   if (force_nsplit <= 0)
     while (ns > 1 && (size_t)ns * numel * Np * 4 > kPartialCap) {
       const int lower = balance(p.units, ns - 1);
-      if (gemv_lds(f, p.mb, G, p.units, lower) > kGemvLdsCap) break;
+      if (!mfma && gemv_lds(f, p.mb, G, p.units, lower) > kGemvLdsCap) break;
       ns = lower;
     }
-  if (gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) return QG_EUNSUPPORTED;
-  p.lds = gemv_lds(f, p.mb, G, p.units, ns);
+  if (!mfma) {
+    if (gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) return QG_EUNSUPPORTED;
+    p.lds = gemv_lds(f, p.mb, G, p.units, ns);
+  }
   p.nsplit = ns;
   p.ws = ns > 1 ? (size_t)ns * numel * Np * 4 : 0;
   return QG_OK;
@@ -411,6 +423,17 @@ int check_moe(int T, int topk, int N, int K, int G, int prec, int has_zp, int E,
 }
 
 }  // namespace
+
+int qgemm_moe_default_block(int T, int topk, int E, int group, int N) {
+  if (T < 1 || topk < 1 || E < 1) return 1;
+  if (T == 1 || group != 128 || N % 8 != 0) return T == 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));
+  // one 16-row MFMA block holds every row of an expert when T <= 16 (a
+  // token's experts are distinct); beyond, size the block for about twice
+  // the average rows per expert
+  if (T <= 16) return 16;
+  const long long twice_avg = 2LL * T * topk / E;
+  return twice_avg <= 16 ? 16 : (twice_avg <= 32 ? 32 : 64);
+}
 
 size_t qgemm_moe_workspace_bytes(int T, int topk, int N, int K, int group, int prec, int E, int block) {
   Formats f;
@@ -441,26 +464,51 @@ int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp
     if (!workspace || workspace_bytes < p.ws) return QG_EWORKSPACE;
     if (!aligned16(workspace)) return QG_EALIGN;
   }
-  GemvArgs a = {};
-  a.A = A;
-  a.W = (const uint32_t *)w_packed;
-  a.S = scales;
-  a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
-  a.out = out;
-  a.partial = p.nsplit > 1 ? (float *)workspace : nullptr;
-  a.M = numel; a.N = N; a.K = K; a.G = group; a.Np = (int)padded_cols(N);
-  a.ngroups = K / group;
-  a.nsplit = p.nsplit;
-  a.sorted_ids = sorted_ids;
-  a.tile_experts = tile_experts;
-  a.num_post_pad = num_post_pad;
-  a.topk = topk;
-  a.w_expert_words = qgemm_packed_bytes(K, N, prec) / 4;
-  a.s_expert_bytes = (size_t)(K / group) * N * 2;
-  a.z_expert_words = (size_t)(K / group) * (N / 8);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_gemv_grouped(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.mblocks, p.nsplit), p.lds, s);
-  if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, a.partial, out, numel, N, a.Np, p.nsplit, s);
+  float *partial = p.nsplit > 1 ? (float *)workspace : nullptr;
+  const int Np = (int)padded_cols(N);
+  hipError_t e;
+  if (p.path == QG_PATH_SMALL) {
+    SmallArgs a = {};
+    a.A = (const uint16_t *)A;
+    a.W = (const uint32_t *)w_packed;
+    a.S = (const uint16_t *)scales;
+    a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
+    a.out = out;
+    a.partial = partial;
+    a.M = numel; a.N = N; a.K = K; a.Np = Np;
+    a.ngroups = K / 128;
+    a.nsplit = p.nsplit;
+    a.sorted_ids = sorted_ids;
+    a.tile_experts = tile_experts;
+    a.num_post_pad = num_post_pad;
+    a.topk = topk;
+    a.arows = T;
+    a.w_expert_words = qgemm_packed_bytes(K, N, prec) / 4;
+    a.s_expert_elems = (size_t)(K / 128) * N;
+    a.z_expert_words = (size_t)(K / 128) * (N / 8);
+    e = launch_gemm_small_grouped(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.nsplit, p.mblocks), s);
+  } else {
+    GemvArgs a = {};
+    a.A = A;
+    a.W = (const uint32_t *)w_packed;
+    a.S = scales;
+    a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
+    a.out = out;
+    a.partial = partial;
+    a.M = numel; a.N = N; a.K = K; a.G = group; a.Np = Np;
+    a.ngroups = K / group;
+    a.nsplit = p.nsplit;
+    a.sorted_ids = sorted_ids;
+    a.tile_experts = tile_experts;
+    a.num_post_pad = num_post_pad;
+    a.topk = topk;
+    a.w_expert_words = qgemm_packed_bytes(K, N, prec) / 4;
+    a.s_expert_bytes = (size_t)(K / group) * N * 2;
+    a.z_expert_words = (size_t)(K / group) * (N / 8);
+    e = launch_gemv_grouped(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.mblocks, p.nsplit), p.lds, s);
+  }
+  if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, partial, out, numel, N, Np, p.nsplit, s);
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 

@@ -185,14 +185,19 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
  * times its expert's weights,
  *     out[i][n] = sum_g s_e[g,n] * sum_{k in g} A[i / topk][k] * (q_e[k,n] - z_e[g,n]),
  * e = topk_ids[i]. Rows of one expert are gathered into blocks of `block`
- * rows (1, 2, 4 or 8) by the align step (section 六.3), so each block reads
- * its expert's weights once.
+ * rows by the align step (section 六.3), so each block reads its expert's
+ * weights once: blocks of 1, 2, 4 or 8 rows run on the vector-ALU GEMV,
+ * blocks of 16, 32 or 64 rows on the small-M MFMA path (groups of 128,
+ * N % 8 == 0). qgemm_moe_default_block gives the block this library
+ * recommends for a shape (1 for a single token, whose experts each get one
+ * row; 16 up to 16 tokens, which puts every expert's rows in one block).
  *
  * qgemm_moe_max_tiles: row blocks the align step may produce for numel
  * routed slots (0 if the arguments are invalid); sorted_ids holds
  * max_tiles * block ints and tile_experts max_tiles ints.
  */
 int qgemm_moe_max_tiles(int numel, int E, int block);
+int qgemm_moe_default_block(int T, int topk, int E, int group, int N);
 
 /*
  * Align (section 六.3), one kernel on `stream`: from topk_ids (int32

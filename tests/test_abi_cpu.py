@@ -145,7 +145,14 @@ def test_moe_validation():
     assert L.qgemm_moe_max_tiles(0, 3, 4) == 2            # (0 + 3 * 3) // 4
     assert L.qgemm_moe_max_tiles(10, 0, 4) == 0            # no experts
     assert L.qgemm_moe_max_tiles(10, 2000, 4) == 0         # more experts than the align step holds
-    assert L.qgemm_moe_max_tiles(10, 3, 3) == 0            # block not 1, 2, 4, 8
+    assert L.qgemm_moe_max_tiles(10, 3, 3) == 0            # block not 1, 2, 4, 8, 16, 32, 64
+    assert L.qgemm_moe_max_tiles(10, 3, 16) == (10 + 3 * 15) // 16
+    assert L.qgemm_moe_max_tiles(10, 3, 128) == 0
+    assert L.qgemm_moe_default_block(1, 2, 8, 128, 28672) == 1
+    assert L.qgemm_moe_default_block(16, 2, 8, 128, 28672) == 16
+    assert L.qgemm_moe_default_block(64, 6, 64, 128, 2816) == 16     # 2 * 64 * 6 / 64 = 12
+    assert L.qgemm_moe_default_block(512, 2, 8, 128, 4096) == 64
+    assert L.qgemm_moe_default_block(16, 2, 8, 32, 4096) == 8        # groups of 32: the GEMV
     a = lambda ids=P, n=10, E=3, b=4, s=P2, t=P, npp=P: L.qgemm_moe_align(ids, n, E, b, s, t, npp, None)
     assert a(n=-1) == qg.EINVAL
     assert a(b=3) == qg.EUNSUPPORTED
@@ -159,6 +166,7 @@ def test_moe_validation():
     assert r(topk=0) == qg.EINVAL and r(T=-1) == qg.EINVAL
     assert r(G=64) == qg.EUNSUPPORTED and r(K=200) == qg.EINVAL
     assert r(zp=1, N=250, Z=P) == qg.EUNSUPPORTED and r(zp=1, Z=None) == qg.EINVAL
+    assert r(b=16, G=32) == qg.EUNSUPPORTED and r(b=16, N=250) == qg.EUNSUPPORTED   # MFMA blocks
     for kw in ("A", "W", "S", "srt", "te", "npp", "out"):
         assert r(**{kw: None}) == qg.EINVAL, kw
         assert r(**{kw: MIS}) == qg.EALIGN, kw

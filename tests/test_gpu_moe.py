@@ -54,7 +54,8 @@ def _check_align(ids, E, block):
 
 
 @pytest.mark.parametrize("T,topk,E,block", [(5, 2, 3, 4), (1, 1, 1, 1), (16, 2, 8, 4), (64, 6, 64, 8),
-                                            (300, 8, 256, 2), (7, 3, 40, 8)])
+                                            (300, 8, 256, 2), (7, 3, 40, 8), (16, 2, 8, 16), (100, 6, 64, 32),
+                                            (512, 2, 8, 64)])
 def test_align(T, topk, E, block):
     rng = np.random.Generator(np.random.PCG64(1700 + T + E))
     ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)])
@@ -104,6 +105,11 @@ def _run_case(p, block, prec, slots=None, cols=None):
     (16, 2, 8, 4, 32, False, 776, 512),
     (7, 3, 40, 8, 128, True, 256, 256),
     (33, 6, 16, 2, 32, True, 520, 1024),
+    # blocks of 16, 32, 64 rows: the small-M MFMA path (groups of 128)
+    (5, 2, 3, 16, 128, False, 1000, 512),
+    (16, 2, 8, 16, 128, True, 776, 1024),
+    (40, 3, 4, 32, 128, False, 256, 256),
+    (70, 2, 2, 64, 128, True, 512, 512),
 ])
 def test_moe_run(prec, T, topk, E, block, G, zp, N, K):
     p = wl.make_moe_problem(T, topk, E, N, K, G, zp, seed=1800 + T + E + N + prec)
@@ -139,5 +145,15 @@ def test_moe_workload_full_size(name):
     p = wl.make_moe_config(name)
     cols = sample_indices(p.N, 192, 6)
     slots = sample_indices(p.T * p.topk, 48, 7) if p.T * p.topk > 48 else None
-    o, ref, bound = _run_case(p, 4, 1, slots=slots, cols=cols)
-    check(o, ref, bound, f"{name}", bf16_out=True)
+    block = qg.moe_default_block(p.T, p.topk, p.E, p.G, p.N)
+    o, ref, bound = _run_case(p, block, 1, slots=slots, cols=cols)
+    check(o, ref, bound, f"{name} block={block}", bf16_out=True)
+
+
+@pytest.mark.parametrize("block", [4, 16])
+def test_moe_gemv_and_mfma_blocks_agree(block):
+    """The same routing through the GEMV (4-row blocks) and the MFMA path
+    (16-row blocks): both within the gate of the oracle."""
+    p = wl.make_moe_problem(12, 2, 6, 1024, 1024, 128, True, seed=1950)
+    o, ref, bound = _run_case(p, block, 6)
+    check(o, ref, bound, f"moe block={block}")

@@ -12,10 +12,12 @@ Also reported: the MFMA path at M=1024 (TFLOP/s), the prefill crossover
 sweep against a dense bf16 torch.matmul on the same shapes, and the fp64 CPU
 oracle timed on the host cores (cpu_baseline).
 
-Timing: the K steps are captured in a HIP graph (the library's calls are
-capture-safe) and replayed; HIP events on the launch stream bracket the
-replay, with torch.cuda.synchronize() on both sides. --mode eager times a
-plain launch loop instead.
+Timing: each measurement first runs its step untimed for about 0.25 s (so
+the timed steps see the clocks the device settles at under that load), then
+the W warmup steps; the K timed steps are captured in a HIP graph (the
+library's calls are capture-safe) and replayed; HIP events on the launch
+stream bracket the replay, with torch.cuda.synchronize() on both sides.
+--mode eager times a plain launch loop instead.
 """
 import argparse
 import ctypes
@@ -33,6 +35,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 ROTATE_BYTES = 640 << 20
+SETTLE_S = 0.25
 
 
 def log(*a):
@@ -68,6 +71,15 @@ def time_steps(fn, steps, warmup, mode):
     needs a non-default stream)."""
     import torch
     stream = torch.cuda.current_stream()
+    # settle: run the step untimed for about SETTLE_S seconds first, so the
+    # timed steps see the clocks the device holds under this load
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(50):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()

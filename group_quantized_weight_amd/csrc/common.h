@@ -89,8 +89,9 @@ hipError_t launch_gemm_small_grouped(int ofmt, bool zp, int mb, const SmallArgs 
 // routing metadata for the grouped GEMV (counting sort by expert)
 hipError_t launch_moe_align(const int *topk_ids, int numel, int E, int block, int max_tiles, int *sorted_ids,
                             int *tile_experts, int *num_post_pad, hipStream_t stream);
-// int8 activations (float32 scales and output)
-hipError_t launch_gemv_i8(int wfmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds_bytes,
+// int8 activations (float32 scales and output); dq: the activations are
+// float32 and the kernel quantizes them per (row, group) itself
+hipError_t launch_gemv_i8(int wfmt, bool zp, bool dq, int mb, const GemvArgs &a, dim3 grid, size_t lds_bytes,
                           hipStream_t stream);
 hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t stream);
 // mb = ceil(M / 16) row blocks; grid (Np / 64, nsplit)

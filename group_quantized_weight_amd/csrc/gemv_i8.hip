@@ -26,6 +26,14 @@
 // The code sums and the activation scales of the workgroup's rows and groups
 // are computed / loaded once into LDS; the 4 group lanes sharing a column and
 // then the waves are added in a fixed order at the end.
+//
+// With DQ the activations arrive in float32 and the prologue quantizes the
+// rows and groups the workgroup needs (the dynamic per-group quantization
+// ahead of the integer product, in float32: scale = max|a| / 127, or 1 for a
+// group of zeros; code = clamp(rint(a / scale), -127, 127), the division
+// correctly rounded), so the codes never leave LDS: a lane takes 8
+// consecutive k of one (row, group), and the G / 8 lanes of a group combine
+// their maxima and code sums with lane exchanges.
 #include "common.h"
 
 namespace qg {
@@ -72,7 +80,16 @@ __device__ __forceinline__ u32x4_v stage_order(u32x4_v c) {
 
 }  // namespace
 
-template <int WF, bool ZP, int MB, int G>
+// 8 codes in k order -> the LDS order of stage_order.
+template <int WF>
+__device__ __forceinline__ uint2 stage_order8(uint32_t lo, uint32_t hi) {
+  if constexpr (WF == W4)
+    return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+  else
+    return make_uint2(lo, hi);
+}
+
+template <int WF, bool ZP, int MB, int G, bool DQ>
 __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(GemvArgs a) {
   constexpr int KPW = WF == W4 ? 8 : 4;   // k per packed word = staged bytes per word-row
   constexpr int RPG = G / KPW;             // word-rows per group: 4, 8, 16 or 32
@@ -141,6 +158,58 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(GemvArgs a) {
     }
   };
 
+  const int nasc = MB * gcount;
+  if constexpr (DQ) {
+    // ---- prologue: float32 activations quantized into LDS (codes, scales,
+    // code sums); the first weight batch is issued first ----
+    constexpr int L8 = G / 8;                       // lanes per (row, group)
+    const int ntask = nasc * L8;
+    issue(0);
+    for (int t0 = 0; t0 < ntask; t0 += kThreads) {  // uniform trip count: the exchanges see whole groups
+      const int t = t0 + threadIdx.x;
+      const int mg = t / L8, sub = t - mg * L8;
+      const int m = mg / gcount, g = mg - m * gcount;
+      const bool ok = t < ntask && m0 + m < a.M;
+      u32x4_v v0 = {0, 0, 0, 0}, v1 = v0;
+      if (ok) {
+        const float *src = (const float *)a.A + (size_t)(m0 + m) * a.K + (size_t)(gb + g) * G + 8 * sub;
+        v0 = *(const u32x4_v *)src;
+        v1 = *(const u32x4_v *)(src + 4);
+      }
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = __uint_as_float(v0[j]);
+        x[4 + j] = __uint_as_float(v1[j]);
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+#pragma unroll
+      for (int d = 1; d < L8; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+      const float sc = amax > 0.f ? amax / 127.f : 1.f;
+      uint32_t w[2] = {0u, 0u};
+      int csum = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = (int)fminf(fmaxf(__builtin_rintf(x[j] / sc), -127.f), 127.f);
+        csum += q;
+        w[j >> 2] |= ((uint32_t)(q & 0xFF)) << (8 * (j & 3));
+      }
+#pragma unroll
+      for (int d = 1; d < L8; d <<= 1) csum += __shfl_xor(csum, d);
+      if (t < ntask) {
+        *(uint2 *)(s_act + (size_t)m * row_bytes + (size_t)g * G + 8 * sub) = stage_order8<WF>(w[0], w[1]);
+        if (sub == 0) {
+          s_asc[mg] = ok ? sc : 0.f;
+          s_gsum[mg] = csum;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  } else {
   // ---- prologue: activation and scale loads, the first weight batch, LDS ----
   // Vector loads complete in order: the activations are issued before the
   // weights, so waiting for them never waits for the weight stream.
@@ -155,7 +224,6 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(GemvArgs a) {
     st[s] = *(const u32x4_v *)((const int8_t *)a.A + off);
     if (!ok) st[s] = (u32x4_v){0, 0, 0, 0};
   }
-  const int nasc = MB * gcount;
   float asc0 = 0.f;
   {
     const int idx = threadIdx.x < nasc ? threadIdx.x : 0;
@@ -195,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(GemvArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
 
   // ---- main loop: batches of LPB loads, group epilogues as groups finish ----
   float acc[MB][4];
@@ -317,30 +386,36 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(GemvArgs a) {
   }
 }
 
-template <int WF, bool ZP, int MB>
+template <int WF, bool ZP, int MB, bool DQ>
 static hipError_t go_i8(int G, const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   if (G == 32)
-    gemv_i8_kernel<WF, ZP, MB, 32><<<grid, kThreads, lds, st>>>(a);
+    gemv_i8_kernel<WF, ZP, MB, 32, DQ><<<grid, kThreads, lds, st>>>(a);
   else
-    gemv_i8_kernel<WF, ZP, MB, 128><<<grid, kThreads, lds, st>>>(a);
+    gemv_i8_kernel<WF, ZP, MB, 128, DQ><<<grid, kThreads, lds, st>>>(a);
   return hipGetLastError();
 }
 
-template <int WF, bool ZP>
+template <int WF, bool ZP, bool DQ>
 static hipError_t go_i8_mb(int mb, int G, const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   switch (mb) {
-    case 1: return go_i8<WF, ZP, 1>(G, a, grid, lds, st);
-    case 2: return go_i8<WF, ZP, 2>(G, a, grid, lds, st);
-    case 4: return go_i8<WF, ZP, 4>(G, a, grid, lds, st);
-    default: return go_i8<WF, ZP, 8>(G, a, grid, lds, st);
+    case 1: return go_i8<WF, ZP, 1, DQ>(G, a, grid, lds, st);
+    case 2: return go_i8<WF, ZP, 2, DQ>(G, a, grid, lds, st);
+    case 4: return go_i8<WF, ZP, 4, DQ>(G, a, grid, lds, st);
+    default: return go_i8<WF, ZP, 8, DQ>(G, a, grid, lds, st);
   }
 }
 
-hipError_t launch_gemv_i8(int wfmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+template <bool DQ>
+static hipError_t go_i8_fmt(int wfmt, bool zp, int mb, const GemvArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   if (wfmt == W4)
-    return zp ? go_i8_mb<W4, true>(mb, a.G, a, grid, lds, st) : go_i8_mb<W4, false>(mb, a.G, a, grid, lds, st);
-  if (wfmt == W8 && !zp) return go_i8_mb<W8, false>(mb, a.G, a, grid, lds, st);
+    return zp ? go_i8_mb<W4, true, DQ>(mb, a.G, a, grid, lds, st) : go_i8_mb<W4, false, DQ>(mb, a.G, a, grid, lds, st);
+  if (wfmt == W8 && !zp) return go_i8_mb<W8, false, DQ>(mb, a.G, a, grid, lds, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_i8(int wfmt, bool zp, bool dq, int mb, const GemvArgs &a, dim3 grid, size_t lds,
+                          hipStream_t st) {
+  return dq ? go_i8_fmt<true>(wfmt, zp, mb, a, grid, lds, st) : go_i8_fmt<false>(wfmt, zp, mb, a, grid, lds, st);
 }
 
 }  // namespace qg

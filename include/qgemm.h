@@ -67,8 +67,10 @@ enum {
     QG_W8_A_F32_DQ8 = 8    /* int8  | float32, quantized    | float32 | float32 */
 };
 /* Precisions 7 and 8 take float32 activations and quantize them inside the
- * call, exactly as qgemm_quantize_activations does, into the workspace; the
- * product then runs as precision 4 / 5 on those codes and scales. */
+ * call, exactly as qgemm_quantize_activations does: for M <= 4 inside the
+ * product kernel (the codes and scales stay on chip), above that with a
+ * pre-pass into the workspace. The product is then that of precision 4 / 5
+ * on those codes and scales, bit for bit. */
 
 /* Paths (for qgemm_plan / qgemm_run_ex). */
 enum {
@@ -109,9 +111,9 @@ int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, 
 /*
  * Device workspace bytes qgemm_run needs for this problem (0: none, and the
  * workspace pointer may be NULL). The workspace holds the int8 codes and
- * float32 scales of in-call activation quantization (precisions 7 and 8),
- * on the MFMA path the float32 activation sums per (group, row) of a
- * pre-pass, and the float32 partial sums of a K-split; its contents before a call do not matter. Calls
+ * float32 scales of in-call activation quantization (precisions 7 and 8,
+ * M > 4), on the MFMA path the float32 activation sums per (group, row) of
+ * a pre-pass, and the float32 partial sums of a K-split; its contents before a call do not matter. Calls
  * that share a workspace must not run concurrently.
  */
 size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec);
@@ -131,8 +133,7 @@ int qgemm_plan(int M, int N, int K, int group, int prec, int force_path, int for
  * out = the group-quantized product described at the top of this file.
  * Enqueues one kernel, or two when K is split (nsplit > 1: the partial sums
  * of the K-slices, then their fixed-order reduction); the MFMA path first
- * enqueues a pre-pass that sums each group of activations, and precisions 7
- * and 8 first enqueue the activation quantization.
+ * enqueues a pre-pass that sums each group of activations.
  *   M >= 0 (M == 0 is a no-op), N >= 1, K >= 1, K % group == 0, group in {32, 128}.
  *   A:         activations [M][K] (bf16 / float32 / int8 by prec)
  *   a_scales:  float32 [M][K/G] for *_A_I8, else NULL (unused)

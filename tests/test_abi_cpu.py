@@ -44,7 +44,7 @@ def test_layout_and_sizes():
     (dict(prec=qg.W4_A_F32_DQ8, A=MIS), qg.EALIGN),
     (dict(prec=qg.W8_A_F32_DQ8, K=100), qg.EINVAL),
     (dict(prec=qg.W4_A_F32_DQ8, path=qg.PATH_GEMM, M=300, G=128), qg.EUNSUPPORTED),
-    (dict(prec=qg.W4_A_F32_DQ8), qg.EWORKSPACE),      # its codes and scales live in the workspace
+
     (dict(M=-1), qg.EINVAL),
     (dict(N=0), qg.EINVAL),
     (dict(K=0), qg.EINVAL),
@@ -185,7 +185,8 @@ def test_pack_validation():
 
 CASES = [(1, 28672, 4096, 128, 1), (8, 28672, 8192, 128, 1), (1, 128256, 4096, 128, 1),
          (32, 11264, 2048, 32, 2), (32, 11000, 2048, 32, 5), (1, 256, 256, 32, 2),
-         (1, 11264, 2048, 32, 7), (32, 11264, 2048, 32, 8), (32, 11000, 2048, 32, 7),
+         (1, 11264, 2048, 32, 7), (32, 11264, 2048, 32, 8), (32, 11000, 2048, 32, 7), (4, 11264, 2048, 32, 8),
+         (5, 11264, 2048, 128, 7),
          (300, 4096, 4096, 128, 8)]
 CASES += [(M, 4096, 4096, 128, 1) for M in (1, 16, 64, 256, 1024, 4096)]
 
@@ -199,10 +200,11 @@ def test_plan_is_pure_and_consistent(M, N, K, G, prec):
     assert 1 <= ns <= K // G
     assert ws == qg.lib().qgemm_workspace_bytes(M, N, K, G, prec)
     if prec in (7, 8):
-        # int8 codes [M][K] and float32 scales [M][K/G] (each rounded up to 256
-        # bytes), then the plan of the same product on int8 activations
+        # the plan of the same product on int8 activations; above M = 4 the
+        # int8 codes [M][K] and float32 scales [M][K/G] (each rounded up to
+        # 256 bytes) come first in the workspace
         assert (path, ns) == qg.plan(M, N, K, G, prec - 3)[:2]
-        pre = -(-M * K // 256) * 256 + -(-M * (K // G) * 4 // 256) * 256
+        pre = 0 if M <= 4 else -(-M * K // 256) * 256 + -(-M * (K // G) * 4 // 256) * 256
         assert ws == pre + qg.plan(M, N, K, G, prec - 3)[2]
         assert path == qg.PATH_GEMV
         return

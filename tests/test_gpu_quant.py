@@ -89,10 +89,11 @@ def test_zero_rows_is_noop():
 
 @pytest.mark.parametrize("prec,zp", [(7, False), (7, True), (8, False)])
 @pytest.mark.parametrize("G", [32, 128])
-@pytest.mark.parametrize("M", [1, 4, 20])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 20])
 def test_in_call_quantization_matches_two_step(prec, zp, G, M):
     """Precision 7/8 equals quantize_activations followed by precision 4/5,
-    bit for bit, and meets the gate against the oracle."""
+    bit for bit, and meets the gate against the oracle (M <= 4: quantized in
+    the product kernel's prologue; M > 4: by a pre-pass into the workspace)."""
     import torch
     N, K = 1000, 1024
     p = wl.make_problem(M, N, K, G, prec, zp, seed=9300 + 10 * M + G + prec + zp, outlier_frac=0.01)

@@ -75,8 +75,9 @@ __global__ __launch_bounds__(256) void fp8_quant_block_kernel(const uint16_t *__
   if ((threadIdx.x & 15) == 0) a_scale[e / 128] = sc;
 }
 
-// One workgroup per row (per-token scale): the row's maximum over the
-// workgroup (lane exchanges, then LDS), then a second pass over the row.
+// Long rows (K > 8192), one workgroup per row (per-token scale): the row's
+// maximum over the workgroup (lane exchanges, then LDS), then a second pass
+// over the row.
 __global__ __launch_bounds__(256) void fp8_quant_row_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aq,
                                                            float *__restrict__ a_scale, int K) {
   __shared__ float s_max[4];
@@ -94,12 +95,55 @@ __global__ __launch_bounds__(256) void fp8_quant_row_kernel(const uint16_t *__re
   if (threadIdx.x == 0) a_scale[blockIdx.x] = sc;
 }
 
+// Rows of up to 512 NCH values: one wave per row (4 rows per workgroup), the
+// row held in registers (NCH 16-byte pieces per lane), so it is read once;
+// the wave's maximum by lane exchanges.
+template <int NCH>
+__global__ __launch_bounds__(256) void fp8_quant_row_wave_kernel(const uint16_t *__restrict__ A,
+                                                                uint8_t *__restrict__ Aq,
+                                                                float *__restrict__ a_scale, int M, int K) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;   // whole waves: every lane of a wave has the same row
+  const uint16_t *src = A + (size_t)row * K;
+  u32x4_v v[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int k = 8 * (lane + 64 * c);
+    v[c] = k < K ? *(const u32x4_v *)(src + k) : (u32x4_v){0, 0, 0, 0};
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) amax = fmaxf(amax, absmax8(v[c]));
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  uint8_t *dst = Aq + (size_t)row * K;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int k = 8 * (lane + 64 * c);
+    if (k < K) *(uint2 *)(dst + k) = quant8(v[c], sc);
+  }
+  if (lane == 0) a_scale[row] = sc;
+}
+
 hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int M, int K, int block,
                             hipStream_t st) {
   if (M == 0) return hipSuccess;
   if (block == 128) {
     const size_t total = (size_t)M * K;
     fp8_quant_block_kernel<<<(unsigned)((total / 8 + 255) / 256), 256, 0, st>>>(A, Aq, a_scale, total);
+  } else if (K <= 512 * 16) {
+    const dim3 grid((M + 3) / 4);
+    const int nch = (K + 511) / 512;
+    if (nch <= 2)
+      fp8_quant_row_wave_kernel<2><<<grid, 256, 0, st>>>(A, Aq, a_scale, M, K);
+    else if (nch <= 4)
+      fp8_quant_row_wave_kernel<4><<<grid, 256, 0, st>>>(A, Aq, a_scale, M, K);
+    else if (nch <= 8)
+      fp8_quant_row_wave_kernel<8><<<grid, 256, 0, st>>>(A, Aq, a_scale, M, K);
+    else
+      fp8_quant_row_wave_kernel<16><<<grid, 256, 0, st>>>(A, Aq, a_scale, M, K);
   } else {
     fp8_quant_row_kernel<<<M, 256, 0, st>>>(A, Aq, a_scale, K);
   }

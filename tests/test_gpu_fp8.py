@@ -55,8 +55,13 @@ def _quant_same(A_bits, block, what):
 
 
 @pytest.mark.parametrize("block", [0, 128])
-@pytest.mark.parametrize("M,K", [(1, 128), (3, 4096), (7, 384), (64, 1024), (333, 256)])
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 4096), (7, 384), (64, 1024), (333, 256), (5, 1000), (6, 8192),
+                                 (3, 8200), (2, 12288)])
 def test_quantize_bit_exact(block, M, K):
+    """Per token: one wave per row with the row in registers (K <= 8192, full
+    and partial last pieces), one workgroup per row beyond; per block of 128."""
+    if block == 128 and K % 128:
+        pytest.skip("blocks of 128 need K % 128 == 0")
     rng = np.random.Generator(np.random.PCG64(1200 + M + K + block))
     a, _ = wl.make_activations(rng, M, K, 128, "f32", outlier_frac=0.01)
     _quant_same(wl.f32_to_bf16_bits(a), block, f"M={M} K={K} block={block}")

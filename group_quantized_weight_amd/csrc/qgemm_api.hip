@@ -161,9 +161,12 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   base = (long long)p.tiles_x * p.tiles_y;  // workgroups without a K-split
 
   // K-split: only when the tiles alone leave compute units idle; then aim at
-  // two workgroups per compute unit (one for the small-M MFMA path, whose
-  // partials grow with M: measured best on MI355X).
-  const long long target = path == QG_PATH_SMALL ? cus : 2LL * cus;
+  // two workgroups per compute unit for the GEMV, one for the MFMA paths
+  // (the tiled GEMM's LDS ring fits one workgroup per compute unit, and the
+  // small-M path's partials grow with M). Measured on MI355X, K = N = 4096:
+  // M = 256 26.1 us at nsplit 4 vs 31.4 us at 8; M = 512 31.2 us at 2 vs
+  // 38.7 us at 4.
+  const long long target = path == QG_PATH_GEMV ? 2LL * cus : cus;
   int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((target + base - 1) / base));
   ns = balance(p.units, ns);
   if (path == QG_PATH_GEMV)

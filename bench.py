@@ -301,6 +301,35 @@ def run_moe(name, steps, warmup, mode, block=None):
     return res
 
 
+def stream_read_context(steps=20, warmup=5):
+    """Context only, not the product: a plain streaming read over rotated
+    buffers of the decode weight size (torch's float32 sum of bf16 data), as
+    "achievable HBM" next to the GEMV; and the shader clock rocm-smi reports
+    afterwards (best effort)."""
+    import subprocess
+    import torch
+    n = 12 * 58720256 // 2            # 704 MB: one launch per step, larger than the 256 MiB Infinity Cache
+    buf = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    ms = time_steps(lambda i: torch.sum(buf, dtype=torch.float32), steps, warmup, "eager")
+    res = {"read_bytes": 2 * n, "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+           "how": "torch.sum of one 704 MB bf16 buffer (float32 accumulation): a library reduction, "
+                  "not a bandwidth ceiling"}
+    # the HIP runtime's device-to-device copy kernel, 256 MiB each way
+    src = buf[: (256 << 20) // 2]
+    dst = torch.empty_like(src)
+    ms = time_steps(lambda i: dst.copy_(src), steps, warmup, "eager")
+    res["copy_read_plus_write_gbs"] = round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+        res["sclk"] = [l.strip() for l in out.splitlines() if "sclk" in l.lower()][:2]
+    except Exception as e:  # rocm-smi missing or refused on this host
+        res["sclk"] = f"unavailable ({type(e).__name__})"
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(p, seconds=10.0):
     import numpy as np
     import oracle
@@ -313,9 +342,17 @@ def cpu_baseline(p, seconds=10.0):
         if el >= seconds:
             break
     per = el / passes
-    return dict(value=algorithmic_bytes(p) / per / 1e9, unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+    cores = oracle.num_threads()
+    # the same oracle on one core: one pass
+    prev = oracle.set_threads(1)
+    t1 = time.perf_counter()
+    oracle.for_problem(p)
+    one = time.perf_counter() - t1
+    oracle.set_threads(prev)
+    return dict(value=algorithmic_bytes(p) / per / 1e9, unit="GB/s", cores=cores, kind="oracle",
                 sample=f"the whole {p.name} problem (M={p.M}, K={p.K}, N={p.N}), {passes} passes in {el:.1f} s; "
-                       f"{per * 1e3:.1f} ms per pass")
+                       f"{per * 1e3:.1f} ms per pass",
+                value_1core=algorithmic_bytes(p) / one / 1e9, ms_per_pass_1core=round(one * 1e3, 1))
 
 
 def main():
@@ -432,6 +469,10 @@ def bench(args):
             log(f"bench: {name}: gemm {r['gemm_us']} us ({r['gemm_tflops']} TFLOP/s), with quantization "
                 f"{r['step_us']} us, torch._scaled_mm {r['scaled_mm_us']}")
 
+    context = stream_read_context()
+    log(f"bench: torch.sum read {context['gbs']} GB/s, runtime copy {context['copy_read_plus_write_gbs']} GB/s "
+        f"(read + write); {context['sclk']}")
+
     moe = []
     if not args.no_moe:
         for name in ("moe_e8_top2_t1", "moe_e8_top2_t16", "moe_e64_top6_t16", "moe_e64_top6_t64"):
@@ -470,6 +511,7 @@ def bench(args):
         "crossover": sweep,
         "fp8_w8a8": fp8,
         "moe_grouped_gemv": moe,
+        "hbm_context": context,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

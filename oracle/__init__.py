@@ -47,6 +47,7 @@ def load(path: str = _LIB):
     lib.oracle_qgemm.argtypes = [c_int] * 8 + [vp] * 5 + [i64p, c_int, i64p, c_int, vp, vp]
     lib.oracle_int_partials.argtypes = [c_int] * 6 + [vp, vp, vp, i64p, c_int, i64p, c_int, vp]
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_threads.argtypes = [c_int]
     lib.oracle_quantize_act.argtypes = [c_int, c_int, c_int, vp, vp, vp]
     lib.oracle_fp8_value.argtypes = [c_int]
     lib.oracle_fp8_value.restype = ctypes.c_double
@@ -249,6 +250,11 @@ def fp8_gemm(M, N, K, scaling, Aq, a_scale, Wq, w_scale, rows=None, cols=None, l
     if rc != 0:
         raise ValueError(f"oracle_fp8_gemm rejected its arguments (rc={rc})")
     return ref, bound
+
+
+def set_threads(n: int, lib=None) -> int:
+    """Use n OpenMP threads from now on; returns the previous count."""
+    return int((lib or load()).oracle_set_threads(int(n)))
 
 
 def num_threads(lib=None) -> int:

@@ -441,6 +441,21 @@ int oracle_fp8_gemm(int M, int N, int K, int scaling, const uint8_t *Aq, const f
     return 0;
 }
 
+/* Threads the OpenMP loops use from now on (n >= 1); returns the previous
+ * count. The per-element summation order does not depend on it. */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    const int prev = omp_get_max_threads();
+    if (n >= 1)
+        omp_set_num_threads(n);
+    return prev;
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -192,9 +192,10 @@ def moe_default_block(T: int, topk: int, E: int, G: int, N: int) -> int:
     return int(lib().qgemm_moe_default_block(T, topk, E, G, N))
 
 
-def moe_align(topk_ids, E: int, block: int, stream=None):
+def moe_align(topk_ids, E: int, block: int, stream=None, out=None):
     """(sorted_ids, tile_experts, num_post_pad) int32 device tensors for the
-    grouped GEMV (see include/qgemm.h); topk_ids: int32 [T, topk] or flat."""
+    grouped GEMV (see include/qgemm.h); topk_ids: int32 [T, topk] or flat.
+    out: a previous result of the same shape to write in place."""
     import torch
     ids = topk_ids.reshape(-1)
     numel = ids.numel()
@@ -202,9 +203,12 @@ def moe_align(topk_ids, E: int, block: int, stream=None):
     if mt == 0:
         raise QGemmError(EUNSUPPORTED, "qgemm_moe_max_tiles")
     dev = topk_ids.device
-    sorted_ids = torch.empty(mt * block, dtype=torch.int32, device=dev)
-    tile_experts = torch.empty(mt, dtype=torch.int32, device=dev)
-    npp = torch.empty(4, dtype=torch.int32, device=dev)
+    if out is not None:
+        sorted_ids, tile_experts, npp = out
+    else:
+        sorted_ids = torch.empty(mt * block, dtype=torch.int32, device=dev)
+        tile_experts = torch.empty(mt, dtype=torch.int32, device=dev)
+        npp = torch.empty(4, dtype=torch.int32, device=dev)
     st = lib().qgemm_moe_align(_ptr(ids), numel, E, block, _ptr(sorted_ids), _ptr(tile_experts), _ptr(npp),
                                stream if stream is not None else _stream(dev))
     if st != OK:
@@ -233,13 +237,17 @@ def moe_run(A, w_packed, scales, routing, *, topk: int, N: int, G: int, E: int, 
     return out
 
 
-def fp8_quantize(A, block: int = FP8_PER_TOKEN, stream=None):
+def fp8_quantize(A, block: int = FP8_PER_TOKEN, stream=None, Aq=None, a_scales=None):
     """(codes uint8 [M, K], scales float32 [M] or [M, K/128]): dynamic E4M3
-    quantization of bf16 activations A [M, K] (see include/qgemm.h)."""
+    quantization of bf16 activations A [M, K] (see include/qgemm.h); Aq and
+    a_scales, when given, are written in place."""
     import torch
     M, K = A.shape
-    Aq = torch.empty((M, K), dtype=torch.uint8, device=A.device)
-    sc = torch.empty((M,) if block == FP8_PER_TOKEN else (M, K // 128), dtype=torch.float32, device=A.device)
+    if Aq is None:
+        Aq = torch.empty((M, K), dtype=torch.uint8, device=A.device)
+    sc = a_scales
+    if sc is None:
+        sc = torch.empty((M,) if block == FP8_PER_TOKEN else (M, K // 128), dtype=torch.float32, device=A.device)
     st = lib().qgemm_fp8_quantize(_ptr(A), M, K, block, _ptr(Aq), _ptr(sc),
                                   stream if stream is not None else _stream(A.device))
     if st != OK:

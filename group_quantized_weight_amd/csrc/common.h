@@ -20,8 +20,8 @@ constexpr int kTileCols = 64;                // packed layout: columns per tile
 
 // GEMV path: one workgroup = 4 waves over one 64-column tile; lane l owns the
 // 4 adjacent columns 4 (l % 16) .. +3 of the tile and every 4th word-row
-// (l / 16) of its wave's K range. (Eight waves per workgroup measured slower:
-// fewer workgroups fit per compute unit.)
+// (l / 16) of its wave's K range. (Eight or sixteen waves per workgroup
+// measured slower on MI355X, for single-row decode and the other shapes.)
 __host__ __device__ constexpr int gemv_waves(int) { return 4; }
 
 // GEMM path: one workgroup = 4 waves (each 128 x 32), tile 128 x 128, K

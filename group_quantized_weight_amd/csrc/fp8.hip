@@ -20,6 +20,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_v;
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 typedef __attribute__((ext_vector_type(2))) float f32x2_v;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_v;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBufWord3 = 0x00020000;   // raw buffer: 32-bit data, no swizzle
@@ -173,6 +174,12 @@ hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int 
 // 8 consecutive rows hit 8 different bank groups. A lane's fragment is 32
 // consecutive bytes of k (k = 32 (lane / 16) .. +31) of row lane % 16, the
 // same k for both operands, so the instruction's sum runs over all 128 k.
+// The weight fragment is the instruction's first operand and the activation
+// fragment its second, so each tile is computed transposed: a lane holds 4
+// adjacent output columns of one row, which the epilogue scales (one
+// activation scale per row) and writes with one 8-byte store (the other
+// order, 4 rows of one column per lane, took 3 us more at M = 1024, K = N =
+// 4096: 64 scale loads and 64 two-byte stores per lane).
 // ---------------------------------------------------------------------------
 constexpr int kF8Tile = 128;
 constexpr int kF8Row = 128;                       // bytes per operand row per K step
@@ -247,61 +254,123 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
 
-  copy_step(0, 0, 0);
-  if constexpr (STAGES == 3) copy_step(1, 1, nsteps > 1 ? 0 : kDead);
-  for (int i = 0; i < nsteps; ++i) {
-    // this step's copies are done when at most the next step's remain in flight
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
-    // every wave is past step i - 1: its stage takes step i + STAGES - 1
-    const int nx = i + STAGES - 1;
-    copy_step(nx, nx % STAGES, nx < nsteps ? 0 : kDead);
-    const unsigned char *sb = s_ring + (i % STAGES) * kF8Stage;
-    i32x8_v af[4], bfr[4];
+  if constexpr (!BLOCKWISE) {
+    // Per token: the fragments of step i + 1 are read from LDS while the
+    // MFMAs of step i run, alternating one MFMA and one LDS read (two
+    // register sets, so no copies between them). This needs step i + 1 in
+    // LDS at the top of step i, so the ring takes step i + STAGES into the
+    // stage step i used (read into registers during step i - 1). Measured
+    // 2-17% faster than reading each step's fragments at its own top
+    // (M = 16..4096, K = N = 4096); the blockwise loop, whose MFMA results
+    // also feed float32 promotions, measured 4-7% slower this way and keeps
+    // the simpler order below.
+    struct Frags {
+      i32x8_v a[4], b[4];
+    };
+    auto read_step = [&](int step, Frags &F) {
+      const unsigned char *sb = s_ring + (step % STAGES) * kF8Stage;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      af[f] = frag(sb, 64 * wr + 16 * f + li);
-      bfr[f] = frag(sb + kF8OpBytes, 64 * wc + 16 * f + li);
-    }
-    if constexpr (BLOCKWISE) {
-      const float sb_w = w_scale[(size_t)(n0 / 128) * nsteps + i];   // one per workgroup tile and block
-      const float *sa = (const float *)(sb + 2 * kF8OpBytes);
-#pragma unroll
-      for (int fm = 0; fm < 4; ++fm) {
-        const f32x4_v s4 = *(const f32x4_v *)(sa + 64 * wr + 16 * fm + 4 * lk) * sb_w;
-#pragma unroll
-        for (int fn = 0; fn < 4; ++fn) {
-          const f32x4_v p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[fm], bfr[fn], (f32x4_v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(s4[r], p[r], acc[fm][fn][r]);
-        }
+      for (int f = 0; f < 4; ++f) {
+        F.a[f] = frag(sb, 64 * wr + 16 * f + li);
+        F.b[f] = frag(sb + kF8OpBytes, 64 * wc + 16 * f + li);
       }
-    } else {
+    };
+    auto step = [&](int i, const Frags &C, Frags &Nx) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(8 * (STAGES - 2)) : "memory");
+      const int nx = i + STAGES;
+      copy_step(nx, i % STAGES, nx < nsteps ? 0 : kDead);
+      read_step(i + 1, Nx);
 #pragma unroll
       for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0, 127,
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(C.b[fn], C.a[fm], acc[fm][fn], 0, 0, 0, 127,
                                                                          0, 127);
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < STAGES; ++p) copy_step(p, p, nsteps > p ? 0 : kDead);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (STAGES - 1)) : "memory");
+    Frags f0, f1;
+    read_step(0, f0);
+    for (int i = 0; i < nsteps; i += 2) {
+      step(i, f0, f1);
+      if (i + 1 < nsteps) step(i + 1, f1, f0);
+    }
+  } else {
+    copy_step(0, 0, 0);
+    if constexpr (STAGES == 3) copy_step(1, 1, nsteps > 1 ? 0 : kDead);
+    for (int i = 0; i < nsteps; ++i) {
+      // this step's copies are done when at most the next step's remain in flight
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
+      // every wave is past step i - 1: its stage takes step i + STAGES - 1
+      const int nx = i + STAGES - 1;
+      copy_step(nx, nx % STAGES, nx < nsteps ? 0 : kDead);
+      const unsigned char *sb = s_ring + (i % STAGES) * kF8Stage;
+      i32x8_v af[4], bfr[4];
+  #pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        af[f] = frag(sb, 64 * wr + 16 * f + li);
+        bfr[f] = frag(sb + kF8OpBytes, 64 * wc + 16 * f + li);
+      }
+      if constexpr (BLOCKWISE) {
+        const float sb_w = w_scale[(size_t)(n0 / 128) * nsteps + i];   // one per workgroup tile and block
+        const float *sa = (const float *)(sb + 2 * kF8OpBytes);
+  #pragma unroll
+        for (int fm = 0; fm < 4; ++fm) {
+          const float s1 = sa[64 * wr + 16 * fm + li] * sb_w;
+  #pragma unroll
+          for (int fn = 0; fn < 4; ++fn) {
+            const f32x4_v p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bfr[fn], af[fm], (f32x4_v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(s1, p[r], acc[fm][fn][r]);
+          }
+        }
+      } else {
+  #pragma unroll
+        for (int fm = 0; fm < 4; ++fm)
+  #pragma unroll
+          for (int fn = 0; fn < 4; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0, 127,
+                                                                           0, 127);
+      }
     }
   }
 
-  // ---- epilogue: tile (fm, fn) element r is row 16 fm + 4 lk + r, column 16 fn + li ----
+  // ---- epilogue: tile (fm, fn) element r is row 16 fm + li, column 16 fn + 4 lk + r ----
 #pragma unroll
-  for (int fn = 0; fn < 4; ++fn) {
-    const int n = n0 + 64 * wc + 16 * fn + li;
-    if (n >= N) continue;
-    const float ws = BLOCKWISE ? 1.f : w_scale[n];
+  for (int fm = 0; fm < 4; ++fm) {
+    const int m = m0 + 64 * wr + 16 * fm + li;
+    if (m >= M) continue;
+    const float as = BLOCKWISE ? 1.f : a_scale[m];
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
+    for (int fn = 0; fn < 4; ++fn) {
+      const int n = n0 + 64 * wc + 16 * fn + 4 * lk;
+      if (n >= N) continue;
+      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 64 * wr + 16 * fm + 4 * lk + r;
-        if (m >= M) continue;
-        const float v = BLOCKWISE ? acc[fm][fn][r] : a_scale[m] * (ws * acc[fm][fn][r]);
-        const f32x2_v two = {v, 0.f};
-        out[(size_t)m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_v)) & 0xFFFFu);
+      for (int r = 0; r < 4; ++r)
+        v[r] = BLOCKWISE ? acc[fm][fn][r] : as * ((n + r < N ? w_scale[n + r] : 0.f) * acc[fm][fn][r]);
+      const f32x2_v lo = {v[0], v[1]}, hi = {v[2], v[3]};
+      const uint32_t b01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_v));
+      const uint32_t b23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_v));
+      uint16_t *o = out + (size_t)m * N + n;
+      if (n + 4 <= N && ((((size_t)m * N + n) & 3) == 0)) {   // 8-byte aligned: one store
+        *(u32x2_v *)o = (u32x2_v){b01, b23};
+      } else {   // the ragged end of a row, or N % 4 != 0
+        const uint16_t e[4] = {(uint16_t)(b01 & 0xFFFFu), (uint16_t)(b01 >> 16), (uint16_t)(b23 & 0xFFFFu),
+                               (uint16_t)(b23 >> 16)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) o[r] = e[r];
       }
+    }
   }
 }
 

@@ -60,6 +60,7 @@ struct GemmArgs {
   float *asum;             // [K/128][Mp] activation sums per group, x -136 without zero-points (workspace)
   int M, N, K, G, Np, Mp;  // Mp = M rounded up to kGemmBM
   int nchunks, nsplit;     // K / kGemmKC chunks split into nsplit slices
+  int stages;              // LDS ring depth: 3, or 2 with at least two tiles per compute unit
 };
 
 struct SmallArgs {

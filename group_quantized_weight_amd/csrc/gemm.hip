@@ -12,9 +12,13 @@
 //     MFMAs);
 //   - the chunk's activation tile, scales, zero-points and activation sums
 //     are copied by buffer loads straight into LDS (no registers on the way),
-//     into a ring of 3 stages (one chunk in use, two in flight). Each wave
-//     waits for its own copies, then a barrier makes every wave's copies
-//     visible;
+//     into a ring of ST stages: 3 (one chunk in use, two in flight; 103 KiB,
+//     one workgroup per compute unit) when the grid is about one workgroup
+//     per compute unit, 2 (one in flight; 69 KiB, so two workgroups share a
+//     compute unit and cover each other's waits) when there are at least two
+//     tiles per compute unit (measured on MI355X, K = N = 4096: M = 4096 151
+//     -> 136 us, M = 2048 77 -> 70 us). Each wave waits for its own copies,
+//     then a barrier makes every wave's copies visible;
 //   - the activation tile's 16-byte pieces are XOR-swizzled with the row
 //     index, so the MFMA fragment reads of 16 rows hit 16 different 4-bank
 //     groups; rows past M read zeros through the buffer's range check (their
@@ -54,7 +58,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 // [zero-points 16 x 4 B]. Each small slot is as large as one wave-wide copy
 // writes (lanes past the useful part copy neighbouring data into the slot's
 // tail, never read). The packed weights go straight to registers.
-constexpr int kStages = 3;                           // 1 chunk in use, 2 in flight
 constexpr int kARow = kGemmKC * 2;                   // 256 B per activation row
 constexpr int kAOff = 0;
 constexpr int kSOff = kAOff + kGemmBM * kARow;       // 32 KiB
@@ -106,9 +109,9 @@ __device__ __forceinline__ T lds_read(const unsigned char *base, int off) {
 // 4 waves, one per SIMD: wave w owns all 128 rows and the 32 columns
 // n0 + 32 w .. +31 of the tile (8 x 2 MFMA tiles), so a weight fragment is
 // dequantized once and feeds 8 MFMAs.
-template <int OF, bool ZP>
+template <int OF, bool ZP, int ST>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) unsigned char s_ring[kStages * kStageBytes];
+  __shared__ __align__(16) unsigned char s_ring[ST * kStageBytes];
   constexpr int FM = 8, FN = 2;
 
   const int t = threadIdx.x;
@@ -201,16 +204,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   float sc[FN] = {0.f, 0.f};   // scales of the chunk whose sums are in P
   u32x2_t bcur[4], bnext[4];
 
-  // Chunk i (local) lives in stage i % 3. While chunk i is computed, its
+  // Chunk i (local) lives in stage i % ST. While chunk i is computed, its
   // MFMA sequence also issues, one piece per activation fragment, the
   // weight loads of chunk i + 1 (first, into registers) and then the copies
-  // of chunk i + 2 into the stage chunk i - 1 used: every wave has passed
-  // the barrier at the top of chunk i, so every wave is done with it.
+  // of chunk i + ST - 1 into the stage chunk i - 1 used: every wave has
+  // passed the barrier at the top of chunk i, so every wave is done with it.
   // Spreading the loads keeps the compute unit's address unit from stalling
-  // every wave with one burst. At the top of chunk i, at most the 9 copies
-  // of chunk i + 1 may still be in flight (they were issued after the weight
-  // loads of chunk i), so vmcnt(8) covers chunk i's copies and weights on
-  // every wave (waves 0..2 also wait for their small copy, issued early).
+  // every wave with one burst. With 3 stages, at the top of chunk i at most
+  // the 9 copies of chunk i + 1 may still be in flight (they were issued
+  // after the weight loads of chunk i), so vmcnt(8) covers chunk i's copies
+  // and weights on every wave (waves 0..2 also wait for their small copy,
+  // issued early); with 2 stages nothing may be (vmcnt(0)).
   //
   // One chunk on the MFMA units is software-pipelined with the promotion of
   // the previous chunk: tile (fm, fn) of P is first added into acc with the
@@ -218,9 +222,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
   // chunk's first k-step. (Without zero-points the pre-pass already stores
   // -136 * sum(a).)
   auto run_chunk = [&](int i) {
-    const unsigned char *sb = s_ring + (i % kStages) * kStageBytes;
-    const int db = i + 1 < ccount ? 0 : kDead, dc = i + 2 < ccount ? 0 : kDead;
-    const int cs = (i + 2) % kStages;
+    const unsigned char *sb = s_ring + (i % ST) * kStageBytes;
+    constexpr int AH = ST - 1;   // copies run AH chunks ahead
+    const int db = i + 1 < ccount ? 0 : kDead, dc = i + AH < ccount ? 0 : kDead;
+    const int cs = (i + AH) % ST;
     const uint32_t sv = lds_read<uint32_t>(sb, s_off);
     float bias[FN] = {1.f, 1.f};
     if constexpr (ZP) {
@@ -246,9 +251,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
       if (q < 4)
         bnext[q] = load_b(cb + i + 1, q, db);
       else if (q == 4)
-        copy_small(cb + i + 2, cs, dc);
+        copy_small(cb + i + AH, cs, dc);
       else if (q >= 6 && (q - 6) % 3 == 0 && (q - 6) / 3 < 8)
-        copy_a(cb + i + 2, cs, (q - 6) / 3, dc);
+        copy_a(cb + i + AH, cs, (q - 6) / 3, dc);
       if (fm == 0) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) bfr[fn] = dequant_word(bcur[s][fn], magic);
@@ -282,12 +287,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     for (int j = 0; j < 8; ++j) copy_a(cb, 0, j, d0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) bcur[s] = load_b(cb, s, d0);
-    copy_small(cb + 1, 1, d1);
+    if constexpr (ST == 3) {
+      copy_small(cb + 1, 1, d1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) copy_a(cb + 1, 1, j, d1);
+      for (int j = 0; j < 8; ++j) copy_a(cb + 1, 1, j, d1);
+    }
   }
   for (int i = 0; i < ccount; ++i) {
-    wait_then_barrier<8>();
+    wait_then_barrier<ST == 3 ? 8 : 0>();
     run_chunk(i);
   }
 #pragma unroll
@@ -375,7 +382,10 @@ __global__ __launch_bounds__(256) void asum_kernel(const uint16_t *__restrict__ 
 
 template <int OF, bool ZP>
 static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
-  gemm_kernel<OF, ZP><<<grid, kGemmThreads, 0, st>>>(a);
+  if (a.stages == 2)
+    gemm_kernel<OF, ZP, 2><<<grid, kGemmThreads, 0, st>>>(a);
+  else
+    gemm_kernel<OF, ZP, 3><<<grid, kGemmThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

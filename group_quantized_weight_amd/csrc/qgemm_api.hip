@@ -95,6 +95,7 @@ struct Plan {
   size_t codes = 0;       //   by a pre-pass into the workspace: bytes of int8 codes,
   size_t ascale = 0;      //   then of their float32 scales, at its start
   size_t asum = 0;        // MFMA path: bytes of activation sums (after the above)
+  int stages = 3;         // MFMA path: LDS ring depth
   size_t ws = 0;
 };
 
@@ -162,8 +163,8 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
 
   // K-split: only when the tiles alone leave compute units idle; then aim at
   // two workgroups per compute unit for the GEMV, one for the MFMA paths
-  // (the tiled GEMM's LDS ring fits one workgroup per compute unit, and the
-  // small-M path's partials grow with M). Measured on MI355X, K = N = 4096:
+  // (the tiled GEMM's 3-stage LDS ring fits one workgroup per compute unit,
+  // and the small-M path's partials grow with M). Measured on MI355X, K = N = 4096:
   // M = 256 26.1 us at nsplit 4 vs 31.4 us at 8; M = 512 31.2 us at 2 vs
   // 38.7 us at 4.
   const long long target = path == QG_PATH_GEMV ? 2LL * cus : cus;
@@ -182,6 +183,9 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
     p.lds = gemv_lds(f, p.mb, G, p.units, ns);
   }
   p.nsplit = ns;
+  // the tiled GEMM's ring: 2 stages, so that two workgroups share a compute
+  // unit, once there are at least two workgroups per compute unit
+  p.stages = base * ns >= 2LL * cus ? 2 : 3;
   p.asum = path == QG_PATH_GEMM ? gemm_asum_bytes(M, K) : 0;
   if (f.dq) {
     // Each workgroup quantizes the rows and groups it stages; that repeats
@@ -337,6 +341,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np; a.Mp = (int)padded_rows(M);
     a.nchunks = K / kGemmKC;
     a.nsplit = p.nsplit;
+    a.stages = p.stages;
     e = launch_gemm(f.o, has_zp != 0, group, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), s);
   }
   if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, partial, out, M, N, Np, p.nsplit, s);

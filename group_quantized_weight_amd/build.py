@@ -52,7 +52,10 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda so: _compile(*so), zip(SOURCES, objs)))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    # -Bsymbolic: the library's calls into its own functions bind inside it,
+    # so another library in the process that exports the same names (another
+    # build of this one, say) cannot take them over
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -25,6 +25,31 @@ def test_library_exports_header_symbols():
         assert hasattr(lib, name), name
 
 
+def test_library_binds_its_own_symbols():
+    """The library is linked -Bsymbolic (DT_FLAGS has DF_SYMBOLIC, 0x2): its
+    calls into its own functions do not resolve to another library in the
+    process that exports the same names."""
+    import struct
+    with open(qg.LIB_PATH, "rb") as f:
+        data = f.read()
+    assert data[:4] == b"\x7fELF" and data[4] == 2 and data[5] == 1, "64-bit little-endian ELF expected"
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum = struct.unpack_from("<HH", data, 0x3A)
+    flags = None
+    for i in range(shnum):
+        sh = shoff + i * shentsize
+        sh_type, = struct.unpack_from("<I", data, sh + 4)
+        if sh_type != 6:   # SHT_DYNAMIC
+            continue
+        off, size = struct.unpack_from("<QQ", data, sh + 0x18)   # sh_offset, sh_size
+        entsize, = struct.unpack_from("<Q", data, sh + 0x38)      # sh_entsize
+        for j in range(size // entsize):
+            tag, val = struct.unpack_from("<qQ", data, off + j * entsize)
+            if tag in (16, 30):   # DT_SYMBOLIC, or DT_FLAGS
+                flags = (flags or 0) | (0x2 if tag == 16 else val)
+    assert flags is not None and flags & 0x2, "libqgemm.so is not linked -Bsymbolic"
+
+
 def test_layout_and_sizes():
     assert qg.layout_version() == 2
     assert qg.packed_bytes(4096, 28672, qg.W4_A_BF16) == 4096 // 8 * 28672 * 4

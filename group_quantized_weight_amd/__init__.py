@@ -52,6 +52,12 @@ def lib():
         if _lib is None:
             if not os.path.exists(LIB_PATH):
                 raise ImportError(f"{LIB_PATH} is not built: run `python -m group_quantized_weight_amd.build`")
+            # torch first: it ships its own HIP runtime (soname libamdhip64.so.7),
+            # and the library must resolve to that same runtime, so that torch's
+            # streams and memory are valid in its calls. Loaded before torch, the
+            # library would pull in the system copy and the process would then
+            # hold two runtimes.
+            import torch  # noqa: F401
             L = ctypes.CDLL(LIB_PATH)
             c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
             L.qgemm_layout_version.restype = c_int

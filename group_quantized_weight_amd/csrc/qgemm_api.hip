@@ -76,6 +76,13 @@ int device_cus() {
   return cus;
 }
 
+// hipGetLastError reports the last error of any runtime call on this thread,
+// and it stays pending until read. Each entry point reads and drops such an
+// error, left by some earlier call that is not ours, right before its first
+// launch, so that the check after its own launches sees only their errors.
+// A fault of the device persists and is still reported.
+void drop_pending_error() { (void)hipGetLastError(); }
+
 size_t padded_cols(int N) { return ((size_t)N + kColAlign - 1) / kColAlign * kColAlign; }
 
 constexpr size_t kPartialCap = 256ull << 20;  // bytes of float32 partials at most
@@ -243,6 +250,7 @@ int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, 
   if (f.w == W4 ? K % 8 : K % 4) return QG_EINVAL;
   if ((f.w == W4 ? K / 8 : K / 4) > 65535 || padded_cols(N) > (size_t)INT_MAX) return QG_EUNSUPPORTED;
   if (!aligned16(w_canonical) || !aligned16(w_packed)) return QG_EALIGN;
+  drop_pending_error();
   const hipError_t e = launch_pack(f.w, w_canonical, (uint32_t *)w_packed, K, N, (int)padded_cols(N),
                                    (hipStream_t)stream);
   return e == hipSuccess ? QG_OK : QG_EHIP;
@@ -294,6 +302,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
   char *ws = (char *)workspace;
   float *partial = p.nsplit > 1 ? (float *)(ws + p.codes + p.ascale + p.asum) : nullptr;
   const int Np = (int)padded_cols(N);
+  drop_pending_error();
   hipError_t e = hipSuccess;
   if (f.dq && !p.dq_fused) {
     // the product then reads the codes and scales this writes
@@ -364,6 +373,7 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
   if (M == 0) return QG_OK;
   if (!A || !Aq || !a_scales) return QG_EINVAL;
   if (!aligned16(A) || !aligned16(Aq) || !aligned16(a_scales)) return QG_EALIGN;
+  drop_pending_error();
   const hipError_t e = launch_quant((const float *)A, (int8_t *)Aq, (float *)a_scales, M, K, group,
                                     (hipStream_t)stream);
   return e == hipSuccess ? QG_OK : QG_EHIP;
@@ -388,6 +398,7 @@ int qgemm_moe_align(const int *topk_ids, int numel, int E, int block, int *sorte
   if ((numel > 0 && !aligned16(topk_ids)) || !aligned16(sorted_ids) || !aligned16(tile_experts) ||
       !aligned16(num_post_pad))
     return QG_EALIGN;
+  drop_pending_error();
   const hipError_t e = launch_moe_align(topk_ids, numel, E, block, max_tiles, sorted_ids, tile_experts,
                                         num_post_pad, (hipStream_t)stream);
   return e == hipSuccess ? QG_OK : QG_EHIP;
@@ -486,6 +497,7 @@ int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp
   hipStream_t s = (hipStream_t)stream;
   float *partial = p.nsplit > 1 ? (float *)workspace : nullptr;
   const int Np = (int)padded_cols(N);
+  drop_pending_error();
   hipError_t e;
   if (p.path == QG_PATH_SMALL) {
     SmallArgs a = {};
@@ -539,6 +551,7 @@ int qgemm_fp8_quantize(const void *A, int M, int K, int block, void *Aq, void *a
   if (M == 0) return QG_OK;
   if (!A || !Aq || !a_scales) return QG_EINVAL;
   if (!aligned16(A) || !aligned16(Aq) || !aligned16(a_scales)) return QG_EALIGN;
+  drop_pending_error();
   const hipError_t e = launch_fp8_quant((const uint16_t *)A, (uint8_t *)Aq, (float *)a_scales, M, K, block,
                                         (hipStream_t)stream);
   return e == hipSuccess ? QG_OK : QG_EHIP;
@@ -557,6 +570,7 @@ int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void 
   if (!Aq || !a_scales || !Wq || !w_scales || !out) return QG_EINVAL;
   if (!aligned16(Aq) || !aligned16(a_scales) || !aligned16(Wq) || !aligned16(w_scales) || !aligned16(out))
     return QG_EALIGN;
+  drop_pending_error();
   const hipError_t e = launch_fp8_gemm(scaling, (const uint8_t *)Aq, (const float *)a_scales, (const uint8_t *)Wq,
                                        (const float *)w_scales, (uint16_t *)out, M, N, K, device_cus(),
                                        (hipStream_t)stream);

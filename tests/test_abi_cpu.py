@@ -50,6 +50,25 @@ def test_library_binds_its_own_symbols():
     assert flags is not None and flags & 0x2, "libqgemm.so is not linked -Bsymbolic"
 
 
+def test_library_shares_torchs_hip_runtime():
+    """Loaded before anything imported torch, the library still resolves to
+    the HIP runtime torch ships (one runtime in the process), so torch's
+    streams and memory are valid in its calls. Checked in a fresh
+    interpreter from the mapped files."""
+    import os
+    import subprocess
+    import sys
+    code = ("import os, group_quantized_weight_amd as qg; qg.lib(); "
+            "print(sorted({l.split()[-1] for l in open('/proc/%d/maps' % os.getpid()) if 'amdhip' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300,
+                       env=dict(os.environ, PYTHONPATH=root))
+    assert r.returncode == 0, r.stderr[-2000:]
+    import ast
+    mapped = ast.literal_eval(r.stdout.strip().splitlines()[-1])
+    assert len(mapped) == 1 and "torch" in mapped[0], mapped
+
+
 def test_layout_and_sizes():
     assert qg.layout_version() == 2
     assert qg.packed_bytes(4096, 28672, qg.W4_A_BF16) == 4096 // 8 * 28672 * 4

@@ -34,7 +34,15 @@
  * no call synchronizes the host or copies between host and device.
  *
  * Errors: arguments are validated before anything is enqueued; on error
- * nothing is launched and nothing is written.
+ * nothing is launched and nothing is written. QG_EHIP reports an error of the
+ * library's own launches only: an error that an earlier runtime call of the
+ * caller's left pending on the thread (the runtime keeps the last one until
+ * it is read) is read and dropped right before the first launch. A fault of
+ * the device persists and is still reported.
+ *
+ * The library and the caller must share one HIP runtime (the one that made
+ * the caller's streams and memory): in a process that also loads PyTorch,
+ * load PyTorch first, since it ships its own runtime under the same name.
  */
 #ifndef QGEMM_H
 #define QGEMM_H

@@ -9,8 +9,9 @@ Cache from serving the weights, consecutive steps cycle through R copies of
 the packed weights and scales whose total exceeds 640 MiB.
 
 Also reported: the MFMA path at M=1024 (TFLOP/s), the prefill crossover
-sweep against a dense bf16 torch.matmul on the same shapes, and the fp64 CPU
-oracle timed on the host cores (cpu_baseline).
+sweep against a dense bf16 torch.matmul on the same shapes and against the
+pages' prefill alternative (dequantize the weights to bf16, then the dense
+GEMM), and the fp64 CPU oracle timed on the host cores (cpu_baseline).
 
 Timing: each measurement first runs its step untimed for about 0.25 s (so
 the timed steps see the clocks the device settles at under that load), then
@@ -185,6 +186,50 @@ def dense_bf16(M, N, K, steps, warmup, mode):
             mode = "eager"
     ms = time_steps(fn, steps, warmup, mode)
     del A, Ws, out
+    torch.cuda.empty_cache()
+    return ms
+
+
+def dequant_dense(name, steps, warmup, mode):
+    """The pages' prefill alternative on the same problem: dequantize the
+    packed int4 weights to bf16 (this library's qgemm_dequantize), then
+    torch.matmul in bf16 (hipBLASLt); one step is both, weights rotated like
+    the fused run. A comparison line only: the library's own path is the
+    fused kernel."""
+    import torch
+    import group_quantized_weight_amd as qg
+    import workloads as wl
+    p = wl.make_config(name)
+    per_copy = qg.packed_bytes(p.K, p.N, p.prec) + (p.K // p.G) * p.N * 2
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / per_copy)))
+    A, _, Ws, Ss, Z = device_problem(p, copies)
+    Wd = torch.empty((p.K, p.N), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+
+    def fn(i):
+        qg.dequantize(Ws[i % copies], Ss[i % copies], p.K, p.N, p.G, zeros=Z, out=Wd)
+        torch.matmul(A, Wd, out=out)
+
+    if mode == "graph":
+        # replay check, as for the dense baseline
+        fn(0)
+        ref = out.clone()
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=torch.cuda.current_stream()):
+            fn(0)
+        ok = True
+        for _ in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            ok &= bool(torch.equal(out, ref))
+        del g
+        if not ok:
+            log("dequantize + dense: graph replay differs from eager; timing eagerly")
+            mode = "eager"
+    ms = time_steps(fn, steps, warmup, mode)
+    del A, Ws, Ss, Z, Wd, out
     torch.cuda.empty_cache()
     return ms
 
@@ -455,11 +500,13 @@ def bench(args):
             st = 200 if M <= 1024 else 100
             r, _ = run_workload(f"prefill_w4a16_m{M}", st, 20, args.mode)
             d_ms = dense_bf16(M, 4096, 4096, st, 20, args.mode)
+            dd_ms = dequant_dense(f"prefill_w4a16_m{M}", st, 20, args.mode)
             sweep.append(dict(M=M, w4_us=r["ms"] * 1e3, bf16_us=d_ms * 1e3, w4_path=r["path"],
                               w4_nsplit=r["nsplit"], w4_tflops=r["tflops"], w4_gbs=r["gbs"],
                               bf16_tflops=2 * M * 4096 * 4096 / (d_ms * 1e-3) / 1e12,
-                              w4_speedup=d_ms / r["ms"]))
-            log(f"bench: sweep M={M}: w4 {r['ms'] * 1e3:.1f} us ({r['path']}), bf16 {d_ms * 1e3:.1f} us")
+                              w4_speedup=d_ms / r["ms"], dequant_dense_us=dd_ms * 1e3))
+            log(f"bench: sweep M={M}: w4 {r['ms'] * 1e3:.1f} us ({r['path']}), bf16 {d_ms * 1e3:.1f} us, "
+                f"dequantize + bf16 {dd_ms * 1e3:.1f} us")
 
     fp8 = []
     if not args.no_fp8:

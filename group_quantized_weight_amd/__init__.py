@@ -92,6 +92,8 @@ def lib():
             L.qgemm_fp8_gemm.argtypes = [c_int] * 4 + [vp] * 6
             L.qgemm_quantize_activations.restype = c_int
             L.qgemm_quantize_activations.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
+            L.qgemm_dequantize.restype = c_int
+            L.qgemm_dequantize.argtypes = [vp, vp, vp] + [c_int] * 5 + [vp, vp]
             L.qgemm_strerror.restype = ctypes.c_char_p
             L.qgemm_strerror.argtypes = [c_int]
             _lib = L
@@ -175,6 +177,21 @@ def workspace(nbytes: int, device):
 def out_dtype(prec: int):
     import torch
     return torch.bfloat16 if _PREC_FMT[prec][3] == "bf16" else torch.float32
+
+
+def dequantize(w_packed, scales, K: int, N: int, G: int, prec: int = W4_A_BF16, zeros=None, out=None,
+               stream=None):
+    """bf16 [K, N] = s * (q - z) rounded once to bf16, from packed int4
+    weights (see include/qgemm.h); out, when given, is written in place."""
+    import torch
+    if out is None:
+        out = torch.empty((K, N), dtype=torch.bfloat16, device=w_packed.device)
+    st = lib().qgemm_dequantize(_ptr(w_packed), _ptr(scales), _ptr(zeros), K, N, G, prec,
+                                int(zeros is not None), _ptr(out),
+                                stream if stream is not None else _stream(w_packed.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_dequantize")
+    return out
 
 
 def quantize_activations(A, G: int, Aq=None, a_scales=None, stream=None):

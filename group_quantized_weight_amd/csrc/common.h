@@ -106,6 +106,9 @@ hipError_t launch_quant(const float *A, int8_t *Aq, float *a_scale, int M, int K
 // scale per row; 128: one per 128 elements) and the GEMM (scaling 0: per
 // token x per channel; 1: per 128 x 128 block).
 hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int M, int K, int block, hipStream_t stream);
+// whole-matrix int4 -> bf16 dequantization (dequant.hip)
+hipError_t launch_dequant_w4(const uint32_t *W, const uint16_t *S, const uint32_t *Z, uint16_t *out, int K, int N,
+                             int G, hipStream_t st);
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
                            const float *w_scale, uint16_t *out, int M, int N, int K, int cus, hipStream_t stream);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.

@@ -379,6 +379,23 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 
+int qgemm_dequantize(const void *w_packed, const void *scales, const void *zeros, int K, int N, int group,
+                     int prec, int has_zp, void *out, void *stream) {
+  if (prec != QG_W4_A_BF16 && prec != QG_W4_A_BF16_OF32) return QG_EUNSUPPORTED;
+  if (group != 32 && group != 128) return QG_EUNSUPPORTED;
+  if (K <= 0 || N <= 0 || K % group != 0) return QG_EINVAL;
+  if (K / 8 > 65535 || padded_cols(N) > (size_t)INT_MAX) return QG_EUNSUPPORTED;
+  if (has_zp && N % 8 != 0) return QG_EUNSUPPORTED;
+  if (!w_packed || !scales || !out || (has_zp && !zeros)) return QG_EINVAL;
+  if (!aligned16(w_packed) || !aligned16(scales) || !aligned16(out) || (has_zp && !aligned16(zeros)))
+    return QG_EALIGN;
+  drop_pending_error();
+  const hipError_t e = launch_dequant_w4((const uint32_t *)w_packed, (const uint16_t *)scales,
+                                         has_zp ? (const uint32_t *)zeros : nullptr, (uint16_t *)out, K, N, group,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
 bool moe_block_ok(int block) {
   return block == 1 || block == 2 || block == 4 || block == 8 || block == 16 || block == 32 || block == 64;
 }

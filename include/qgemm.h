@@ -186,6 +186,25 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
 int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq, void *a_scales,
                                void *stream);
 
+/* Whole-matrix dequantization of packed int4 weights to bf16, for comparing
+ * the fused kernels with dequantization followed by a dense bf16 GEMM (the
+ * prefill alternative of the page "quantization-and-fused-kernels"
+ * (arganzheng.life), sections 三.2 and 三.4):
+ *     out[k][n] = bf16(s[k/G][n] * (q[k][n] - z[k/G][n]))
+ * with z = 8 without zero-points. s * (q - z) is exact in float32, so out is
+ * the correctly rounded (nearest even) bf16 of the exact value.
+ *   w_packed: qgemm_pack's output for K, N and prec (device, read)
+ *   scales:   bf16 [K/G][N]; zeros: [K/G][N/8] packed int4 when has_zp, else
+ *             NULL (device, read)
+ *   out:      bf16 [K][N], row-major (device, written)
+ * prec is QG_W4_A_BF16 or QG_W4_A_BF16_OF32 (int4 weights, bf16 scales);
+ * group in {32, 128}, K % group == 0, K / 8 <= 65535, has_zp requires
+ * N % 8 == 0; pointers 16-byte aligned. One kernel, enqueued on `stream`;
+ * nothing is allocated. Errors as for qgemm_run.
+ */
+int qgemm_dequantize(const void *w_packed, const void *scales, const void *zeros, int K, int N, int group,
+                     int prec, int has_zp, void *out, void *stream);
+
 /*
  * Grouped (MoE) W4A16 GEMV -- grouped GEMM #1 of the fused MoE pipeline on
  * the page "quantization-and-fused-kernels" (arganzheng.life), section 六:

@@ -118,6 +118,28 @@ def dequant(N, K, G, wfmt, sfmt, has_zp, W, S, Z, cols=None, lib=None):
     return out
 
 
+def round_bf16(x):
+    """float64 values that float32 holds exactly -> their bf16 bit patterns
+    (uint16), rounded to nearest with ties to even: the float32 -> bf16
+    conversion of the page "quantization-and-fused-kernels" (arganzheng.life),
+    section 二.3. Written out on the float32 bits: add 0x7FFF plus the lowest
+    kept bit, drop the low 16 bits."""
+    f = np.asarray(x, dtype=np.float64)
+    f32 = f.astype(np.float32)
+    if not np.array_equal(f32.astype(np.float64), f):
+        raise ValueError("round_bf16 takes values that float32 holds exactly")
+    b = f32.view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def dequant_bf16(N, K, G, has_zp, W, S, Z, cols=None, lib=None):
+    """bf16 bit patterns [K, len(cols)] of w_hat = s (q - z) for int4 weights
+    with bf16 scales: the exact value (dequant, in fp64) rounded once to bf16.
+    s (8 significant bits) times an integer of magnitude <= 15 has at most 12
+    significant bits, so float32 holds it exactly."""
+    return round_bf16(dequant(N, K, G, "w4", "bf16", has_zp, W, S, Z, cols=cols, lib=lib))
+
+
 def int_partials(M, N, K, G, wfmt, has_zp, Aq, W, Z, rows=None, cols=None, lib=None):
     """Returns int64 P [len(rows), K/G, len(cols)]: per-group integer dots."""
     lib = lib or load()

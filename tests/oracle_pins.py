@@ -569,6 +569,51 @@ def check_moe_vs_brute(lib, orc=oracle):
         assert np.allclose(ref[i], exact, rtol=1e-12, atol=1e-15), (i, e, t)
 
 
+def check_round_bf16_hand(lib):
+    """Worked cases of round to nearest even into bf16 (8 significant bits):
+    exact values stay, a tie goes to the even neighbour, anything past the
+    tie goes up (by magnitude; signs mirror)."""
+    cases = [(1.0, 0x3F80), (1.0 + 2.0 ** -8, 0x3F80), (1.0 + 3 * 2.0 ** -8, 0x3F82),
+             (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81), (3.0234375, 0x4042), (-3.0234375, 0xC042),
+             (0.0, 0x0000), (-2.5, 0xC020), (255.5, 0x4380), (2.0 ** -126, 0x0080)]
+    x = np.array([c[0] for c in cases])
+    got = oracle.round_bf16(x)
+    assert [int(v) for v in got] == [c[1] for c in cases], [hex(int(v)) for v in got]
+
+
+def check_round_bf16_vs_torch(lib):
+    """Against torch's float32 -> bfloat16 cast (a library routine) on random
+    float32 values over many binades, and on every tie of one binade."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(43))
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))).astype(np.float32)
+    ties = (np.float32(1.0) + (np.arange(128, dtype=np.float32) * 2 + 1) * np.float32(2.0 ** -8)).astype(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_bf16(x.astype(np.float64))
+    bad = np.nonzero(got != t)[0]
+    assert bad.size == 0, (bad[:5], x[bad[:5]], got[bad[:5]], t[bad[:5]])
+
+
+def check_dequant_bf16(lib):
+    """Symmetric int4 with s = 0.5: every w_hat = (q - 8) / 2 is exact in bf16
+    and equals the hand value; with s = 1 + 2^-7 and q - z = 3 the exact
+    3.0234375 is a tie between bf16 neighbours and goes to the even one,
+    3.03125; the rounded values are the rounded exact ones everywhere."""
+    K, N, G = 8, 2, 8
+    W = np.array([[0x76543210, 0xFEDCBA98]], dtype=np.uint32)      # column 0: q = 0..7, column 1: q = 8..15
+    S = _bf16_bits(np.array([[0.5, 0.5]]))
+    got = oracle.dequant_bf16(N, K, G, False, W, S, None, lib=lib)
+    want = _bf16_bits(np.array([[(q - 8) / 2, (q + 8 - 8) / 2] for q in range(8)]))
+    assert np.array_equal(got, want), (got, want)
+    # a tie: z packed = 5 for column 0 (q = 8 -> 3), 8 for column 1 (q = 11 -> 3)
+    W = np.array([[0x88888888, 0xBBBBBBBB]], dtype=np.uint32)
+    S = np.array([[0x3F81, 0x3F81]], dtype=np.uint16)             # 1 + 2^-7
+    Z = np.array([[0x00000085]], dtype=np.uint32)                  # n = 0: 5, n = 1: 8
+    got = oracle.dequant_bf16(N, K, G, True, W, S, Z, lib=lib)
+    assert np.all(got == 0x4042), [hex(int(v)) for v in got.ravel()]
+
+
 def all_checks():
     """(name, callable(lib)) for every pin."""
     out = [(f"hand_{c['id']}", (lambda c: lambda lib: check_hand_case(lib, c))(c)) for c in HAND]
@@ -592,4 +637,6 @@ def all_checks():
             ("fp8_gemm_brute_1", lambda lib: check_fp8_gemm_brute(lib, 1)),
             ("fp8_blockwise_uniform", check_fp8_blockwise_uniform)]
     out += [("moe_align_hand", check_moe_align_hand), ("moe_vs_brute", check_moe_vs_brute)]
+    out += [("round_bf16_hand", check_round_bf16_hand), ("round_bf16_vs_torch", check_round_bf16_vs_torch),
+            ("dequant_bf16", check_dequant_bf16)]
     return out

@@ -142,6 +142,25 @@ def test_workspace_checked_before_launch():
     assert qg.plan(1, 28672, 4096, 128, qg.W4_A_BF16)[1:] == (1, 0)
 
 
+def test_dequantize_validation():
+    L = qg.lib()
+
+    def dq(w=P, s=P, z=None, K=256, N=256, G=128, prec=qg.W4_A_BF16, zp=0, out=P2):
+        return L.qgemm_dequantize(w, s, z, K, N, G, prec, zp, out, None)
+
+    assert dq(prec=qg.W8_A_F32) == qg.EUNSUPPORTED
+    assert dq(prec=qg.W4_A_F32) == qg.EUNSUPPORTED
+    assert dq(G=64) == qg.EUNSUPPORTED
+    assert dq(K=0) == qg.EINVAL
+    assert dq(N=0) == qg.EINVAL
+    assert dq(K=200, G=128) == qg.EINVAL       # K % G
+    assert dq(K=8 * 65536, G=128) == qg.EUNSUPPORTED
+    assert dq(zp=1, z=P, N=100) == qg.EUNSUPPORTED
+    assert dq(zp=1, z=None) == qg.EINVAL
+    assert dq(w=None) == qg.EINVAL and dq(s=None) == qg.EINVAL and dq(out=None) == qg.EINVAL
+    assert dq(w=MIS) == qg.EALIGN and dq(out=MIS) == qg.EALIGN and dq(zp=1, z=MIS) == qg.EALIGN
+
+
 def test_quantize_validation():
     L = qg.lib()
     q = lambda A=P, M=4, K=256, G=32, Aq=P2, s=P: L.qgemm_quantize_activations(A, M, K, G, Aq, s, None)

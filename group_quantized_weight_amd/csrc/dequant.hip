@@ -1,7 +1,7 @@
 // Whole-matrix dequantization of packed int4 weights to bf16, for comparing
 // the fused kernels with the pages' prefill alternative: dequantize once, then
 // run a dense bf16 GEMM (the switch vLLM's AWQ makes above a token count, page
-// "quantization-and-fused-kernels" (arganzheng.life), sections 三.2 and 三.4).
+// "quantization-and-fused-kernels" (arganzheng.life), section 三.2).
 //
 //   w_hat[k][n] = bf16(s[k/G][n] * (q[k][n] - z[k/G][n]))
 //

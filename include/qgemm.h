@@ -189,7 +189,7 @@ int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq,
 /* Whole-matrix dequantization of packed int4 weights to bf16, for comparing
  * the fused kernels with dequantization followed by a dense bf16 GEMM (the
  * prefill alternative of the page "quantization-and-fused-kernels"
- * (arganzheng.life), sections 三.2 and 三.4):
+ * (arganzheng.life), section 三.2):
  *     out[k][n] = bf16(s[k/G][n] * (q[k][n] - z[k/G][n]))
  * with z = 8 without zero-points. s * (q - z) is exact in float32, so out is
  * the correctly rounded (nearest even) bf16 of the exact value.

@@ -63,6 +63,18 @@ struct GemmArgs {
   int stages;              // LDS ring depth: 3, or 2 with at least two tiles per compute unit
 };
 
+struct SmallI8Args {
+  const int8_t *A;         // [M][K] int8 codes
+  const float *a_scale;    // [M][K/G]
+  const uint32_t *W;       // packed int4 or int8, layout version 2
+  const float *S;          // [K/G][N] float32
+  const uint32_t *Z;       // [K/G][N/8] or null (int4 only)
+  float *out;              // [M][N] float32 (nsplit == 1)
+  float *partial;          // [nsplit][M][Np] (nsplit > 1)
+  int M, N, K, G, Np;
+  int nsplit;              // K / 128 chunks split into nsplit slices
+};
+
 struct SmallArgs {
   const uint16_t *A;       // [M][K] bf16, M <= 64
   const uint32_t *W;       // packed int4, layout version 2
@@ -109,6 +121,8 @@ hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int 
 // whole-matrix int4 -> bf16 dequantization (dequant.hip)
 hipError_t launch_dequant_w4(const uint32_t *W, const uint16_t *S, const uint32_t *Z, uint16_t *out, int K, int N,
                              int G, hipStream_t st);
+// small-M integer MFMA path for int8 activations (gemm_small_i8.hip)
+hipError_t launch_gemm_small_i8(int wfmt, bool zp, int mb, const SmallI8Args &a, dim3 grid, hipStream_t st);
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
                            const float *w_scale, uint16_t *out, int M, int N, int K, int cus, hipStream_t stream);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.

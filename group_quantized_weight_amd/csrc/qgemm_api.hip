@@ -87,6 +87,7 @@ size_t padded_cols(int N) { return ((size_t)N + kColAlign - 1) / kColAlign * kCo
 
 constexpr size_t kPartialCap = 256ull << 20;  // bytes of float32 partials at most
 constexpr int kSmallMaxM = 64;                // rows the small-M MFMA path takes (4 blocks of 16)
+constexpr int kSmallI8MinM = 9;               // int8 activations: fewer rows stay on the vector-ALU GEMV
 constexpr size_t kGemvLdsCap = 60 * 1024;     // dynamic LDS per workgroup (static LDS comes on top)
 constexpr int kMoeMaxExperts = 1024;          // experts the align step's LDS counters hold
 constexpr int kDqFuseMaxM = 4;                // in-call int8 quantization fused into the GEMV up to this M
@@ -140,11 +141,18 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   const size_t Np = padded_cols(N);
   const bool gemm_ok = f.a == A_BF16 && G == 128 && K % kGemmKC == 0 && N % 8 == 0 && M <= 65535 &&
                        gemm_asum_bytes(M, K) <= (size_t)INT_MAX;
-  const bool small_ok = f.a == A_BF16 && G == 128 && N % 8 == 0 && M <= kSmallMaxM &&
-                        (size_t)M * K * 2 <= (size_t)INT_MAX;
+  // int8 activations (given, or quantized by the pre-pass) take the integer
+  // MFMA kernel from kSmallI8MinM rows on
+  const bool small_i8 = f.a == A_I8;
+  const bool small_ok = small_i8 ? ((G == 32 || G == 128) && K % 128 == 0 && N % 4 == 0 && M <= kSmallMaxM &&
+                                    (size_t)M * K <= (size_t)INT_MAX)
+                                 : (f.a == A_BF16 && G == 128 && N % 8 == 0 && M <= kSmallMaxM &&
+                                    (size_t)M * K * 2 <= (size_t)INT_MAX);
   int path = force_path;
   if (path == QG_PATH_AUTO)
-    path = (M >= 2 && small_ok) ? QG_PATH_SMALL : (M > 8 && gemm_ok) ? QG_PATH_GEMM : QG_PATH_GEMV;
+    path = (M >= (small_i8 ? kSmallI8MinM : 2) && small_ok) ? QG_PATH_SMALL
+           : (M > 8 && gemm_ok)                             ? QG_PATH_GEMM
+                                                            : QG_PATH_GEMV;
   if ((path == QG_PATH_GEMM && !gemm_ok) || (path == QG_PATH_SMALL && !small_ok)) return QG_EUNSUPPORTED;
   if (path != QG_PATH_GEMV && path != QG_PATH_GEMM && path != QG_PATH_SMALL) return QG_EINVAL;
   p.path = path;
@@ -326,6 +334,18 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     const dim3 grid(p.tiles_x, p.mblocks, p.nsplit);
     e = f.a == A_I8 ? launch_gemv_i8(f.w, has_zp != 0, p.dq_fused, p.mb, a, grid, p.lds, s)
                     : launch_gemv(f.w, f.a, f.s, f.o, has_zp != 0, p.mb, a, grid, p.lds, s);
+  } else if (p.path == QG_PATH_SMALL && f.a == A_I8) {
+    SmallI8Args a;
+    a.A = (const int8_t *)A;
+    a.a_scale = (const float *)a_scales;
+    a.W = (const uint32_t *)w_packed;
+    a.S = (const float *)scales;
+    a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
+    a.out = (float *)out;
+    a.partial = partial;
+    a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np;
+    a.nsplit = p.nsplit;
+    e = launch_gemm_small_i8(f.w, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.nsplit), s);
   } else if (p.path == QG_PATH_SMALL) {
     SmallArgs a;
     a.A = (const uint16_t *)A;

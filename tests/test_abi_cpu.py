@@ -254,6 +254,12 @@ CASES = [(1, 28672, 4096, 128, 1), (8, 28672, 8192, 128, 1), (1, 128256, 4096, 1
 CASES += [(M, 4096, 4096, 128, 1) for M in (1, 16, 64, 256, 1024, 4096)]
 
 
+def _int8_path(M, N, K, G):
+    """int8 activations: the integer MFMA kernel for 9..64 rows on shapes it
+    takes (K % 128 == 0, N % 4 == 0), else the vector-ALU GEMV."""
+    return qg.PATH_SMALL if 9 <= M <= 64 and K % 128 == 0 and N % 4 == 0 else qg.PATH_GEMV
+
+
 @pytest.mark.parametrize("M,N,K,G,prec", CASES)
 def test_plan_is_pure_and_consistent(M, N, K, G, prec):
     a = qg.plan(M, N, K, G, prec)
@@ -269,8 +275,10 @@ def test_plan_is_pure_and_consistent(M, N, K, G, prec):
         assert (path, ns) == qg.plan(M, N, K, G, prec - 3)[:2]
         pre = 0 if M <= 4 else -(-M * K // 256) * 256 + -(-M * (K // G) * 4 // 256) * 256
         assert ws == pre + qg.plan(M, N, K, G, prec - 3)[2]
-        assert path == qg.PATH_GEMV
+        assert path == _int8_path(M, N, K, G)
         return
+    if prec in (4, 5):
+        assert path == _int8_path(M, N, K, G)
     if path in (qg.PATH_GEMV, qg.PATH_SMALL):
         assert (ws == 0) == (ns == 1)
         assert ws == (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)
@@ -298,6 +306,13 @@ def test_forced_plans():
         qg.plan(65, 1000, 1024, 128, qg.W4_A_BF16, qg.PATH_SMALL, 0)
     with pytest.raises(qg.QGemmError):   # ... bf16 activations and groups of 128 only
         qg.plan(16, 1000, 1024, 32, qg.W4_A_BF16, qg.PATH_SMALL, 0)
+    # int8 activations: the integer MFMA kernel, groups of 32 or 128, K % 128 == 0, N % 4 == 0
+    for prec in (qg.W4_A_I8, qg.W8_A_I8, qg.W4_A_F32_DQ8, qg.W8_A_F32_DQ8):
+        assert qg.plan(3, 1000, 1024, 32, prec, qg.PATH_SMALL, 0)[0] == qg.PATH_SMALL
+        assert qg.plan(64, 1000, 1024, 128, prec, qg.PATH_SMALL, 0)[0] == qg.PATH_SMALL
+        for bad in ((16, 1002, 1024, 32), (16, 1000, 1056, 32), (65, 1000, 1024, 32)):
+            with pytest.raises(qg.QGemmError):
+                qg.plan(*bad, prec, qg.PATH_SMALL, 0)
     # the MFMA paths need N % 8 == 0; automatic dispatch sends other N to the GEMV
     with pytest.raises(qg.QGemmError):
         qg.plan(300, 1001, 1024, 128, qg.W4_A_BF16, qg.PATH_GEMM, 0)

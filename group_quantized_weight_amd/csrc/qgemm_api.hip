@@ -182,8 +182,15 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   // and the small-M path's partials grow with M). Measured on MI355X, K = N = 4096:
   // M = 256 26.1 us at nsplit 4 vs 31.4 us at 8; M = 512 31.2 us at 2 vs
   // 38.7 us at 4.
+  // The small-M MFMA paths split only when the tiles leave at least half the
+  // compute units idle: at 176 tiles (K = 2048, N = 11264, int8 activations,
+  // M = 32) no split ran 12.4 vs 15.3 us (2 slices), while at 64 tiles
+  // (K = N = 4096, bf16, M = 16 / 64) 4 slices ran 8.5 / 15.6 vs 11.2 / 22.9
+  // us unsplit (the partials and the reduce cost more than the extra
+  // workgroups recover once most units are busy).
   const long long target = path == QG_PATH_GEMV ? 2LL * cus : cus;
-  int ns = force_nsplit > 0 ? force_nsplit : (base >= cus ? 1 : (int)((target + base - 1) / base));
+  const long long full = path == QG_PATH_SMALL ? (cus + 1) / 2 : cus;
+  int ns = force_nsplit > 0 ? force_nsplit : (base >= full ? 1 : (int)((target + base - 1) / base));
   ns = balance(p.units, ns);
   if (path == QG_PATH_GEMV)
     while (ns < p.units && gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) ns = balance(p.units, ns + 1);

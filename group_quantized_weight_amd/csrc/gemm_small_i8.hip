@@ -12,10 +12,11 @@
 // "quantization-and-fused-kernels" (arganzheng.life), section 三.3, item 6).
 //
 // Structure, as the bf16 small-M kernel (gemm_small.hip):
-//   - a workgroup (4 waves) covers one 64-column tile of the packed layout and
-//     a K-slice of whole 128-wide chunks (the z-split of the first page,
-//     section 3.3); each wave takes a contiguous share of the slice's chunks
-//     and loads the next chunk while it computes the current one;
+//   - a workgroup (8 waves for int4 weights and M <= 48, else 4) covers one
+//     64-column tile of the packed layout and a K-slice of whole 128-wide
+//     chunks (the z-split of the first page, section 3.3); each wave takes a
+//     contiguous share of the slice's chunks (with 4 waves it loads the next
+//     chunk while it computes the current one);
 //   - M is padded to MB blocks of 16 rows; rows past M read zeros through the
 //     buffer's range check and are not written;
 //   - a chunk is 4 k-steps of 32; a group is one step (G = 32) or four
@@ -31,7 +32,7 @@
 //     zero-points), all in int32;
 //   - int8: two word-rows per step, bytes in k order, D = P;
 //   - per group: acc += (a_scale * s) * float(D);
-//   - the 4 waves' results are added in wave order through LDS, then written
+//   - the waves' results are added in wave order through LDS, then written
 //     to the output (nsplit == 1) or to float32 partials that a second kernel
 //     adds in the order z = 0..nsplit-1.
 #include "common.h"
@@ -45,7 +46,6 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_i;
 typedef __attribute__((ext_vector_type(4))) int i32x4_i;
 typedef __attribute__((ext_vector_type(4))) float f32x4_i;
 
-constexpr int kWavesI = 4;
 constexpr int kBufWord3i = 0x00020000;
 constexpr int kStreamPolicyI = 2;   // non-temporal
 constexpr int kDeadI = (int)0x80000000u;
@@ -56,8 +56,20 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 
 }  // namespace
 
+// Waves per workgroup: 8 for int4 weights (4 loads per chunk; the second
+// wave on each SIMD hides a chunk's latency, and twice the waves share the
+// per-group float32 work: K = 2048, N = 11264, M = 32, 12.4 -> 11.4 us), 4
+// for int8 weights, which load the next chunk while computing the current
+// one (8 loads per chunk: 4 waves with that prefetch 12.4 us, 8 without it
+// 13.3 us). Two chunk register sets do not fit in 256 VGPRs, the limit with
+// two waves per SIMD, and neither does one with 4 row blocks (M > 48), which
+// also keep 4 waves.
+template <int WF, int MB>
+constexpr int i8_waves() { return WF == W4 && MB <= 3 ? 8 : 4; }
+
 template <int WF, int G, int MB, bool ZP>
-__global__ __launch_bounds__(kWavesI * kWave) void gemm_small_i8_kernel(SmallI8Args a) {
+__global__ __launch_bounds__((i8_waves<WF, MB>() * kWave)) void gemm_small_i8_kernel(SmallI8Args a) {
+  constexpr int kWavesI = i8_waves<WF, MB>();
   extern __shared__ __align__(16) unsigned char s_red[];   // [waves - 1][MB * 16][64] float32
   constexpr int KPW = WF == W4 ? 8 : 4;          // k per packed word
   constexpr int RPC = 128 / KPW;                 // word-rows per chunk
@@ -215,15 +227,23 @@ __global__ __launch_bounds__(kWavesI * kWave) void gemm_small_i8_kernel(SmallI8A
     }
   };
 
-  ChunkLoads cur, nxt;
-  issue(0, cur);
-  for (int ci = 0; ci < wcc; ++ci) {
-    issue(ci + 1, nxt);
-    compute(cur);
-    cur = nxt;
+  if constexpr (kWavesI == 4) {
+    ChunkLoads cur, nxt;
+    issue(0, cur);
+    for (int ci = 0; ci < wcc; ++ci) {
+      issue(ci + 1, nxt);
+      compute(cur);
+      cur = nxt;
+    }
+  } else {
+    ChunkLoads cur;
+    for (int ci = 0; ci < wcc; ++ci) {
+      issue(ci, cur);
+      compute(cur);
+    }
   }
 
-  // ---- the 4 waves' results, added in wave order: waves 1..3 hand theirs
+  // ---- the waves' results, added in wave order: waves 1.. hand theirs
   // to wave 0 through LDS (element (16 fm + 4 lk + r, 4 li + fn) of wave w at
   // s_red[(((w - 1) * MB + fm) * 16 + 4 lk + r) * 64 + 4 li + fn]) ----
   float *red = (float *)s_red;
@@ -259,6 +279,7 @@ __global__ __launch_bounds__(kWavesI * kWave) void gemm_small_i8_kernel(SmallI8A
 
 template <int WF, int G, int MB, bool ZP>
 static hipError_t go_i8(const SmallI8Args &a, dim3 grid, hipStream_t st) {
+  constexpr int kWavesI = i8_waves<WF, MB>();
   const size_t lds = (size_t)(kWavesI - 1) * MB * 16 * 64 * 4;
   gemm_small_i8_kernel<WF, G, MB, ZP><<<grid, kWavesI * kWave, lds, st>>>(a);
   return hipGetLastError();

@@ -128,6 +128,37 @@ def test_int8_partials_bit_exact(prec, zp, M):
     assert np.array_equal(out, P.sum(axis=1).astype(np.float64))
 
 
+@pytest.mark.parametrize("prec,zp", [(4, False), (4, True), (5, False), (7, True), (8, False)])
+@pytest.mark.parametrize("G", [32, 128])
+@pytest.mark.parametrize("M,ns", [(9, 1), (16, 3), (33, 1), (48, 3), (49, 1), (64, 3)])
+def test_int8_mfma_path(prec, zp, G, M, ns):
+    """The integer-MFMA kernel for int8 activations (forced, with a K-split of
+    1 or 3): every row-block count (8-wave and 4-wave builds), both group
+    sizes, int4 with and without zero-points, int8 weights, ragged N (1000:
+    a partial last tile), given or in-call quantized activations."""
+    N, K = 1000, 1024
+    p = wl.make_problem(M, N, K, G, prec, zp, seed=7300 + M + G + prec + zp)
+    assert qg.plan(M, N, K, G, prec, qg.PATH_SMALL, ns)[:2] == (qg.PATH_SMALL, ns)
+    out = Dev(p).run(force_path=qg.PATH_SMALL, force_nsplit=ns)
+    ref, bound = oracle.for_problem(p)
+    check(to_f64(out), ref, bound, f"int8 mfma prec={prec} zp={zp} G={G} M={M} ns={ns}")
+
+
+@pytest.mark.parametrize("prec,zp", [(4, True), (5, False)])
+@pytest.mark.parametrize("M,ns", [(33, 1), (64, 4)])
+def test_int8_mfma_partials_bit_exact(prec, zp, M, ns):
+    """Unit scales: the float32 output of the integer-MFMA kernel is the sum of
+    the exact per-group integer partials (below 2^24), with or without a
+    K-split."""
+    N, K, G = 1000, 2048, 32
+    p = wl.make_problem(M, N, K, G, prec, zp, seed=7400 + M + prec)
+    p.S = np.ones_like(p.S)
+    p.a_scale = np.ones_like(p.a_scale)
+    out = to_f64(Dev(p).run(force_path=qg.PATH_SMALL, force_nsplit=ns))
+    P = oracle.int_partials(M, N, K, G, p.wfmt, zp, p.A, p.W, p.Z)
+    assert np.array_equal(out, P.sum(axis=1).astype(np.float64))
+
+
 @pytest.mark.parametrize("prec,path,M", [(6, 0, 1), (6, 1, 40), (6, 2, 24), (2, 0, 3), (3, 0, 1), (4, 0, 2)])
 def test_scale_doubling_bitwise(prec, path, M):
     p = wl.make_problem(M, 512, 1024, 128 if prec == 6 else 32, prec, False, seed=8000 + M)

@@ -182,14 +182,17 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   // and the small-M path's partials grow with M). Measured on MI355X, K = N = 4096:
   // M = 256 26.1 us at nsplit 4 vs 31.4 us at 8; M = 512 31.2 us at 2 vs
   // 38.7 us at 4.
-  // The small-M MFMA paths split only when the tiles leave at least half the
-  // compute units idle: at 176 tiles (K = 2048, N = 11264, int8 activations,
-  // M = 32) no split ran 12.4 vs 15.3 us (2 slices), while at 64 tiles
-  // (K = N = 4096, bf16, M = 16 / 64) 4 slices ran 8.5 / 15.6 vs 11.2 / 22.9
-  // us unsplit (the partials and the reduce cost more than the extra
-  // workgroups recover once most units are busy).
+  // The GEMV and the small-M MFMA path split only when the tiles leave at
+  // least half the compute units idle (the partials and the reduce cost more
+  // than the extra workgroups recover once most units are busy). At 176
+  // tiles (K = 2048, N = 11264) no split ran: GEMV M = 1, int8 activations,
+  // q4_0 6.1 vs 9.1 us (3 slices), q8_0 7.7 vs 9.9 us, float32 activations
+  // 9.2 vs 9.7 and 10.1 vs 11.3 us; integer MFMA, M = 32, 12.4 vs 15.3 us (2
+  // slices). At 64 tiles (K = N = 4096, bf16, M = 16 / 64) 4 slices ran 8.5
+  // / 15.6 vs 11.2 / 22.9 us unsplit. The tiled GEMM splits below one tile
+  // per unit (M = 512, 128 tiles: 31.2 us at 2 slices).
   const long long target = path == QG_PATH_GEMV ? 2LL * cus : cus;
-  const long long full = path == QG_PATH_SMALL ? (cus + 1) / 2 : cus;
+  const long long full = path == QG_PATH_GEMM ? cus : (cus + 1) / 2;
   int ns = force_nsplit > 0 ? force_nsplit : (base >= full ? 1 : (int)((target + base - 1) / base));
   ns = balance(p.units, ns);
   if (path == QG_PATH_GEMV)

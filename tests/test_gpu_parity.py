@@ -95,6 +95,41 @@ def test_edge_shapes():
         check(out, ref, bound, f"edge M={M} N={N} K={K} G={G} prec={prec} zp={zp}", bf16_out=prec == 1)
 
 
+# the largest K the ABI takes: 65535 packed word-rows (int4: K <= 524280, int8
+# codes: K <= 262140), rounded down to whole groups; and the largest M of the
+# tiled GEMM (65535 rows). Ragged N, every path, the planned K-split.
+KMAX4, KMAX8 = 524160, 262016
+
+
+@pytest.mark.parametrize("M,N,K,G,prec,zp,path", [
+    (1, 72, KMAX4, 128, 1, True, qg.PATH_GEMV),
+    (3, 40, KMAX4, 128, 6, False, qg.PATH_GEMV),
+    (3, 40, KMAX4, 128, 6, False, qg.PATH_SMALL),
+    (2, 72, KMAX4, 32, 2, False, qg.PATH_GEMV),
+    (2, 72, KMAX8, 128, 3, False, qg.PATH_GEMV),
+    (2, 72, KMAX4, 128, 4, True, qg.PATH_GEMV),
+    (3, 72, KMAX4, 32, 7, False, qg.PATH_GEMV),
+    (20, 72, KMAX4, 128, 1, True, qg.PATH_SMALL),
+    (20, 72, KMAX4, 32, 7, False, qg.PATH_SMALL),
+    (33, 72, KMAX8, 128, 5, False, qg.PATH_SMALL),
+    (130, 72, KMAX4, 128, 1, False, qg.PATH_GEMM),
+    (65535, 8, 256, 128, 1, True, qg.PATH_GEMM),
+    (65535, 8, 128, 128, 6, False, qg.PATH_GEMM),
+])
+def test_maximum_sizes(M, N, K, G, prec, zp, path):
+    p = wl.make_problem(M, N, K, G, prec, zp, seed=4100 + M + N + G + prec)
+    planned = qg.plan(M, N, K, G, prec, path)
+    assert planned[0] == path, planned
+    d = Dev(p)
+    out = to_f64(d.run(force_path=path))
+    rows = sample_indices(M, 24, 3) if M * K > (1 << 24) else None
+    ref, bound = oracle.for_problem(p, rows=rows)
+    if rows is not None:
+        out = out[rows]
+    check(out, ref, bound, f"max M={M} N={N} K={K} G={G} prec={prec} zp={zp} plan={planned}",
+          bf16_out=p.ofmt == "bf16")
+
+
 # ---------------------------------------------------------------------------
 # invariants with exact answers
 # ---------------------------------------------------------------------------

@@ -18,7 +18,9 @@ the timed steps see the clocks the device settles at under that load), then
 the W warmup steps; the K timed steps are captured in a HIP graph (the
 library's calls are capture-safe) and replayed; HIP events on the launch
 stream bracket the replay, with torch.cuda.synchronize() on both sides.
---mode eager times a plain launch loop instead.
+--mode eager times a plain launch loop instead. Beside the mean step time,
+per_call_us gives the spread of single calls (median, p10, p90 of 100 calls,
+each bracketed by events on an idle device, so launch latency is included).
 """
 import argparse
 import ctypes
@@ -108,6 +110,25 @@ def time_steps(fn, steps, warmup, mode):
     return e0.elapsed_time(e1) / steps
 
 
+def per_call_spread(fn, runs=100):
+    """Per-call time including the launch: each call is enqueued on an idle
+    device, bracketed by HIP events on the launch stream; median, p10 and p90
+    over `runs` calls (cycling through the rotated weight copies), in us."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for i, (e0, e1) in enumerate(ev):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    q = lambda f: t[min(runs - 1, int(round(f * (runs - 1))))]
+    return {"median": round(q(0.5), 2), "p10": round(q(0.1), 2), "p90": round(q(0.9), 2), "runs": runs,
+            "how": "HIP events around each call on an idle device (eager, launch included)"}
+
+
 def device_problem(p, copies):
     """Device tensors of a workloads.Problem with `copies` packed weight/scale copies."""
     from tests.gpu_util import to_dev
@@ -143,10 +164,11 @@ def run_workload(name, steps, warmup, mode, M=None, force_path=-1, force_nsplit=
     stream = torch.cuda.current_stream().cuda_stream
     call = Prepared(qg, p.M, p.N, p.K, p.G, p.prec, A, a_scale, Ws, Ss, Z, out, stream, force_path, force_nsplit)
     ms = time_steps(call, steps, warmup, mode)
+    spread = per_call_spread(call)
     path, ns, ws = qg.plan(p.M, p.N, p.K, p.G, p.prec, force_path, force_nsplit)
     res = dict(workload=name, M=p.M, N=p.N, K=p.K, group=p.G, prec=qg._PREC_FMT[p.prec], has_zp=p.has_zp,
                path=["gemv", "gemm", "small"][path], nsplit=ns, copies=copies, ms=ms,
-               bytes=algorithmic_bytes(p), flops=2 * p.M * p.N * p.K)
+               bytes=algorithmic_bytes(p), flops=2 * p.M * p.N * p.K, per_call_us=spread)
     res["gbs"] = res["bytes"] / (ms * 1e-3) / 1e9
     res["tflops"] = res["flops"] / (ms * 1e-3) / 1e12
     del A, a_scale, Ws, Ss, Z, out, call
@@ -552,9 +574,11 @@ def bench(args):
                    "weight_copies_rotated": head["copies"], "timing": args.mode},
         "roofline": {"bound": "hbm", "achieved": round(head["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "per_call_us": head["per_call_us"],
         "gemm_m1024": {"workload": "prefill_w4a16_m1024", "us": round(gemm["ms"] * 1e3, 2),
                        "tflops": round(gemm["tflops"], 2), "peak_tflops": BF16_PEAK_TFLOPS,
-                       "frac": round(gemm["tflops"] / BF16_PEAK_TFLOPS, 4), "nsplit": gemm["nsplit"]},
+                       "frac": round(gemm["tflops"] / BF16_PEAK_TFLOPS, 4), "nsplit": gemm["nsplit"],
+                       "per_call_us": gemm["per_call_us"]},
         "crossover": sweep,
         "fp8_w8a8": fp8,
         "moe_grouped_gemv": moe,

@@ -190,10 +190,22 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   // 9.2 vs 9.7 and 10.1 vs 11.3 us; integer MFMA, M = 32, 12.4 vs 15.3 us (2
   // slices). At 64 tiles (K = N = 4096, bf16, M = 16 / 64) 4 slices ran 8.5
   // / 15.6 vs 11.2 / 22.9 us unsplit. The tiled GEMM splits below one tile
-  // per unit (M = 512, 128 tiles: 31.2 us at 2 slices).
+  // per unit (M = 512, 128 tiles: 31.2 us at 2 slices), into at most one
+  // workgroup per unit: its 3-stage ring holds one workgroup per unit, so a
+  // slice count that overshoots runs a second round of workgroups (M = 384,
+  // 96 tiles: 3 slices 39.5 us, 2 slices 31.1 us; M = 96 .. 512 the rounded
+  // down count is the fastest or within 5% of it).
   const long long target = path == QG_PATH_GEMV ? 2LL * cus : cus;
   const long long full = path == QG_PATH_GEMM ? cus : (cus + 1) / 2;
-  int ns = force_nsplit > 0 ? force_nsplit : (base >= full ? 1 : (int)((target + base - 1) / base));
+  int ns;
+  if (force_nsplit > 0)
+    ns = force_nsplit;
+  else if (base >= full)
+    ns = 1;
+  else if (path == QG_PATH_GEMM)
+    ns = (int)(cus / base);
+  else
+    ns = (int)((target + base - 1) / base);
   ns = balance(p.units, ns);
   if (path == QG_PATH_GEMV)
     while (ns < p.units && gemv_lds(f, p.mb, G, p.units, ns) > kGemvLdsCap) ns = balance(p.units, ns + 1);

@@ -293,6 +293,26 @@ def test_plan_is_pure_and_consistent(M, N, K, G, prec):
         assert path == qg.PATH_GEMV
 
 
+def test_tiled_gemm_split_stays_within_one_round():
+    """The tiled GEMM's 3-stage ring holds one workgroup per compute unit (256
+    without a device), so its automatic K-split never makes more workgroups
+    than units: floor(units / tiles) slices, evened out over the K chunks."""
+    cus = 256
+    for M in (65, 96, 128, 192, 256, 320, 384, 448, 512, 640, 896, 1024, 4096):
+        for N in (1000, 4096, 11008):
+            path, ns, _ = qg.plan(M, N, 4096, 128, qg.W4_A_BF16, qg.PATH_GEMM, 0)
+            tiles = -(-M // 128) * -(-N // 128)
+            assert path == qg.PATH_GEMM
+            if tiles >= cus:
+                assert ns == 1, (M, N, ns)
+            else:
+                assert tiles * ns <= cus, (M, N, tiles, ns)
+                # floor(units / tiles) slices, evened out over the 32 chunks
+                units, want = 4096 // 128, min(cus // tiles, 4096 // 128)
+                per = -(-units // want)
+                assert ns == -(-units // per), (M, N, tiles, ns)
+
+
 def test_forced_plans():
     for ns in (1, 2, 3, 7, 32, 1000):
         path, got, ws = qg.plan(1, 1000, 4096, 128, qg.W4_A_BF16, qg.PATH_GEMV, ns)

@@ -55,7 +55,8 @@ def _check_align(ids, E, block):
 
 @pytest.mark.parametrize("T,topk,E,block", [(5, 2, 3, 4), (1, 1, 1, 1), (16, 2, 8, 4), (64, 6, 64, 8),
                                             (300, 8, 256, 2), (7, 3, 40, 8), (16, 2, 8, 16), (100, 6, 64, 32),
-                                            (512, 2, 8, 64)])
+                                            (512, 2, 8, 64), (40, 8, 1024, 4), (200, 6, 1000, 16),
+                                            (2048, 8, 256, 16)])
 def test_align(T, topk, E, block):
     rng = np.random.Generator(np.random.PCG64(1700 + T + E))
     ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)])

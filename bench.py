@@ -276,10 +276,14 @@ def run_fp8(name, steps, warmup, mode):
     out = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
     L = qg.lib()
     stream = vp(torch.cuda.current_stream().cuda_stream)
+    # the automatic K-split of qgemm_fp8_gemm_ex (none from 256 output tiles up)
+    ws_bytes = L.qgemm_fp8_workspace_bytes(p.M, p.N, p.K, p.scaling)
+    wsb = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def gemm(i):
-        st = L.qgemm_fp8_gemm(p.M, p.N, p.K, p.scaling, vp(Aq.data_ptr()), vp(sc.data_ptr()),
-                              vp(Ws[i % copies].data_ptr()), vp(ws0.data_ptr()), vp(out.data_ptr()), stream)
+        st = L.qgemm_fp8_gemm_ex(p.M, p.N, p.K, p.scaling, vp(Aq.data_ptr()), vp(sc.data_ptr()),
+                                 vp(Ws[i % copies].data_ptr()), vp(ws0.data_ptr()), vp(out.data_ptr()),
+                                 vp(wsb.data_ptr()), ws_bytes, 0, stream)
         assert st == 0, st
 
     def step(i):
@@ -293,7 +297,8 @@ def run_fp8(name, steps, warmup, mode):
     res = dict(workload=name, M=p.M, N=p.N, K=p.K, scaling=["per_token", "blockwise"][p.scaling],
                gemm_us=round(ms_gemm * 1e3, 2), step_us=round(ms_step * 1e3, 2),
                gemm_tflops=round(flops / (ms_gemm * 1e-3) / 1e12, 1),
-               frac_fp8_peak=round(flops / (ms_gemm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4), scaled_mm_us=None)
+               frac_fp8_peak=round(flops / (ms_gemm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4), scaled_mm_us=None,
+               nsplit=qg.fp8_nsplit(p.M, p.N, p.K, p.scaling))
     if p.scaling == 0:
         try:
             a8 = Aq.view(torch.float8_e4m3fn)
@@ -308,7 +313,7 @@ def run_fp8(name, steps, warmup, mode):
             res["scaled_mm_us"] = round(time_steps(sm, steps, warmup, "eager") * 1e3, 2)
         except Exception as e:   # not every torch build has row-wise FP8 scaling on this GPU
             log(f"bench: torch._scaled_mm unavailable here ({type(e).__name__})")
-    del A, Ws, Aq, sc, out
+    del A, Ws, Aq, sc, out, wsb
     torch.cuda.empty_cache()
     return res
 
@@ -532,7 +537,8 @@ def bench(args):
 
     fp8 = []
     if not args.no_fp8:
-        for name in ("fp8_tok_m1024", "fp8_blk_m1024", "fp8_tok_m4096", "fp8_blk_m4096"):
+        for name in ("fp8_tok_m16", "fp8_tok_m256", "fp8_tok_m1024", "fp8_blk_m1024", "fp8_tok_m4096",
+                     "fp8_blk_m4096"):
             r = run_fp8(name, 100, 20, args.mode)
             fp8.append(r)
             log(f"bench: {name}: gemm {r['gemm_us']} us ({r['gemm_tflops']} TFLOP/s), with quantization "

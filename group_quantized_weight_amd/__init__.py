@@ -90,6 +90,10 @@ def lib():
             L.qgemm_fp8_quantize.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
             L.qgemm_fp8_gemm.restype = c_int
             L.qgemm_fp8_gemm.argtypes = [c_int] * 4 + [vp] * 6
+            L.qgemm_fp8_workspace_bytes.restype = c_size
+            L.qgemm_fp8_workspace_bytes.argtypes = [c_int] * 4
+            L.qgemm_fp8_gemm_ex.restype = c_int
+            L.qgemm_fp8_gemm_ex.argtypes = [c_int] * 4 + [vp] * 6 + [c_size, c_int, vp]
             L.qgemm_quantize_activations.restype = c_int
             L.qgemm_quantize_activations.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
             L.qgemm_dequantize.restype = c_int
@@ -278,19 +282,42 @@ def fp8_quantize(A, block: int = FP8_PER_TOKEN, stream=None, Aq=None, a_scales=N
     return Aq, sc
 
 
-def fp8_gemm(Aq, a_scales, Wq, w_scales, scaling: int = FP8_PER_TOKEN, out=None, stream=None):
+def fp8_gemm(Aq, a_scales, Wq, w_scales, scaling: int = FP8_PER_TOKEN, out=None, stream=None, ws=None,
+             force_nsplit: int = 0, split: bool = True):
     """bf16 [M, N] = FP8 GEMM of E4M3 codes Aq [M, K] and Wq [N, K] with
-    float32 scales (see include/qgemm.h)."""
+    float32 scales (see include/qgemm.h). With split (the default) the call
+    is qgemm_fp8_gemm_ex, which splits K when the output tiles leave compute
+    units idle (ws: a workspace of qgemm_fp8_workspace_bytes, allocated here
+    when not given); split=False calls qgemm_fp8_gemm, never split."""
     import torch
     M, K = Aq.shape
     N = Wq.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=Aq.device)
-    st = lib().qgemm_fp8_gemm(M, N, K, scaling, _ptr(Aq), _ptr(a_scales), _ptr(Wq), _ptr(w_scales), _ptr(out),
-                              stream if stream is not None else _stream(Aq.device))
+    st_arg = stream if stream is not None else _stream(Aq.device)
+    if not split:
+        st = lib().qgemm_fp8_gemm(M, N, K, scaling, _ptr(Aq), _ptr(a_scales), _ptr(Wq), _ptr(w_scales), _ptr(out),
+                                  st_arg)
+        if st != OK:
+            raise QGemmError(st, "qgemm_fp8_gemm")
+        return out
+    need = lib().qgemm_fp8_workspace_bytes(M, N, K, scaling)
+    if force_nsplit > 0:
+        need = max(need, force_nsplit * M * -(-N // 128) * 128 * 4)
+    if ws is None:
+        ws = workspace(need, Aq.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().qgemm_fp8_gemm_ex(M, N, K, scaling, _ptr(Aq), _ptr(a_scales), _ptr(Wq), _ptr(w_scales), _ptr(out),
+                                 _ptr(ws) if ws is not None else None, ws_bytes, force_nsplit, st_arg)
     if st != OK:
-        raise QGemmError(st, "qgemm_fp8_gemm")
+        raise QGemmError(st, "qgemm_fp8_gemm_ex")
     return out
+
+
+def fp8_nsplit(M: int, N: int, K: int, scaling: int = FP8_PER_TOKEN) -> int:
+    """The automatic K-split of qgemm_fp8_gemm_ex, from its workspace size."""
+    b = lib().qgemm_fp8_workspace_bytes(M, N, K, scaling)
+    return b // (M * -(-N // 128) * 128 * 4) if b else 1
 
 
 def run(A, w_packed, scales, *, N: int, G: int, prec: int, zeros=None, a_scales=None, out=None,

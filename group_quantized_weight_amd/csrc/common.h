@@ -124,7 +124,8 @@ hipError_t launch_dequant_w4(const uint32_t *W, const uint16_t *S, const uint32_
 // small-M integer MFMA path for int8 activations (gemm_small_i8.hip)
 hipError_t launch_gemm_small_i8(int wfmt, bool zp, int mb, const SmallI8Args &a, dim3 grid, hipStream_t st);
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
-                           const float *w_scale, uint16_t *out, int M, int N, int K, int cus, hipStream_t stream);
+                           const float *w_scale, uint16_t *out, float *partial, int M, int N, int K, int nsplit,
+                           int Np, int cus, hipStream_t stream);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t stream);

@@ -189,7 +189,8 @@ constexpr int kF8Stage = 2 * kF8OpBytes + 512;    // A, B, and the block's 128 a
 template <bool BLOCKWISE, int STAGES>
 __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict__ Aq, const float *__restrict__ a_scale,
                                                       const uint8_t *__restrict__ Wq, const float *__restrict__ w_scale,
-                                                      uint16_t *__restrict__ out, int M, int N, int K) {
+                                                      uint16_t *__restrict__ out, float *__restrict__ partial, int M,
+                                                      int N, int K, int nsplit, int Np) {
   static_assert(STAGES == 2 || STAGES == 3, "ring depth");
   __shared__ __align__(16) unsigned char s_ring[STAGES * kF8Stage];
   const int lane = threadIdx.x & 63;
@@ -198,6 +199,9 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
   const int wr = wave >> 1, wc = wave & 1;
   const int m0 = blockIdx.y * kF8Tile, n0 = blockIdx.x * kF8Tile;
   const int nsteps = K / 128;
+  // K-slice blockIdx.z of nsplit: steps s0 .. s0 + cnt - 1
+  int s0, cnt;
+  split_range(nsteps, nsplit, blockIdx.z, s0, cnt);
 
   // operand resources start at the tile's first row; rows past M (or N) fall
   // outside num_records and read zeros
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
     auto step = [&](int i, const Frags &C, Frags &Nx) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(8 * (STAGES - 2)) : "memory");
       const int nx = i + STAGES;
-      copy_step(nx, i % STAGES, nx < nsteps ? 0 : kDead);
+      copy_step(s0 + nx, i % STAGES, nx < cnt ? 0 : kDead);
       read_step(i + 1, Nx);
 #pragma unroll
       for (int fm = 0; fm < 4; ++fm)
@@ -294,23 +298,23 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
       }
     };
 #pragma unroll
-    for (int p = 0; p < STAGES; ++p) copy_step(p, p, nsteps > p ? 0 : kDead);
+    for (int p = 0; p < STAGES; ++p) copy_step(s0 + p, p, cnt > p ? 0 : kDead);
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 * (STAGES - 1)) : "memory");
     Frags f0, f1;
     read_step(0, f0);
-    for (int i = 0; i < nsteps; i += 2) {
+    for (int i = 0; i < cnt; i += 2) {
       step(i, f0, f1);
-      if (i + 1 < nsteps) step(i + 1, f1, f0);
+      if (i + 1 < cnt) step(i + 1, f1, f0);
     }
   } else {
-    copy_step(0, 0, 0);
-    if constexpr (STAGES == 3) copy_step(1, 1, nsteps > 1 ? 0 : kDead);
-    for (int i = 0; i < nsteps; ++i) {
+    copy_step(s0, 0, cnt > 0 ? 0 : kDead);
+    if constexpr (STAGES == 3) copy_step(s0 + 1, 1, cnt > 1 ? 0 : kDead);
+    for (int i = 0; i < cnt; ++i) {
       // this step's copies are done when at most the next step's remain in flight
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
       // every wave is past step i - 1: its stage takes step i + STAGES - 1
       const int nx = i + STAGES - 1;
-      copy_step(nx, nx % STAGES, nx < nsteps ? 0 : kDead);
+      copy_step(s0 + nx, nx % STAGES, nx < cnt ? 0 : kDead);
       const unsigned char *sb = s_ring + (i % STAGES) * kF8Stage;
       i32x8_v af[4], bfr[4];
   #pragma unroll
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
         bfr[f] = frag(sb + kF8OpBytes, 64 * wc + 16 * f + li);
       }
       if constexpr (BLOCKWISE) {
-        const float sb_w = w_scale[(size_t)(n0 / 128) * nsteps + i];   // one per workgroup tile and block
+        const float sb_w = w_scale[(size_t)(n0 / 128) * nsteps + s0 + i];   // one per workgroup tile and block
         const float *sa = (const float *)(sb + 2 * kF8OpBytes);
   #pragma unroll
         for (int fm = 0; fm < 4; ++fm) {
@@ -357,6 +361,11 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         v[r] = BLOCKWISE ? acc[fm][fn][r] : as * ((n + r < N ? w_scale[n + r] : 0.f) * acc[fm][fn][r]);
+      if (nsplit > 1) {
+        // the slice's scaled float32 partial; the reduce adds slices z = 0..nsplit-1
+        *(f32x4_v *)&partial[((size_t)blockIdx.z * M + m) * Np + n] = (f32x4_v){v[0], v[1], v[2], v[3]};
+        continue;
+      }
       const f32x2_v lo = {v[0], v[1]}, hi = {v[2], v[3]};
       const uint32_t b01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_v));
       const uint32_t b23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_v));
@@ -376,23 +385,30 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
 
 template <bool BLOCKWISE>
 static void go_fp8(int stages, dim3 grid, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
-                   const float *w_scale, uint16_t *out, int M, int N, int K, hipStream_t st) {
+                   const float *w_scale, uint16_t *out, float *partial, int M, int N, int K, int nsplit, int Np,
+                   hipStream_t st) {
   if (stages == 2)
-    fp8_gemm_kernel<BLOCKWISE, 2><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+    fp8_gemm_kernel<BLOCKWISE, 2><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, partial, M, N, K, nsplit, Np);
   else
-    fp8_gemm_kernel<BLOCKWISE, 3><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, M, N, K);
+    fp8_gemm_kernel<BLOCKWISE, 3><<<grid, 256, 0, st>>>(Aq, a_scale, Wq, w_scale, out, partial, M, N, K, nsplit, Np);
 }
 
+// nsplit > 1: the K steps are split into nsplit slices (grid z) that write
+// float32 partials [nsplit][M][Np] to `partial`, then the fixed-order reduce
+// writes `out`.
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
-                           const float *w_scale, uint16_t *out, int M, int N, int K, int cus, hipStream_t st) {
+                           const float *w_scale, uint16_t *out, float *partial, int M, int N, int K, int nsplit,
+                           int Np, int cus, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const dim3 grid((N + kF8Tile - 1) / kF8Tile, (M + kF8Tile - 1) / kF8Tile);
-  const int stages = (long long)grid.x * grid.y >= 2LL * cus ? 2 : 3;
+  const dim3 grid((N + kF8Tile - 1) / kF8Tile, (M + kF8Tile - 1) / kF8Tile, nsplit);
+  const int stages = (long long)grid.x * grid.y * nsplit >= 2LL * cus ? 2 : 3;
   if (scaling == 1)
-    go_fp8<true>(stages, grid, Aq, a_scale, Wq, w_scale, out, M, N, K, st);
+    go_fp8<true>(stages, grid, Aq, a_scale, Wq, w_scale, out, partial, M, N, K, nsplit, Np, st);
   else
-    go_fp8<false>(stages, grid, Aq, a_scale, Wq, w_scale, out, M, N, K, st);
-  return hipGetLastError();
+    go_fp8<false>(stages, grid, Aq, a_scale, Wq, w_scale, out, partial, M, N, K, nsplit, Np, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit <= 1) return e;
+  return launch_reduce(O_BF16, partial, out, M, N, Np, nsplit, st);
 }
 
 }  // namespace qg

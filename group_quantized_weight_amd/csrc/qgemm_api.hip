@@ -616,8 +616,12 @@ int qgemm_fp8_quantize(const void *A, int M, int K, int block, void *Aq, void *a
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
 
-int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void *a_scales, const void *Wq,
-                   const void *w_scales, void *out, void *stream) {
+// FP8 GEMM plan: workgroup tiles of 128 x 128 over (N, M); with fewer tiles
+// than compute units the K steps are split into slices, at most one round of
+// one workgroup per unit (the 3-stage ring holds one workgroup per unit), as
+// for the tiled W4 GEMM, and evened out over the steps. Partials [nsplit][M]
+// [Np] with Np = N rounded up to the tile.
+static int fp8_check(int M, int N, int K, int scaling) {
   if (M < 0 || N <= 0 || K <= 0) return QG_EINVAL;
   if (scaling != QG_FP8_PER_TOKEN && scaling != QG_FP8_BLOCKWISE) return QG_EUNSUPPORTED;
   if (K % 128 != 0) return QG_EINVAL;
@@ -625,15 +629,54 @@ int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void 
   // buffer resources address 128 rows of K bytes, and 128 rows of K / 128 scales,
   // with 32-bit offsets; the grid has ceil(M / 128) rows of workgroups
   if ((size_t)128 * K > (size_t)INT_MAX || (M + 127) / 128 > 65535) return QG_EUNSUPPORTED;
+  if ((size_t)(N + 127) / 128 * 128 > (size_t)INT_MAX) return QG_EUNSUPPORTED;
+  return QG_OK;
+}
+
+static int fp8_nsplit(int M, int N, int K, int force_nsplit, int cus) {
+  const int nsteps = K / 128;
+  const long long tiles = (long long)((N + 127) / 128) * ((M + 127) / 128);
+  const size_t Np = (size_t)(N + 127) / 128 * 128;
+  int ns = force_nsplit > 0 ? force_nsplit : (tiles >= cus ? 1 : (int)(cus / tiles));
+  ns = balance(nsteps, ns);
+  if (force_nsplit <= 0)
+    while (ns > 1 && (size_t)ns * M * Np * 4 > kPartialCap) ns = balance(nsteps, ns - 1);
+  return ns;
+}
+
+size_t qgemm_fp8_workspace_bytes(int M, int N, int K, int scaling) {
+  if (fp8_check(M, N, K, scaling) != QG_OK || M == 0) return 0;
+  const int ns = fp8_nsplit(M, N, K, 0, device_cus());
+  return ns > 1 ? (size_t)ns * M * ((size_t)(N + 127) / 128 * 128) * 4 : 0;
+}
+
+int qgemm_fp8_gemm_ex(int M, int N, int K, int scaling, const void *Aq, const void *a_scales, const void *Wq,
+                      const void *w_scales, void *out, void *workspace, size_t workspace_bytes, int force_nsplit,
+                      void *stream) {
+  const int chk = fp8_check(M, N, K, scaling);
+  if (chk != QG_OK) return chk;
+  if (force_nsplit < 0) return QG_EINVAL;
   if (M == 0) return QG_OK;
   if (!Aq || !a_scales || !Wq || !w_scales || !out) return QG_EINVAL;
   if (!aligned16(Aq) || !aligned16(a_scales) || !aligned16(Wq) || !aligned16(w_scales) || !aligned16(out))
     return QG_EALIGN;
+  const int cus = device_cus();
+  const int ns = fp8_nsplit(M, N, K, force_nsplit, cus);
+  const int Np = (N + 127) / 128 * 128;
+  if (ns > 1) {
+    if (!workspace || workspace_bytes < (size_t)ns * M * Np * 4) return QG_EWORKSPACE;
+    if (!aligned16(workspace)) return QG_EALIGN;
+  }
   drop_pending_error();
   const hipError_t e = launch_fp8_gemm(scaling, (const uint8_t *)Aq, (const float *)a_scales, (const uint8_t *)Wq,
-                                       (const float *)w_scales, (uint16_t *)out, M, N, K, device_cus(),
-                                       (hipStream_t)stream);
+                                       (const float *)w_scales, (uint16_t *)out, (float *)workspace, M, N, K, ns, Np,
+                                       cus, (hipStream_t)stream);
   return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void *a_scales, const void *Wq,
+                   const void *w_scales, void *out, void *stream) {
+  return qgemm_fp8_gemm_ex(M, N, K, scaling, Aq, a_scales, Wq, w_scales, out, nullptr, 0, 1, stream);
 }
 
 const char *qgemm_strerror(int status) {

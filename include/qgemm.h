@@ -302,10 +302,35 @@ int qgemm_fp8_quantize(const void *A, int M, int K, int block, void *Aq, void *a
  *       promoted into a float32 accumulator once per block.
  * M >= 0 (0 is a no-op), N >= 1, K % 128 == 0; N % 128 == 0 for
  * QG_FP8_BLOCKWISE; all pointers device pointers, 16-byte aligned. One
- * kernel on `stream`; nothing allocated; bitwise reproducible.
+ * kernel on `stream` (never split along K); nothing allocated; bitwise
+ * reproducible.
  */
 int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void *a_scales, const void *Wq,
                    const void *w_scales, void *out, void *stream);
+
+/*
+ * The same product with the K steps split into slices when the 128 x 128
+ * output tiles alone leave compute units idle (the z-split of the page
+ * "04 · 分组量化 GEMM 内核" (developer.aliyun.com), section 3.3): each slice
+ * writes its scaled float32 partial to `workspace` ([nsplit][M][Np] float32,
+ * Np = N rounded up to 128), and a second kernel adds the slices in the
+ * fixed order z = 0..nsplit-1, then rounds once to bf16. The split count is a
+ * pure function of (M, N, K) and the device's compute-unit count; results
+ * are bitwise reproducible, and differ from the unsplit sum by float32
+ * rounding order only.
+ *   workspace: device, 16-byte aligned, at least
+ *              qgemm_fp8_workspace_bytes(M, N, K, scaling) bytes (NULL when
+ *              that is 0); contents on entry do not matter.
+ *   force_nsplit: 0 for the automatic split, or a slice count to use (for
+ *              tests and benchmarks; clamped to the K / 128 steps).
+ * QG_EWORKSPACE when the split needs more workspace than given; otherwise
+ * errors as qgemm_fp8_gemm. Two kernels on `stream` when split; nothing
+ * allocated.
+ */
+size_t qgemm_fp8_workspace_bytes(int M, int N, int K, int scaling);
+int qgemm_fp8_gemm_ex(int M, int N, int K, int scaling, const void *Aq, const void *a_scales, const void *Wq,
+                      const void *w_scales, void *out, void *workspace, size_t workspace_bytes, int force_nsplit,
+                      void *stream);
 
 /* Human-readable text of a status code. */
 const char *qgemm_strerror(int status);

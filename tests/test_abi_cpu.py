@@ -202,6 +202,37 @@ def test_fp8_validation():
         assert g(**{kw: MIS}) == qg.EALIGN, kw
 
 
+def test_fp8_split_plan_and_validation():
+    """The K-split FP8 entry point: the split stays within one round of one
+    workgroup per compute unit (256 without a device), the workspace holds
+    [nsplit][M][N rounded up to 128] float32, and a call whose split needs
+    more workspace than given is refused before any launch."""
+    L = qg.lib()
+    for M, N, K, want in [(1, 4096, 4096, 8), (16, 4096, 4096, 8), (128, 4096, 4096, 8), (256, 4096, 4096, 4),
+                          (512, 4096, 4096, 2), (1024, 4096, 4096, 1), (4096, 4096, 4096, 1),
+                          (16, 200, 256, 2), (16, 128, 384, 3), (300, 1000, 4096, 8)]:
+        tiles = -(-M // 128) * -(-N // 128)
+        ns = qg.fp8_nsplit(M, N, K)
+        assert ns == want, (M, N, K, ns)
+        assert ns == 1 or tiles * ns <= 256
+        b = L.qgemm_fp8_workspace_bytes(M, N, K, 0)
+        assert b == (ns * M * -(-N // 128) * 128 * 4 if ns > 1 else 0)
+    assert L.qgemm_fp8_workspace_bytes(16, 200, 256, 1) == 0          # blockwise needs N % 128
+    assert L.qgemm_fp8_workspace_bytes(16, 256, 200, 0) == 0          # K % 128
+    g = lambda M=16, N=256, K=1024, sc=0, ws=None, wsb=0, ns=0, out=P2: L.qgemm_fp8_gemm_ex(
+        M, N, K, sc, P, P, P, P, out, ws, wsb, ns, None)
+    need = L.qgemm_fp8_workspace_bytes(16, 256, 1024, 0)
+    assert need == 8 * 16 * 256 * 4
+    assert g() == qg.EWORKSPACE
+    assert g(ws=P, wsb=need - 1) == qg.EWORKSPACE
+    assert g(ws=MIS, wsb=need) == qg.EALIGN
+    assert g(ns=-1) == qg.EINVAL
+    assert g(ns=3, ws=P, wsb=3 * 16 * 256 * 4 - 4) == qg.EWORKSPACE   # a forced split needs its own size
+    assert g(M=0, out=None) == qg.OK
+    assert g(sc=1, N=200) == qg.EUNSUPPORTED
+    assert g(out=MIS, ws=P, wsb=need) == qg.EALIGN
+
+
 def test_moe_validation():
     L = qg.lib()
     assert L.qgemm_moe_max_tiles(10, 3, 4) == 4            # (10 + 3 * 3) // 4

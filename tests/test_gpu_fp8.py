@@ -114,6 +114,32 @@ def _gemm_case(M, N, K, scaling, seed):
 
 
 @pytest.mark.parametrize("scaling", [0, 1])
+@pytest.mark.parametrize("M,N,K,ns", [(16, 256, 1024, 0), (16, 256, 1024, 3), (33, 384, 2048, 8),
+                                      (130, 512, 1024, 2), (7, 200, 640, 5), (1, 128, 128, 4)])
+def test_gemm_k_split(scaling, M, N, K, ns):
+    """K split into slices (automatic or forced; a single 128-step K clamps
+    to one slice) against the oracle, bitwise reproducible, and the unsplit
+    entry point beside it on the same inputs."""
+    import torch
+    if scaling == 1 and N % 128:
+        pytest.skip("blockwise scaling needs N % 128 == 0")
+    p = wl.make_fp8_problem(M, N, K, scaling, seed=1350 + M + N + K + ns + scaling, outlier_frac=0.01)
+    block = 0 if scaling == 0 else 128
+    Aq, sc = _quant_same(p.A, block, f"split inputs M={M} K={K}")
+    Wq, ws = _u8_dev(p.Wq), _f32_dev(p.w_scale)
+    o1 = qg.fp8_gemm(Aq, sc, Wq, ws, scaling, force_nsplit=ns)
+    o2 = qg.fp8_gemm(Aq, sc, Wq, ws, scaling, force_nsplit=ns)
+    o0 = qg.fp8_gemm(Aq, sc, Wq, ws, scaling, split=False)
+    torch.cuda.synchronize()
+    assert bitwise_equal(o1, o2), "rerun not bitwise equal"
+    ref, bound = oracle.fp8_gemm(M, N, K, scaling, Aq.cpu().numpy(), sc.cpu().numpy(), p.Wq, p.w_scale)
+    used = ns if ns > 0 else qg.fp8_nsplit(M, N, K, scaling)
+    for o, what in ((o1, f"split {used}"), (o0, "unsplit")):
+        check(o.float().cpu().numpy().astype(np.float64), ref, bound,
+              f"fp8 {what} scaling={scaling} M={M} N={N} K={K}", bf16_out=True)
+
+
+@pytest.mark.parametrize("scaling", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (5, 256, 512), (128, 128, 256), (200, 384, 384),
                                    (17, 1024, 1024)])
 def test_gemm_small(scaling, M, N, K):
@@ -135,7 +161,8 @@ def test_gemm_two_stage_ring(scaling):
     Aq, sc = _quant_same(p.A, block, "two-stage inputs")
     Wq, ws = _u8_dev(p.Wq), _f32_dev(p.w_scale)
     out = qg.fp8_gemm(Aq, sc, Wq, ws, scaling)
-    part = qg.fp8_gemm(Aq[:128].contiguous(), sc[:128].contiguous(), Wq, ws, scaling)
+    # unsplit, as the 512-tile product is: the comparison is of the two rings
+    part = qg.fp8_gemm(Aq[:128].contiguous(), sc[:128].contiguous(), Wq, ws, scaling, force_nsplit=1)
     torch.cuda.synchronize()
     assert bitwise_equal(out[:128].contiguous(), part), "2-stage and 3-stage rings differ"
     cols = sample_indices(N, 256, 5)

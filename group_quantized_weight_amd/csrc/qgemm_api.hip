@@ -637,7 +637,12 @@ static int fp8_nsplit(int M, int N, int K, int force_nsplit, int cus) {
   const int nsteps = K / 128;
   const long long tiles = (long long)((N + 127) / 128) * ((M + 127) / 128);
   const size_t Np = (size_t)(N + 127) / 128 * 128;
-  int ns = force_nsplit > 0 ? force_nsplit : (tiles >= cus ? 1 : (int)(cus / tiles));
+  // at most max(4, 128 / M) slices: past that the partials' traffic costs
+  // more than the extra workgroups recover (K = N = 4096, forced sweeps: M = 16
+  // best at 8 slices, 10.5 us vs 11.0 at 4; M = 32, 64, 128 best at 3-4, 6-8%
+  // ahead of 8)
+  const int cap = M > 0 && 128 / M > 4 ? 128 / M : 4;
+  int ns = force_nsplit > 0 ? force_nsplit : (tiles >= cus ? 1 : (int)std::min<long long>(cus / tiles, cap));
   ns = balance(nsteps, ns);
   if (force_nsplit <= 0)
     while (ns > 1 && (size_t)ns * M * Np * 4 > kPartialCap) ns = balance(nsteps, ns - 1);

@@ -204,13 +204,14 @@ def test_fp8_validation():
 
 def test_fp8_split_plan_and_validation():
     """The K-split FP8 entry point: the split stays within one round of one
-    workgroup per compute unit (256 without a device), the workspace holds
+    workgroup per compute unit (256 without a device) and at max(4, 128 / M)
+    slices, evened out over the K steps; the workspace holds
     [nsplit][M][N rounded up to 128] float32, and a call whose split needs
     more workspace than given is refused before any launch."""
     L = qg.lib()
-    for M, N, K, want in [(1, 4096, 4096, 8), (16, 4096, 4096, 8), (128, 4096, 4096, 8), (256, 4096, 4096, 4),
-                          (512, 4096, 4096, 2), (1024, 4096, 4096, 1), (4096, 4096, 4096, 1),
-                          (16, 200, 256, 2), (16, 128, 384, 3), (300, 1000, 4096, 8)]:
+    for M, N, K, want in [(1, 4096, 4096, 8), (16, 4096, 4096, 8), (32, 4096, 4096, 4), (128, 4096, 4096, 4),
+                          (256, 4096, 4096, 4), (512, 4096, 4096, 2), (1024, 4096, 4096, 1), (4096, 4096, 4096, 1),
+                          (16, 200, 256, 2), (16, 128, 384, 3), (300, 1000, 4096, 4), (4, 128, 4096, 32)]:
         tiles = -(-M // 128) * -(-N // 128)
         ns = qg.fp8_nsplit(M, N, K)
         assert ns == want, (M, N, K, ns)

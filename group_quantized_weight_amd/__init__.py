@@ -164,15 +164,22 @@ def pack(w_canonical, K: int, N: int, prec: int):
 _ws_cache = {}
 
 
+_ws_retired = []
+
+
 def workspace(nbytes: int, device):
     """A workspace of at least nbytes on device (cached per device and grown;
-    its contents before a call do not matter to the library)."""
+    its contents before a call do not matter to the library). A workspace
+    that is outgrown is kept alive, never freed: a HIP graph captured while
+    it was current still writes to it on every replay."""
     import torch
     if nbytes == 0:
         return None
     key = str(device)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _ws_retired.append(ws)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws

@@ -101,3 +101,35 @@ def test_moe_in_graph(block):
         qg.moe_run(A, Wp, S, routing, topk=p.topk, N=p.N, G=p.G, E=p.E, block=block, out=out)
 
     _replays_match(fn, out)
+
+
+def test_graph_survives_workspace_growth():
+    """A graph captured while the binding's cached workspace was current keeps
+    its results after a later call grows that workspace and fresh memory is
+    filled: the outgrown workspace stays alive."""
+    import torch
+    qg._ws_cache.clear()      # start from a small workspace (earlier graphs are gone)
+    p = wl.make_problem(16, 1000, 1024, 128, 1, True, seed=2500)
+    d = Dev(p)
+    out = d.run(force_path=qg.PATH_SMALL, force_nsplit=4)
+    small = qg._ws_cache["cuda:0"].numel()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        d.run(force_path=qg.PATH_SMALL, force_nsplit=4, out=out)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            d.run(force_path=qg.PATH_SMALL, force_nsplit=4, out=out)
+        big = wl.make_problem(64, 4096, 2048, 128, 1, False, seed=2501)
+        Dev(big).run(force_path=qg.PATH_SMALL, force_nsplit=8)     # needs a larger workspace
+        assert qg._ws_cache["cuda:0"].numel() > small
+        junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
+        torch.cuda.synchronize()
+        for r in range(3):
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert bitwise_equal(out, ref), f"replay {r} differs after the workspace grew"
+        del g, junk

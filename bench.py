@@ -13,8 +13,10 @@ sweep against a dense bf16 torch.matmul on the same shapes and against the
 pages' prefill alternative (dequantize the weights to bf16, then the dense
 GEMM), and the fp64 CPU oracle timed on the host cores (cpu_baseline).
 
-Timing: each measurement first runs its step untimed for about 0.25 s (so
-the timed steps see the clocks the device settles at under that load), then
+Timing: each measurement first runs its step untimed for about 0.25 s (1 s
+for the headline, the first measurement of the process, which starts from an
+idle device) so the timed steps see the clocks the device settles at under
+that load, then
 the W warmup steps; the K timed steps are captured in a HIP graph (the
 library's calls are capture-safe) and replayed; HIP events on the launch
 stream bracket the replay, with torch.cuda.synchronize() on both sides.
@@ -39,6 +41,7 @@ BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 ROTATE_BYTES = 640 << 20
 SETTLE_S = 0.25
+HEAD_SETTLE_S = 1.0
 
 
 def log(*a):
@@ -68,7 +71,7 @@ class Prepared:
             raise RuntimeError(f"qgemm_run_ex failed: {st}")
 
 
-def time_steps(fn, steps, warmup, mode):
+def time_steps(fn, steps, warmup, mode, settle=None):
     """ms per step of fn(i) for i in range(steps), after warmup steps. Runs on
     torch's current stream, which main() sets to a side stream (graph capture
     needs a non-default stream)."""
@@ -78,7 +81,7 @@ def time_steps(fn, steps, warmup, mode):
     # timed steps see the clocks the device holds under this load
     t0 = time.perf_counter()
     i = 0
-    while time.perf_counter() - t0 < SETTLE_S:
+    while time.perf_counter() - t0 < (SETTLE_S if settle is None else settle):
         for _ in range(50):
             fn(i)
             i += 1
@@ -152,7 +155,7 @@ def algorithmic_bytes(p):
     return wbytes + sbytes + zbytes + abytes + obytes
 
 
-def run_workload(name, steps, warmup, mode, M=None, force_path=-1, force_nsplit=0):
+def run_workload(name, steps, warmup, mode, M=None, force_path=-1, force_nsplit=0, settle=None):
     import torch
     import group_quantized_weight_amd as qg
     import workloads as wl
@@ -163,7 +166,7 @@ def run_workload(name, steps, warmup, mode, M=None, force_path=-1, force_nsplit=
     out = torch.empty((p.M, p.N), dtype=qg.out_dtype(p.prec), device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     call = Prepared(qg, p.M, p.N, p.K, p.G, p.prec, A, a_scale, Ws, Ss, Z, out, stream, force_path, force_nsplit)
-    ms = time_steps(call, steps, warmup, mode)
+    ms = time_steps(call, steps, warmup, mode, settle)
     spread = per_call_spread(call)
     path, ns, ws = qg.plan(p.M, p.N, p.K, p.G, p.prec, force_path, force_nsplit)
     res = dict(workload=name, M=p.M, N=p.N, K=p.K, group=p.G, prec=qg._PREC_FMT[p.prec], has_zp=p.has_zp,
@@ -514,7 +517,8 @@ def bench(args):
         return
 
     log(f"bench: {args.workload} steps={args.steps} warmup={args.warmup} mode={args.mode}")
-    head, p = run_workload(args.workload, args.steps, args.warmup, args.mode)
+    # the first measurement of a fresh process meets an idle device: settle longer
+    head, p = run_workload(args.workload, args.steps, args.warmup, args.mode, settle=HEAD_SETTLE_S)
     log(f"bench: {args.workload}: {head['ms'] * 1e3:.2f} us/step, {head['gbs']:.0f} GB/s")
 
     # long enough runs (milliseconds) that the clocks have settled under MFMA load

@@ -24,9 +24,10 @@ constexpr int kTileCols = 64;                // packed layout: columns per tile
 // measured slower on MI355X, for single-row decode and the other shapes.)
 __host__ __device__ constexpr int gemv_waves(int) { return 4; }
 
-// GEMM path: one workgroup = 4 waves (each 128 x 32), tile 128 x 128, K
-// chunks of 128.
-constexpr int kGemmThreads = 256;
+// GEMM path: one workgroup = 8 waves (two per SIMD, sharing 128 rows x 32
+// columns and splitting each chunk's k-steps), tile 128 x 128, K chunks of
+// 128 (one group).
+constexpr int kGemmThreads = 512;
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmKC = 128;
@@ -51,16 +52,18 @@ struct GemvArgs {
 };
 
 struct GemmArgs {
-  const uint16_t *A;       // [M][K] bf16
+  const uint16_t *A;       // [M][K] bf16 (read by the pre-pass only)
   const uint32_t *W;       // packed int4, layout version 2
-  const uint16_t *S;       // [K/G][N] bf16
-  const uint32_t *Z;       // [K/G][N/8] or null
+  const uint16_t *S;       // [K/128][N] bf16 (read by the pre-pass only)
+  const uint32_t *Z;       // [K/128][N/8] or null
   void *out;               // [M][N] bf16 or float32 (nsplit == 1)
   float *partial;          // [nsplit][M][Np] (nsplit > 1)
-  float *asum;             // [K/128][Mp] activation sums per group, x -136 without zero-points (workspace)
-  int M, N, K, G, Np, Mp;  // Mp = M rounded up to kGemmBM
-  int nchunks, nsplit;     // K / kGemmKC chunks split into nsplit slices
-  int stages;              // LDS ring depth: 3, or 2 with at least two tiles per compute unit
+  // written by the pre-pass into the workspace:
+  uint16_t *A16;           // [M][K] fp16: a * 2^e(m), exact for |a| within 2^-14 .. 2^15 after scaling
+  int *rexp;               // [M] the row's exponent e(m)
+  float *S32;              // [K/128][Np] float32 scales, zero past N
+  int M, N, K, Np;
+  int nchunks, nsplit;     // K / 128 chunks (groups) split into nsplit slices
 };
 
 struct SmallI8Args {
@@ -106,7 +109,9 @@ hipError_t launch_moe_align(const int *topk_ids, int numel, int E, int block, in
 // float32 and the kernel quantizes them per (row, group) itself
 hipError_t launch_gemv_i8(int wfmt, bool zp, bool dq, int mb, const GemvArgs &a, dim3 grid, size_t lds_bytes,
                           hipStream_t stream);
-hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t stream);
+// pre-pass (fp16 activations, exponents, float32 scales), then the MFMA
+// kernel on grid (Np / 128, ceil(M / 128), nsplit)
+hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStream_t stream);
 // mb = ceil(M / 16) row blocks; grid (Np / 64, nsplit)
 hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np,

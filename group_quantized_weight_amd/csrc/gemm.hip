@@ -2,81 +2,82 @@
 // bf16 scales, optional int4 zero-points, groups of 128; for M large enough
 // that the work is a dense contraction (prefill).
 //
-// Structure (the W4A16 main loop of the page "quantization-and-fused-kernels"
-// (arganzheng.life), section 三.1: int4 tile -> unpack in registers -> matrix
-// instruction in bf16 with float32 accumulation; and the multi-stage
-// global-to-shared pipeline of its section 三.3, item 2):
-//   - workgroup tile 128 x 128, K in chunks of 128 = one group; 4 waves, one
-//     per SIMD, each owning all 128 rows and 32 columns (8 x 2 tiles of
-//     v_mfma_f32_16x16x32_bf16, so each dequantized weight fragment feeds 8
-//     MFMAs);
-//   - the chunk's activation tile, scales, zero-points and activation sums
-//     are copied by buffer loads straight into LDS (no registers on the way),
-//     into a ring of ST stages: 3 (one chunk in use, two in flight; 103 KiB,
-//     one workgroup per compute unit) when the grid is about one workgroup
-//     per compute unit, 2 (one in flight; 69 KiB, so two workgroups share a
-//     compute unit and cover each other's waits) when there are at least two
-//     tiles per compute unit (measured on MI355X, K = N = 4096: M = 4096 151
-//     -> 136 us, M = 2048 77 -> 70 us). Each wave waits for its own copies,
-//     then a barrier makes every wave's copies visible;
-//   - the activation tile's 16-byte pieces are XOR-swizzled with the row
-//     index, so the MFMA fragment reads of 16 rows hit 16 different 4-bank
-//     groups; rows past M read zeros through the buffer's range check (their
-//     results are not written);
-//   - weights: each lane loads 8 bytes of packed words (2 adjacent columns x
-//     8 k) into registers one chunk ahead, and turns each word into four bf16
-//     pairs (128 + q) with one and-or per pair (bf16 magic number 0x4300,
-//     section 二.4 of the same page); the two columns feed the two column
-//     tiles of the wave, so column j of tile f is physical column n + 2j + f.
-//     The weight fragment is the MFMA's first operand and the activation
-//     fragment its second, so each tile is computed transposed: a lane holds
-//     row 16 fm + l % 16 and, over its two tiles, the 8 adjacent columns
-//     32 w + 8 (l / 16) .. +7, which the epilogue writes with one 16-byte
-//     store (8-byte stores of 2 columns x 4 rows per lane before: measured
-//     M = 4096 142 -> 135 us, M = 2048 75 -> 69 us, M = 1024 about 2% faster,
-//     M = 256 2% slower);
-//   - per group, the MFMA accumulates sum_k a_k (128 + q_k) on top of the
-//     initial value -(128 + z) * sum_k a_k, which gives sum_k a_k (q_k - z);
-//     the group's scale is then applied in float32 (acc += s * P), the
-//     per-block promotion of the same page, section 四.3, overlapped with the
-//     next chunk's MFMAs. The (q - z) values are exact in bf16 and the scale
-//     never rounds into a bf16 weight. The per-(group, row) activation sums
-//     come from asum_kernel, a pre-pass that adds each group's 128 values in
-//     a fixed order;
-//   - with nsplit > 1, K-slices of whole chunks write float32 partial tiles
-//     that a second kernel adds in the fixed order z = 0..nsplit-1 (the
-//     z-split and fixed-order reduce of the page "04 · 分组量化 GEMM 内核"
-//     (developer.aliyun.com), section 3.3).
+// The page "quantization-and-fused-kernels" (arganzheng.life) describes the
+// W4A16 main loop (section 三.1: int4 tile -> unpack in registers -> matrix
+// instruction with float32 accumulation), the fp16 magic-number dequant
+// (section 二.4) and the per-block float32 promotion of a blockwise-scaled
+// product (section 四.3). Here:
+//
+//   - The weight operand is the exact integer q - z in fp16. The word's codes
+//     are placed into the low mantissa bits of 1024.0 (0x6400 | q, and
+//     0x6400 | 16 q for the codes one nibble higher), and one packed fp16
+//     add or fma per pair subtracts 1024 + z (or scales by 1/16 and subtracts
+//     64 + z). Every step is exact, so a column whose codes equal its
+//     zero-point contributes exactly zero: no biased sum is formed and no
+//     bias is removed afterwards.
+//   - The activation operand is fp16: a pre-pass writes a(m, k) * 2^e(m),
+//     with one power of two per row chosen so that the row's largest
+//     magnitude lands in [2^14, 2^15). That is exact for every bf16 value
+//     whose scaled magnitude is at least 2^-14 (fp16's normal range; the
+//     rest, 2^28 or more below the row's maximum, round to fp16 subnormals).
+//     The epilogue multiplies by 2^-e(m), exactly. The pre-pass also widens
+//     the bf16 scales to float32 in a zero-padded [K/128][Np] array.
+//   - Products of fp16 a and small integers are exact in float32, so the
+//     MFMA accumulates sum_k a_k (q_k - z) per group in float32; then
+//     acc += s(g, n) * P in float32 (the promotion), overlapped with the next
+//     group's MFMAs. The scale never rounds into an fp16 weight.
+//
+// Tiling: workgroup tile 128 x 128, 4 waves (one per SIMD), each wave all 128
+// rows and 32 columns as 4 tiles of v_mfma_f32_32x32x16_f16, so each
+// dequantized weight fragment feeds 4 MFMAs. The weights are the MFMA's first
+// operand: a lane holds output row 32 fm + (l % 32) and, by the choice of the
+// weight row-to-column map, the 16 adjacent columns 32 w + 16 (l / 32) .. +15.
+// K is processed in chunks of 128 (one group). A chunk's activations (fp16,
+// 32 KiB), packed weights (8 KiB), float32 scales and zero-points are copied
+// by buffer loads straight into LDS (buffer_load ... lds), 2 chunks ahead,
+// into a ring of 3 stages (weights and activations) and 4 stages (scales and
+// zero-points: a chunk's scales are still read during the next chunk). The
+// group's products go to one of two accumulator sets that alternate between
+// chunks, so the promotion of a chunk is spread over the next chunk's MFMAs
+// (two float32 FMAs per MFMA).
+//
+// With nsplit > 1, K-slices of whole chunks write float32 partial tiles that
+// a second kernel adds in the fixed order z = 0..nsplit-1 (the z-split and
+// fixed-order reduce of the page "04 · 分组量化 GEMM 内核"
+// (developer.aliyun.com), section 3.3).
 #include "common.h"
 
 namespace qg {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_g;
-typedef __attribute__((ext_vector_type(2))) float f32x2_g;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One LDS stage holds the operands of one chunk that all waves share:
-// [activations 128 x 256 B][scales 128 x 2 B][activation sums 128 x 4 B]
-// [zero-points 16 x 4 B]. Each small slot is as large as one wave-wide copy
-// writes (lanes past the useful part copy neighbouring data into the slot's
-// tail, never read). The packed weights go straight to registers.
-constexpr int kARow = kGemmKC * 2;                   // 256 B per activation row
-constexpr int kAOff = 0;
-constexpr int kSOff = kAOff + kGemmBM * kARow;       // 32 KiB
-constexpr int kQOff = kSOff + 1024;
-constexpr int kZOff = kQOff + 1024;
-constexpr int kStageBytes = kZOff + 256;             // 35072
 constexpr int kBufWord3 = 0x00020000;
-constexpr int kPolicyStream = 2;                     // non-temporal
+constexpr int kPolicyStream = 2;  // non-temporal
+
+// Main ring stage: [activations 128 rows x 256 B][weights 16 word-rows x 128 columns x 4 B].
+constexpr int kARow = 256;
+constexpr int kAOff = 0;
+constexpr int kWOff = 128 * kARow;               // 32 KiB
+constexpr int kStage = kWOff + 16 * 128 * 4;     // 40 KiB
+constexpr int kST = 3;
+// Small ring stage: one 1 KiB slot per wave, each written by one
+// 16-byte-per-lane copy: [scales 128 x 4 B][zero-points 16 x 4 B][six idle
+// slots] (lanes past the useful part fill the slot's tail, never read).
+constexpr int kSOff = 0;
+constexpr int kZOff = 1024;
+constexpr int kSmall = 8192;
+constexpr int kSR = 4;
 
 // Wait until at most N of this wave's global loads (including the copies
 // into LDS) are outstanding and its LDS reads are done, then the workgroup
 // barrier; the memory clobber keeps the compiler from moving memory
-// accesses across it. Loads complete in issue order.
+// accesses across it. Vector memory loads complete in issue order.
 template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt");
@@ -84,27 +85,35 @@ __device__ __forceinline__ void wait_then_barrier() {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2_g v = {lo, hi};
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_g;
+  f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_g));
 }
 
-// The bf16 magic pattern 0x4300 in both halves as an opaque VGPR value, so
-// that (w & mask) | magic compiles to one v_and_or_b32.
-__device__ __forceinline__ uint32_t bf16_magic_pair() {
-  uint32_t m;
-  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
-  return m;
+// fp16 pairs: h(x) reinterprets a 32-bit word.
+__device__ __forceinline__ f16x2_t h2(uint32_t x) { return __builtin_bit_cast(f16x2_t, x); }
+__device__ __forceinline__ uint32_t u32(f16x2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Packed word (layout v2: the codes of k = 2i and 2i + 1 in bits 4i and
+// 4i + 16) -> the 8 exact values q - z in fp16, k ascending, as an MFMA
+// operand. c0 = -(1024 + z) and c1 = -(64 + z) in both halves.
+__device__ __forceinline__ f16x8_t dequant_f16(uint32_t w, uint32_t magic, f16x2_t c0, f16x2_t c1) {
+  const f16x2_t sixteenth = h2(0x2C002C00u);  // 1/16
+  const uint32_t t = w >> 8;
+  u32x4_t x;
+  x[0] = u32(h2((w & 0x000F000Fu) | magic) + c0);
+  x[1] = u32(__builtin_elementwise_fma(h2((w & 0x00F000F0u) | magic), sixteenth, c1));
+  x[2] = u32(h2((t & 0x000F000Fu) | magic) + c0);
+  x[3] = u32(__builtin_elementwise_fma(h2((t & 0x00F000F0u) | magic), sixteenth, c1));
+  return __builtin_bit_cast(f16x8_t, x);
 }
 
-// One packed word (8 codes, even k low / odd k high) -> 8 bf16 values 128 + q
-// in k order, as an MFMA operand.
-__device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, uint32_t magic) {
-  u32x4_t x;
-  x[0] = (w & 0x000F000Fu) | magic;
-  x[1] = ((w >> 4) & 0x000F000Fu) | magic;
-  x[2] = ((w >> 8) & 0x000F000Fu) | magic;
-  x[3] = ((w >> 12) & 0x000F000Fu) | magic;
-  return __builtin_bit_cast(bf16x8_t, x);
+// The fp16 magic pattern 0x6400 (1024.0) in both halves as an opaque VGPR
+// value, so that (w & mask) | magic is one v_and_or_b32.
+__device__ __forceinline__ uint32_t f16_magic_pair() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
 }
 
 template <typename T>
@@ -112,295 +121,437 @@ __device__ __forceinline__ T lds_read(const unsigned char *base, int off) {
   return *(const T *)(base + off);
 }
 
-// 4 waves, one per SIMD: wave w owns all 128 rows and the 32 columns
-// n0 + 32 w .. +31 of the tile (8 x 2 MFMA tiles), so a weight fragment is
-// dequantized once and feeds 8 MFMAs.
-template <int OF, bool ZP, int ST>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) unsigned char s_ring[ST * kStageBytes];
-  constexpr int FM = 8, FN = 2;
+template <int OF, bool ZP>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
+  // One LDS object for both rings: the kernel orders its copies and reads
+  // itself (waits at the top of each chunk), and with separate objects the
+  // compiler adds a wait for every copy in flight before each LDS read.
+  __shared__ __align__(16) unsigned char s_lds[kST * kStage + kSR * kSmall];
+  unsigned char *const s_ring = s_lds;
+  unsigned char *const s_small = s_lds + kST * kStage;
+  constexpr int FM = 4;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int li = lane & 15, lk = lane >> 4;
-  const int m0 = blockIdx.y * kGemmBM;
-  const int n0 = blockIdx.x * kGemmBN;
-  const int cw = 32 * wave + 2 * li;                   // this lane's 2 columns, within the tile
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // 0..7
+  const int cg = wave & 3;                                    // column group: 32 columns
+  const int kh = wave >> 2;                                   // k-steps 4 kh .. 4 kh + 3 of each chunk
+  const int j = lane & 31, h = lane >> 5;
+  // Tile order. Workgroups go to the 8 dies (XCDs, each with its own L2) in
+  // turn by launch order; without a K-split the launch order is remapped so
+  // that each die gets a compact block of tiles (up to 4 row tiles by
+  // tiles/4 columns) and its L2 serves the shared activation rows and weight
+  // columns of that block.
+  int tx = blockIdx.x, ty = blockIdx.y;
+  {
+    const int TX = gridDim.x, TY = gridDim.y, T = TX * TY;
+    if (gridDim.z == 1 && T % 8 == 0) {
+      const int L = blockIdx.x + TX * blockIdx.y;
+      const int Lx = (L & 7) * (T >> 3) + (L >> 3);   // consecutive per die
+      const int GM = TY < 4 ? TY : 4;                  // row tiles per group
+      const int per = GM * TX;
+      const int g = Lx / per, first = g * GM;
+      const int gs = TY - first < GM ? TY - first : GM;
+      const int r = Lx - g * per;
+      ty = first + r % gs;
+      tx = r / gs;
+    }
+  }
+  const int m0 = ty * kGemmBM;
+  const int n0 = tx * kGemmBN;
 
   int cb, ccount;
   split_range(a.nchunks, a.nsplit, blockIdx.z, cb, ccount);
 
   const int R = a.K / 8;
-  // activation rows past M read zeros through the range check (the row
-  // offset is in the VGPR operand; the chunk offset in the SGPR one stays
-  // inside a valid row)
+  // weight row j of the MFMA (lane j of each half) is column fj of the
+  // group's 32: the lane's output elements are then 16 adjacent columns
+  const int fj = 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
+  const int cw = 32 * cg + fj;                          // within the workgroup's 128 columns
+
+  // A copy for a chunk past the slice goes through a resource of zero size,
+  // which the buffer's range check turns into zeros without a memory
+  // access; such copies fill a stage no later chunk reads. Issue stays
+  // straight-line and every wave issues the same number of loads per chunk.
+
+  // Buffer resources. Activation rows past M read zeros through the range
+  // check (the row is in the VGPR offset; the chunk offset in the SGPR one
+  // stays inside a valid row).
   const int a_rows = a.M - m0 < kGemmBM ? a.M - m0 : kGemmBM;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.A + (size_t)m0 * a.K), (short)0, a_rows * a.K * 2, kBufWord3);
+      (void *)(a.A16 + (size_t)m0 * a.K), (short)0, a_rows * a.K * 2, kBufWord3);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.W + (size_t)(n0 / kTileCols) * R * kTileCols), (short)0, 2 * R * kTileCols * 4, kBufWord3);
   const __amdgpu_buffer_rsrc_t s_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.S, (short)0, a.nchunks * a.N * 2, kBufWord3);
-  const __amdgpu_buffer_rsrc_t q_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.asum, (short)0, a.nchunks * a.Mp * 4, kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.S32, (short)0, a.nchunks * a.Np * 4, kBufWord3);
   const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)a.Z, (short)0, ZP ? a.nchunks * (a.N >> 3) * 4 : 0, kBufWord3);
-  // Every load is issued unconditionally (straight-line code, so the
-  // compiler counts the loads in flight exactly); a load for a chunk past
-  // the slice sets the top bit of its VGPR offset, which the range check of
-  // the buffer (every resource here has at most INT_MAX bytes) turns into a
-  // zero result without a memory access. Such copies write zeros into a
-  // stage no later chunk uses.
+  const __amdgpu_buffer_rsrc_t none_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, kBufWord3);
+
+  // Activation copy c = wave + 8 tt (tt = 0..3) writes LDS bytes c KiB of the
+  // tile: row r = 32 tt + 4 wave + lane / 16, physical 16-byte slot
+  // lane % 16, holding logical piece (lane % 16) ^ (r % 16) of the row
+  // (r % 16 does not depend on tt), so the fragment reads of 16 rows hit 16
+  // different slots.
+  const int ar0 = 4 * wave + (lane >> 4);
+  const int a_voff0 = ar0 * (a.K * 2) + (((lane & 15) ^ (ar0 & 15)) << 4);
+  const int a_vstep = 32 * a.K * 2;
+  // Weight copy of wave w writes word-rows 2w, 2w + 1 of the chunk: lane ->
+  // word-row 2w + lane / 32, columns 4 (lane % 32) .. +3 of the workgroup
+  // (LDS row-major [word-row][128 columns]).
+  const int w_voff0 = ((((lane & 31) >> 4) * R) + (lane >> 5)) * 256 + (lane & 15) * 16;
+
+  auto copy_a = [&](int chunk, int stage, int tt, const __amdgpu_buffer_rsrc_t &rs) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(s_ring + stage * kStage + kAOff + (wave + 8 * tt) * 1024),
+                                             16, a_voff0 + tt * a_vstep, chunk * 256, 0, 0);
+  };
+  auto copy_w = [&](int chunk, int stage, const __amdgpu_buffer_rsrc_t &rs) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(s_ring + stage * kStage + kWOff + wave * 1024), 16,
+                                             w_voff0, chunk * 4096 + wave * 512, 0, 0);
+  };
+  // the scales (wave 0) and zero-points (wave 1, with zero-points) of a
+  // chunk; the other waves issue a copy with an out-of-range offset (every
+  // resource here has at most INT_MAX bytes) into a slot of their own, so
+  // that every wave issues the same loads per chunk with no branch in the
+  // loop (a branch here measured about 5 us slower at M = 1024)
   constexpr int kDead = (int)0x80000000u;
-
-  // activations: copy j of wave w writes LDS bytes (4j + w) KiB of the tile:
-  // pieces p = 64 (4j + w) + lane; piece p is row p/16 = 16 j + r0, physical
-  // slot p%16, holding logical 16-byte chunk (p%16) ^ (row%16) of the row
-  // (row%16 = r0%16 does not depend on j).
-  const int r0 = 4 * wave + lk;
-  const int a_voff0 = r0 * (a.K * 2) + ((lane & 15) ^ (r0 & 15)) * 16;
-  const int a_vstep = 16 * a.K * 2;          // + j rows of 16
-  // weights: per k-step s, word-row 4s + lk of the chunk and the lane's two
-  // adjacent columns (8 bytes; 16 lanes read a 128-byte row segment). MFMA
-  // column j of tile f is column n0 + 32 w + 2j + f.
-  const int b_voff = ((cw >> 6) * R * kTileCols + lk * kTileCols + (cw & 63)) * 4;
-
-  auto load_b = [&](int chunk, int s, int dead) {
-    return __builtin_bit_cast(
-        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, b_voff | dead, (chunk * 16 + 4 * s) * kTileCols * 4,
-                                                      kPolicyStream));
-  };
-  // The small copies read past their useful part and, at the last chunk,
-  // past the end of their array: those lanes rely on the buffer's range
-  // check (which returns zeros), so the whole offset is in the VGPR operand
-  // (the SGPR offset is not range-checked).
-  auto copy_small = [&](int chunk, int stage, int dead) {
-    unsigned char *st = s_ring + stage * kStageBytes;
-    if (wave == 0) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void *)(st + kSOff), 16,
-                                               ((chunk * a.N + n0) * 2 + lane * 16) | dead, 0, 0, 0);
-    } else if (wave == 1) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(q_rsrc, (lds_void *)(st + kQOff), 16,
-                                               ((chunk * a.Mp + m0) * 4 + lane * 16) | dead, 0, 0, 0);
-    } else if (ZP && wave == 2) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_void *)(st + kZOff), 4,
-                                               ((chunk * (a.N >> 3) + (n0 >> 3)) * 4 + lane * 4) | dead, 0, 0,
-                                               0);
-    }
-  };
-  auto copy_a = [&](int chunk, int stage, int j, int dead) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(s_ring + stage * kStageBytes + kAOff +
-                                                                  (4 * j + wave) * 1024),
-                                             16, (a_voff0 + j * a_vstep) | dead, chunk * kGemmKC * 2, 0, 0);
+  const __amdgpu_buffer_rsrc_t small_rsrc = wave == 0 ? s_rsrc : z_rsrc;
+  const int small_voff = wave == 0 ? n0 * 4 + lane * 16 : ((ZP && wave == 1) ? (n0 >> 3) * 4 + lane * 16 : kDead);
+  const int small_cstride = wave == 0 ? a.Np * 4 : (ZP && wave == 1 ? (a.N >> 3) * 4 : 0);
+  const int small_slot = wave * 1024;
+  auto copy_small = [&](int chunk, int sstage, const __amdgpu_buffer_rsrc_t &rs) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(s_small + sstage * kSmall + small_slot), 16,
+                                             chunk * small_cstride + small_voff, 0, 0, 0);
   };
 
-  const uint32_t magic = bf16_magic_pair();
-  const int c8 = 32 * wave + 8 * lk;                 // first of the lane's 8 output columns, within the tile
-  const int s_off = kSOff + c8 * 2;
-  const int q_off = kQOff + li * 4;                  // + 64 fm
-  const int z_off = kZOff + (c8 >> 3) * 4;
+  const uint32_t magic = f16_magic_pair();
+  f16x2_t c0 = h2(0xE408E408u), c1 = h2(0xD480D480u);  // -(1024 + 8), -(64 + 8)
 
-  f32x4_t acc[FM][FN], P[FM][FN];
+  f32x16_t acc[FM], P[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = P[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float sc[FN][4] = {};   // scales of the chunk whose sums are in P: column 2 r + fn of the lane's 8
-  u32x2_t bcur[4], bnext[4];
+    for (int e = 0; e < 16; ++e) acc[i][e] = P[i][e] = 0.f;
 
-  // Chunk i (local) lives in stage i % ST. While chunk i is computed, its
-  // MFMA sequence also issues, one piece per activation fragment, the
-  // weight loads of chunk i + 1 (first, into registers) and then the copies
-  // of chunk i + ST - 1 into the stage chunk i - 1 used: every wave has
-  // passed the barrier at the top of chunk i, so every wave is done with it.
-  // Spreading the loads keeps the compute unit's address unit from stalling
-  // every wave with one burst. With 3 stages, at the top of chunk i at most
-  // the 9 copies of chunk i + 1 may still be in flight (they were issued
-  // after the weight loads of chunk i), so vmcnt(8) covers chunk i's copies
-  // and weights on every wave (waves 0..2 also wait for their small copy,
-  // issued early); with 2 stages nothing may be (vmcnt(0)).
-  //
-  // One chunk on the MFMA units is software-pipelined with the promotion of
-  // the previous chunk: tile (fm, fn) of P is first added into acc with the
-  // previous chunk's scales, then restarted from -(128 + z) * sum(a) by the
-  // chunk's first k-step. (Without zero-points the pre-pass already stores
-  // -136 * sum(a).)
-  auto run_chunk = [&](int i) {
-    const unsigned char *sb = s_ring + (i % ST) * kStageBytes;
-    constexpr int AH = ST - 1;   // copies run AH chunks ahead
-    const int db = i + 1 < ccount ? 0 : kDead, dc = i + AH < ccount ? 0 : kDead;
-    const int cs = (i + AH) % ST;
-    const u32x4_t sv = lds_read<u32x4_t>(sb, s_off);
-    f32x4_t bias[FN] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
+  // LDS read offsets inside a stage (the stage's base is added per chunk)
+  const int s_rd = kSOff + (32 * cg + 16 * h) * 4;       // the lane's 16 scales in a small stage
+  const int w_rd = kWOff + (h * 128 + cw) * 4 + kh * 4096;  // + s * 1024: word-row 2 (4 kh + s) + h
+  int a_rd[4];                                           // k-step 4 kh + s, row tile 0; + fm * 32 rows
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a_rd[s] = kAOff + j * kARow + (((2 * (4 * kh + s) + h) ^ (j & 15)) << 4);
+
+  // The lane's 16 scales of a chunk serve 16 consecutive slots: tiles 0 and 1
+  // of the chunk (its slots 8..15) and tiles 2 and 3 (the next chunk's slots
+  // 0..7). Two register sets alternate between chunks; a chunk's set is read
+  // at its slot 2.
+  f32x4_t scA[4], scB[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) scA[u] = scB[u] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+  typedef __attribute__((address_space(3))) const f16x8_t lds_f16x8;
+  typedef __attribute__((address_space(3))) const f32x4_t lds_f32x4;
+
+  // One chunk = 16 MFMA slots of this wave's 4 k-steps. Slots 0..7 run row
+  // tiles 0 and 1 (k-step s = slot / 2; each weight word dequantized just
+  // before its first use), slots 8..15 tiles 2 and 3 with the same words.
+  // Each slot also promotes 4 elements (a quad of scales): slots 0..7 tiles
+  // 2 and 3 of the previous chunk (their products stay in P until slot 8
+  // restarts them), slots 8..15 tiles 0 and 1 of this chunk (finished at
+  // slot 7). Activation fragments are read three slots ahead; the copies of
+  // chunk i + 2 are issued between the MFMAs.
+  auto run_chunk = [&](int i, f32x4_t(&scp)[4], f32x4_t(&scc)[4]) __attribute__((always_inline)) {
+    const int sbase = (i % kST) * kStage;
+    const unsigned char *sm = s_small + (i % kSR) * kSmall;
+    const bool live = i + 2 < ccount;
+    const __amdgpu_buffer_rsrc_t ar = live ? a_rsrc : none_rsrc, wr = live ? w_rsrc : none_rsrc,
+                                 sr = live ? small_rsrc : none_rsrc;
+    const int cn = cb + i + 2, stn = (i + 2) % kST;
     if constexpr (ZP) {
-      const uint32_t zw = lds_read<uint32_t>(sb, z_off);
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bias[fn][r] = -(float)(128 + (int)((zw >> (4 * (2 * r + fn))) & 0xFu));
+      const uint32_t zw = *(const uint32_t *)(sm + kZOff + (cw >> 3) * 4);
+      const uint32_t z = (zw >> (4 * (cw & 7))) & 0xFu;
+      const uint32_t zz = z | (z << 16);
+      c0 = h2(0xE400E400u | zz);          // -(1024 + z)
+      c1 = h2(0xD400D400u | (zz << 4));   // -(64 + z)
     }
-    // The 32 activation fragments of the chunk (k-step s, row tile fm) are
-    // read from LDS two fragments ahead of their MFMAs.
-    auto a_frag = [&](int q) {
-      const int s = q / FM, fm = q % FM;
-      return lds_read<bf16x8_t>(sb, kAOff + (16 * fm + li) * kARow + 16 * ((4 * s + lk) ^ li));
+    // Per-chunk base addresses, made opaque to the compiler so that the
+    // constant parts (row tile, k-step, quad) stay in the LDS instructions'
+    // offset fields instead of being hoisted into extra registers and added
+    // at every read.
+    uint32_t ab[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      ab[s] = (uint32_t)(uintptr_t)(s_ring + sbase) + a_rd[s];
+      asm volatile("" : "+v"(ab[s]));
+    }
+    uint32_t wb = (uint32_t)(uintptr_t)(s_ring + sbase) + w_rd;
+    uint32_t qm = (uint32_t)(uintptr_t)sm + s_rd;
+    asm volatile("" : "+v"(wb), "+v"(qm));
+    uint32_t wraw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) wraw[s] = *(lds_u32 *)(wb + s * 1024);
+    auto frag = [&](int q) {
+      const int half = q >> 3, s = (q & 7) >> 1, fm = 2 * half + (q & 1);
+      return *(lds_f16x8 *)(ab[s] + fm * 32 * kARow);
     };
-    bf16x8_t af[3];
-    af[0] = a_frag(0);
-    af[1] = a_frag(1);
-    bf16x8_t bfr[FN];
+    f16x8_t af[4];
+    af[0] = frag(0);
+    af[1] = frag(1);
+    af[2] = frag(2);
+
+    f16x8_t wq[4];
 #pragma unroll
-    for (int q = 0; q < 4 * FM; ++q) {
-      const int s = q / FM, fm = q % FM;
-      if (q + 2 < 4 * FM) af[(q + 2) % 3] = a_frag(q + 2);
-      // loads for later chunks, one piece per fragment
-      if (q < 4)
-        bnext[q] = load_b(cb + i + 1, q, db);
-      else if (q == 4)
-        copy_small(cb + i + AH, cs, dc);
-      else if (q >= 6 && (q - 6) % 3 == 0 && (q - 6) / 3 < 8)
-        copy_a(cb + i + AH, cs, (q - 6) / 3, dc);
-      if (fm == 0) {
+    for (int q = 0; q < 16; ++q) {
+      const int half = q >> 3, s = (q & 7) >> 1, fm = 2 * half + (q & 1);
+      if (q + 3 < 16) af[(q + 3) & 3] = frag(q + 3);
+      if (q == 2) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) bfr[fn] = dequant_word(bcur[s][fn], magic);
+        for (int u = 0; u < 4; ++u) scc[u] = *(lds_f32x4 *)(qm + u * 16);
       }
-      const bf16x8_t afr = af[q % 3];
-      float rs = 0.f;
-      if (s == 0) rs = lds_read<float>(sb, q_off + 64 * fm);
+      if (half == 0 && (q & 1) == 0) wq[s] = dequant_f16(wraw[s], magic, c0, c1);
+      if (s == 0)
+        P[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wq[s], af[q & 3], (f32x16_t){}, 0, 0, 0);
+      else
+        P[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wq[s], af[q & 3], P[fm], 0, 0, 0);
+      {
+        const int r = q & 7;                        // slot within the half
+        const int tt = half == 0 ? 2 + (r >> 2) : (r >> 2);
+        const int e0 = 4 * (r & 3);
+        const f32x4_t sc = half == 0 ? scp[r & 3] : scc[r & 3];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        if (s == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(sc[fn][r], P[fm][fn][r], acc[fm][fn][r]);
-          const f32x4_t init = ZP ? rs * bias[fn] : (f32x4_t){rs, rs, rs, rs};
-          P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr, init, 0, 0, 0);
-        } else {
-          P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], afr, P[fm][fn], 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e) acc[tt][e0 + e] = __builtin_fmaf(sc[e], P[tt][e0 + e], acc[tt][e0 + e]);
       }
+      // copies of chunk i + 2 (small first), spread over the MFMAs
+      if (q == 1) copy_small(cn, (i + 2) % kSR, sr);
+      if (q == 3 || q == 6 || q == 9 || q == 12) copy_a(cn, stn, q / 3 - 1, ar);
+      if (q == 14) copy_w(cn, stn, wr);
+      // keep the slots in this order (the scheduler would otherwise hoist
+      // the fragment reads of many slots and run out of registers)
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[0][r] = __uint_as_float(sv[r] << 16);
-      sc[1][r] = __uint_as_float(sv[r] & 0xFFFF0000u);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) bcur[s] = bnext[s];
   };
 
-  // prologue: copies of chunk 0, weights of chunk 0, copies of chunk 1
+  // prologue: the copies of chunks 0 and 1, each chunk's small copy first
+  // (the waits count on that: at the top of chunk i at most the 5 main
+  // copies of chunk i + 1 may be in flight)
   {
-    const int d0 = ccount > 0 ? 0 : kDead, d1 = ccount > 1 ? 0 : kDead;
-    copy_small(cb, 0, d0);
+    const __amdgpu_buffer_rsrc_t r0a = ccount > 0 ? a_rsrc : none_rsrc, r0w = ccount > 0 ? w_rsrc : none_rsrc,
+                                 r0s = ccount > 0 ? small_rsrc : none_rsrc;
+    const __amdgpu_buffer_rsrc_t r1a = ccount > 1 ? a_rsrc : none_rsrc, r1w = ccount > 1 ? w_rsrc : none_rsrc,
+                                 r1s = ccount > 1 ? small_rsrc : none_rsrc;
+    copy_small(cb, 0, r0s);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) copy_a(cb, 0, j, d0);
+    for (int tt = 0; tt < 4; ++tt) copy_a(cb, 0, tt, r0a);
+    copy_w(cb, 0, r0w);
+    copy_small(cb + 1, 1, r1s);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bcur[s] = load_b(cb, s, d0);
-    if constexpr (ST == 3) {
-      copy_small(cb + 1, 1, d1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) copy_a(cb + 1, 1, j, d1);
-    }
+    for (int tt = 0; tt < 4; ++tt) copy_a(cb + 1, 1, tt, r1a);
+    copy_w(cb + 1, 1, r1w);
   }
-  for (int i = 0; i < ccount; ++i) {
-    wait_then_barrier<ST == 3 ? 8 : 0>();
-    run_chunk(i);
+  // chunk 0 promotes the zero products of a "previous chunk" with zero scales
+  int i = 0;
+  for (; i + 1 < ccount; i += 2) {
+    wait_then_barrier<5>();
+    run_chunk(i, scB, scA);
+    wait_then_barrier<5>();
+    run_chunk(i + 1, scA, scB);
   }
+  if (i < ccount) {
+    wait_then_barrier<5>();
+    run_chunk(i, scB, scA);
+  }
+  // the last chunk's tiles 2 and 3 (tiles 0 and 1 were promoted inside it),
+  // with that chunk's scales (set A after an odd count, else set B)
+  {
+    const bool odd = (ccount & 1) != 0;
+#pragma unroll
+    for (int fm = 2; fm < FM; ++fm)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4_t sc = odd ? scA[e4] : scB[e4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[fm][4 * e4 + e] = __builtin_fmaf(sc[e], P[fm][4 * e4 + e], acc[fm][4 * e4 + e]);
+      }
+  }
+  // The two waves of a column group hold partial sums over complementary
+  // k-steps: the second writes its accumulators to LDS (the ring is free
+  // now), the first adds them (first + second, a fixed order).
+  __syncthreads();
+  float *s_red = (float *)s_lds + (size_t)cg * (FM * 16 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *(f32x4_t *)(s_red + ((fm * 4 + e4) * 64 + lane) * 4) =
+            (f32x4_t){acc[fm][4 * e4], acc[fm][4 * e4 + 1], acc[fm][4 * e4 + 2], acc[fm][4 * e4 + 3]};
+  }
+  __syncthreads();
+  if (kh == 1) return;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4_t o = *(const f32x4_t *)(s_red + ((fm * 4 + e4) * 64 + lane) * 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[fm][fn][q] = __builtin_fmaf(sc[fn][q], P[fm][fn][q], acc[fm][fn][q]);
+      for (int e = 0; e < 4; ++e) acc[fm][4 * e4 + e] = acc[fm][4 * e4 + e] + o[e];
+    }
 
-  // ---- epilogue: row m0 + 16 fm + li, columns n0 + c8 .. +7 (element (fn, r) is column 2 r + fn) ----
-  const int n8 = n0 + c8;
+  // ---- epilogue: row m0 + 32 fm + j, columns n0 + 32 cg + 16 h .. +15 ----
+  const int n16 = n0 + 32 * cg + 16 * h;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const int row = m0 + 16 * fm + li;
+    const int row = m0 + 32 * fm + j;
     if (row >= a.M) continue;
-    const f32x4_t lo = {acc[fm][0][0], acc[fm][1][0], acc[fm][0][1], acc[fm][1][1]};
-    const f32x4_t hi = {acc[fm][0][2], acc[fm][1][2], acc[fm][0][3], acc[fm][1][3]};
+    const int e = a.rexp[row];
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = __builtin_amdgcn_ldexpf(acc[fm][q], -e);
     if (a.nsplit > 1) {
       // K-slice partials; a second kernel adds them in the order z = 0..nsplit-1
-      float *p = &a.partial[((size_t)blockIdx.z * a.M + row) * a.Np + n8];
-      *(f32x4_t *)p = lo;
-      *(f32x4_t *)(p + 4) = hi;
+      float *p = &a.partial[((size_t)blockIdx.z * a.M + row) * a.Np + n16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *(f32x4_t *)(p + 4 * q) = (f32x4_t){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
       continue;
     }
-    if (n8 >= a.N) continue;   // N % 8 == 0: the lane's 8 columns are all in or all out
-    const size_t o = (size_t)row * a.N + n8;
-    if constexpr (OF == O_BF16) {
-      *(u32x4_t *)((uint16_t *)a.out + o) = (u32x4_t){pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                                                      pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
-    } else {
-      *(f32x4_t *)((float *)a.out + o) = lo;
-      *(f32x4_t *)((float *)a.out + o + 4) = hi;
+    // N % 8 == 0: each half of the lane's 16 columns is all in or all out
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int n = n16 + 8 * half;
+      if (n >= a.N) continue;
+      const size_t o = (size_t)row * a.N + n;
+      const float *x = v + 8 * half;
+      if constexpr (OF == O_BF16) {
+        *(u32x4_t *)((uint16_t *)a.out + o) = (u32x4_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                        pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+      } else {
+        *(f32x4_t *)((float *)a.out + o) = (f32x4_t){x[0], x[1], x[2], x[3]};
+        *(f32x4_t *)((float *)a.out + o + 4) = (f32x4_t){x[4], x[5], x[6], x[7]};
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Activation sums: asum[g][m] = mult * sum_{k in group g} a[m][k] (groups of
-// 128), for m < M; row stride Mp. One wave per row: lane l reads 16 bytes of each
-// 1 KiB block of the row (block j covers groups 4j .. 4j+3; lanes 16i .. 16i+15
-// hold group 4j + i), adds its 8 values in k order, and the 16 lanes of a
-// group (one DPP row) combine in a fixed order of row rotations. Up to 8
-// blocks are loaded before any is added, so every lane keeps 8 loads in
-// flight.
+// Pre-pass. Blocks [0, ceil(M / 4)): one wave per row m: e(m) = 141 - E,
+// with E the biased exponent of the row's largest |a| (so that the largest
+// scaled magnitude lies in [2^14, 2^15)), and A16[m][k] = fp16(a * 2^e(m))
+// (round to nearest even; exact unless the scaled value is below 2^-14).
+// Blocks past those: scales S32[g][n] = float(S[g][n]) for n < N, 0 for
+// N <= n < Np (8 per thread).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void asum_kernel(const uint16_t *__restrict__ A, float *__restrict__ asum, int M,
-                                                  int K, int Mp, float mult) {
+template <int PPL>  // 16-byte pieces per lane held in registers (K <= 512 PPL); 0: two passes
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ A, uint16_t *__restrict__ A16,
+                                                   int *__restrict__ rexp, const uint16_t *__restrict__ S,
+                                                   float *__restrict__ S32, int M, int K, int N, int Np,
+                                                   int ngroups, int row_blocks) {
   const int lane = threadIdx.x & 63;
+  if ((int)blockIdx.x >= row_blocks) {
+    const long long idx = ((long long)(blockIdx.x - row_blocks) * 256 + threadIdx.x) * 8;
+    if (idx >= (long long)ngroups * Np) return;
+    const int g = (int)(idx / Np), n = (int)(idx % Np);
+    u32x4_t v = {0, 0, 0, 0};
+    if (n < N) v = *(const u32x4_t *)(S + (size_t)g * N + n);
+    f32x4_t lo = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                  __uint_as_float(v[1] & 0xFFFF0000u)};
+    f32x4_t hi = {__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xFFFF0000u), __uint_as_float(v[3] << 16),
+                  __uint_as_float(v[3] & 0xFFFF0000u)};
+    *(f32x4_t *)(S32 + idx) = lo;
+    *(f32x4_t *)(S32 + idx + 4) = hi;
+    return;
+  }
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
-  const int ngroups = K / 128;
-  const int nblocks = (ngroups + 3) / 4;
-  const uint16_t *row = A + (size_t)m * K;
-  for (int j0 = 0; j0 < nblocks; j0 += 8) {
-    u32x4_t v[8];
+  const int pieces = K / 8;  // 16-byte pieces of the row
+  const u32x4_t *src = (const u32x4_t *)(A + (size_t)m * K);
+  u32x4_t *dst = (u32x4_t *)(A16 + (size_t)m * K);
+  // largest magnitude: bf16 magnitudes compare as integers
+  auto mag = [](const u32x4_t &x) {
+    uint32_t r = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      // past the row's last group: re-read its first piece (in bounds), unused
-      const int g = 4 * (j0 + u) + (lane >> 4);
-      const int off = g < ngroups ? g * 128 + 8 * (lane & 15) : 0;
-      v[u] = *(const u32x4_t *)(row + off);
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t lo = x[c] & 0x7FFFu, hi = (x[c] >> 16) & 0x7FFFu;
+      r = r > lo ? r : lo;
+      r = r > hi ? r : hi;
+    }
+    return r;
+  };
+  u32x4_t v[PPL > 0 ? PPL : 1];
+  uint32_t mb = 0;
+  if constexpr (PPL > 0) {
+    // pieces past the row re-read the row's last piece (in bounds; the
+    // maximum is unchanged and nothing is stored for them)
+#pragma unroll
+    for (int u = 0; u < PPL; ++u) {
+      const int p = lane + 64 * u;
+      v[u] = src[p < pieces ? p : pieces - 1];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int g = 4 * (j0 + u) + (lane >> 4);
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        s += __uint_as_float(v[u][q] << 16);
-        s += __uint_as_float(v[u][q] & 0xFFFF0000u);
-      }
-      // fixed-order sum over the 16 lanes of the group with DPP row rotations
-      // (lane 0 of the row ends with ((s0 + s8) + (s4 + s12)) + ...)
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x128, 0xF, 0xF, false));  // row_ror:8
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x124, 0xF, 0xF, false));  // row_ror:4
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x122, 0xF, 0xF, false));  // row_ror:2
-      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x121, 0xF, 0xF, false));  // row_ror:1
-      if (g < ngroups && (lane & 15) == 0) asum[(size_t)g * Mp + m] = s * mult;
+    for (int u = 0; u < PPL; ++u) {
+      const uint32_t x = mag(v[u]);
+      mb = mb > x ? mb : x;
     }
+  } else {
+    for (int p = lane; p < pieces; p += 64) {
+      const uint32_t x = mag(src[p]);
+      mb = mb > x ? mb : x;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = (uint32_t)__shfl_xor((int)mb, o);
+    mb = mb > y ? mb : y;
+  }
+  const int e = 141 - (int)(mb >> 7);  // bf16 exponent field: bits 14..7 of the magnitude
+  if (lane == 0) rexp[m] = e;
+  auto convert = [&](const u32x4_t &x) {
+    u32x4_t r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f32x2_t f = {__builtin_amdgcn_ldexpf(__uint_as_float(x[c] << 16), e),
+                   __builtin_amdgcn_ldexpf(__uint_as_float(x[c] & 0xFFFF0000u), e)};
+      r[c] = u32(__builtin_convertvector(f, f16x2_t));
+    }
+    return r;
+  };
+  if constexpr (PPL > 0) {
+#pragma unroll
+    for (int u = 0; u < PPL; ++u) {
+      const int p = lane + 64 * u;
+      if (p < pieces) dst[p] = convert(v[u]);
+    }
+  } else {
+    for (int p = lane; p < pieces; p += 64) dst[p] = convert(src[p]);
   }
 }
 
 template <int OF, bool ZP>
 static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
-  if (a.stages == 2)
-    gemm_kernel<OF, ZP, 2><<<grid, kGemmThreads, 0, st>>>(a);
-  else
-    gemm_kernel<OF, ZP, 3><<<grid, kGemmThreads, 0, st>>>(a);
+  gemm_kernel<OF, ZP><<<grid, kGemmThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-// The dispatcher sends only G == 128, K % 128 == 0, N % 8 == 0 here.
-hipError_t launch_gemm(int ofmt, bool zp, int G, const GemmArgs &a, dim3 grid, hipStream_t st) {
-  if (G != 128 || a.K % kGemmKC != 0 || a.N % 8 != 0) return hipErrorInvalidValue;
-  // without zero-points the MFMA starts from -(128 + 8) * sum(a): store that
-  asum_kernel<<<(a.M + 3) / 4, 256, 0, st>>>(a.A, a.asum, a.M, a.K, a.Mp, zp ? 1.f : -136.f);
+// The dispatcher sends only K % 128 == 0, N % 8 == 0 here, with
+// M * K * 2 <= INT_MAX and (K / 128) * Np * 4 <= INT_MAX.
+hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStream_t st) {
+  if (a.K % kGemmKC != 0 || a.N % 8 != 0) return hipErrorInvalidValue;
+  const int row_blocks = (a.M + 3) / 4;
+  const long long sblocks = ((long long)a.nchunks * a.Np / 8 + 255) / 256;
+  const dim3 pgrid((unsigned)(row_blocks + sblocks));
+  const int ppl = (a.K / 8 + 63) / 64;  // pieces per lane
+#define QG_PREP(P) \
+  prep_kernel<P><<<pgrid, 256, 0, st>>>(a.A, a.A16, a.rexp, a.S, a.S32, a.M, a.K, a.N, a.Np, a.nchunks, row_blocks)
+  if (ppl <= 2)
+    QG_PREP(2);
+  else if (ppl <= 4)
+    QG_PREP(4);
+  else if (ppl <= 8)
+    QG_PREP(8);
+  else if (ppl <= 16)
+    QG_PREP(16);
+  else
+    QG_PREP(0);
+#undef QG_PREP
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ofmt == O_BF16) return zp ? go<O_BF16, true>(a, grid, st) : go<O_BF16, false>(a, grid, st);

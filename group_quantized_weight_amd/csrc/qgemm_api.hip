@@ -102,20 +102,17 @@ struct Plan {
   bool dq_fused = false;  // precisions 7, 8: quantized in the GEMV's prologue, or
   size_t codes = 0;       //   by a pre-pass into the workspace: bytes of int8 codes,
   size_t ascale = 0;      //   then of their float32 scales, at its start
-  size_t asum = 0;        // MFMA path: bytes of activation sums (after the above)
-  int stages = 3;         // MFMA path: LDS ring depth
+  size_t prep = 0;        // MFMA path: bytes of the pre-pass's outputs (after the above)
   size_t ws = 0;
 };
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-size_t padded_rows(int M) { return ((size_t)M + kGemmBM - 1) / kGemmBM * kGemmBM; }
-
-// MFMA path: float32 activation sums [K/128][Mp], rounded up to 256 bytes.
-size_t gemm_asum_bytes(int M, int K) {
-  const size_t b = (size_t)(K / kGemmKC) * padded_rows(M) * 4;
-  return (b + 255) / 256 * 256;
-}
+// MFMA path: the pre-pass's fp16 activations [M][K], row exponents [M] and
+// float32 scales [K/128][Np], each rounded up to 256 bytes.
+size_t gemm_a16_bytes(int M, int K) { return round256((size_t)M * K * 2); }
+size_t gemm_rexp_bytes(int M) { return round256((size_t)M * 4); }
+size_t gemm_s32_bytes(int N, int K) { return round256((size_t)(K / kGemmKC) * padded_cols(N) * 4); }
 
 size_t gemv_lds(const Formats &f, int mb, int G, int ngroups, int nsplit) {
   const int kpw = f.w == W4 ? 8 : 4;
@@ -140,7 +137,8 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
   const int cus = device_cus();
   const size_t Np = padded_cols(N);
   const bool gemm_ok = f.a == A_BF16 && G == 128 && K % kGemmKC == 0 && N % 8 == 0 && M <= 65535 &&
-                       gemm_asum_bytes(M, K) <= (size_t)INT_MAX;
+                       (size_t)M * K * 2 <= (size_t)INT_MAX &&
+                       (size_t)(K / kGemmKC) * Np * 4 <= (size_t)INT_MAX;
   // int8 activations (given, or quantized by the pre-pass) take the integer
   // MFMA kernel from kSmallI8MinM rows on
   const bool small_i8 = f.a == A_I8;
@@ -220,10 +218,7 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
     p.lds = gemv_lds(f, p.mb, G, p.units, ns);
   }
   p.nsplit = ns;
-  // the tiled GEMM's ring: 2 stages, so that two workgroups share a compute
-  // unit, once there are at least two workgroups per compute unit
-  p.stages = base * ns >= 2LL * cus ? 2 : 3;
-  p.asum = path == QG_PATH_GEMM ? gemm_asum_bytes(M, K) : 0;
+  p.prep = path == QG_PATH_GEMM ? gemm_a16_bytes(M, K) + gemm_rexp_bytes(M) + gemm_s32_bytes(N, K) : 0;
   if (f.dq) {
     // Each workgroup quantizes the rows and groups it stages; that repeats
     // the work once per column tile, so beyond a few rows one pre-pass that
@@ -236,7 +231,7 @@ int make_plan(int M, int N, int K, int G, const Formats &f, int force_path, int 
       p.ascale = round256((size_t)M * (K / G) * 4);
     }
   }
-  p.ws = p.codes + p.ascale + p.asum + (p.nsplit > 1 ? (size_t)p.nsplit * M * Np * 4 : 0);
+  p.ws = p.codes + p.ascale + p.prep + (p.nsplit > 1 ? (size_t)p.nsplit * M * Np * 4 : 0);
   return QG_OK;
 }
 
@@ -330,7 +325,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
   }
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
-  float *partial = p.nsplit > 1 ? (float *)(ws + p.codes + p.ascale + p.asum) : nullptr;
+  float *partial = p.nsplit > 1 ? (float *)(ws + p.codes + p.ascale + p.prep) : nullptr;
   const int Np = (int)padded_cols(N);
   drop_pending_error();
   hipError_t e = hipSuccess;
@@ -388,12 +383,14 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.Z = has_zp ? (const uint32_t *)zeros : nullptr;
     a.out = out;
     a.partial = partial;
-    a.asum = (float *)(ws + p.codes + p.ascale);
-    a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np; a.Mp = (int)padded_rows(M);
+    char *pp = ws + p.codes + p.ascale;
+    a.A16 = (uint16_t *)pp;
+    a.rexp = (int *)(pp + gemm_a16_bytes(M, K));
+    a.S32 = (float *)(pp + gemm_a16_bytes(M, K) + gemm_rexp_bytes(M));
+    a.M = M; a.N = N; a.K = K; a.Np = Np;
     a.nchunks = K / kGemmKC;
     a.nsplit = p.nsplit;
-    a.stages = p.stages;
-    e = launch_gemm(f.o, has_zp != 0, group, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), s);
+    e = launch_gemm(f.o, has_zp != 0, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), s);
   }
   if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, partial, out, M, N, Np, p.nsplit, s);
   return e == hipSuccess ? QG_OK : QG_EHIP;

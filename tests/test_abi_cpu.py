@@ -314,9 +314,10 @@ def test_plan_is_pure_and_consistent(M, N, K, G, prec):
     if path in (qg.PATH_GEMV, qg.PATH_SMALL):
         assert (ws == 0) == (ns == 1)
         assert ws == (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)
-    else:  # activation sums [K/128][M rounded up to 128] float32, then the split partials
-        asum = -(-(K // 128) * (-(-M // 128) * 128) * 4 // 256) * 256
-        assert ws == asum + (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)
+    else:  # fp16 activations [M][K], row exponents [M], float32 scales [K/128][Np], then the split partials
+        r256 = lambda b: -(-b // 256) * 256
+        prep = r256(M * K * 2) + r256(M * 4) + r256((K // 128) * qg.padded_cols(N) * 4)
+        assert ws == prep + (ns * M * qg.padded_cols(N) * 4 if ns > 1 else 0)
     if prec in (1, 6) and G == 128 and N % 8 == 0 and 2 <= M <= 64:
         assert path == qg.PATH_SMALL
     elif prec in (1, 6) and M > 64:

@@ -347,3 +347,41 @@ def make_config(name: str, M: Optional[int] = None) -> Problem:
     if M is not None:
         c["M"] = M
     return make_problem(name=name, **c)
+
+
+def set_degenerate_columns(p: Problem, zero_cols, near_cols, seed: int) -> Problem:
+    """Input structure for the cancellation cases: in ``zero_cols`` every
+    code equals its column's zero-point (a pruned or padded channel, so the
+    column of w_hat is exactly zero), and in ``near_cols`` every code is
+    within one step of it (uniform in {z-1, z, z+1}, kept in the code range).
+    The zero-point is the stored nibble with zero-points, 8 for int4 without,
+    and 0 for int8 codes. Modifies ``p.W`` in place and returns ``p``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    K, N, G = p.K, p.N, p.G
+    if p.wfmt == "w4":
+        codes = np.zeros((K, N), dtype=np.int64)
+        for j in range(8):
+            codes[j::8, :] = (p.W >> np.uint32(4 * j)) & np.uint32(0xF)
+        if p.Z is not None:
+            zn = np.zeros((K // G, ((N + 7) // 8) * 8), dtype=np.int64)
+            for j in range(8):
+                zn[:, j::8] = (p.Z >> np.uint32(4 * j)) & np.uint32(0xF)
+            zk = np.repeat(zn[:, :N], G, axis=0)
+        else:
+            zk = np.full((K, N), 8, dtype=np.int64)
+        lo, hi = 0, 15
+    else:
+        codes = p.W.astype(np.int64)
+        zk = np.zeros((K, N), dtype=np.int64)
+        lo, hi = -127, 127
+    zc = list(zero_cols)
+    nc = list(near_cols)
+    codes[:, zc] = zk[:, zc]
+    if nc:
+        d = rng.integers(-1, 2, size=(K, len(nc)))
+        codes[:, nc] = np.clip(zk[:, nc] + d, lo, hi)
+    if p.wfmt == "w4":
+        p.W = pack_w4(codes.astype(np.uint8))
+    else:
+        p.W = codes.astype(np.int8)
+    return p

@@ -405,6 +405,32 @@ def stream_read_context(steps=20, warmup=5):
     return res
 
 
+def stream_ceiling(nbytes, steps, warmup, mode):
+    """The in-tree plain streaming-read kernel (qgemm_stream_read) over the
+    same byte count as a workload, rotated over copies like the weights, and
+    timed the same way: the achievable HBM read rate for that size on this
+    box. Several workgroup counts are tried; the fastest is reported."""
+    import torch
+    import group_quantized_weight_amd as qg
+    nbytes = nbytes // 16 * 16
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / nbytes)))
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(i + 1) for i in range(copies)]
+    best = None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for blocks in (cus, 2 * cus, 4 * cus):
+        out = torch.empty(4 * blocks, dtype=torch.int32, device="cuda")
+        ms = time_steps(lambda i: qg.stream_read(bufs[i % copies], nbytes, out, blocks), steps, warmup, mode)
+        if best is None or ms < best[0]:
+            best = (ms, blocks)
+    del bufs
+    torch.cuda.empty_cache()
+    ms, blocks = best
+    return {"bytes": nbytes, "us": round(ms * 1e3, 3), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "blocks": blocks, "copies": copies,
+            "how": "qgemm_stream_read: a plain streaming-read kernel of this library, same byte count and "
+                   "timing as the workload, weights rotated the same way"}
+
+
 def cpu_baseline(p, seconds=10.0):
     import numpy as np
     import oracle
@@ -503,6 +529,9 @@ def bench(args):
     if args.copy_mib:
         copy_calibration(args.copy_mib, args.steps, args.warmup)
         return
+    if args.only and args.only.startswith("stream:"):
+        log(json.dumps(stream_ceiling(int(args.only.split(":")[1]), args.steps, args.warmup, args.mode)))
+        return
     if args.only:
         import workloads as wl
         if args.only in wl.FP8_CONFIGS:
@@ -520,6 +549,9 @@ def bench(args):
     # the first measurement of a fresh process meets an idle device: settle longer
     head, p = run_workload(args.workload, args.steps, args.warmup, args.mode, settle=HEAD_SETTLE_S)
     log(f"bench: {args.workload}: {head['ms'] * 1e3:.2f} us/step, {head['gbs']:.0f} GB/s")
+    ceiling = stream_ceiling(head["bytes"], args.steps, args.warmup, args.mode)
+    log(f"bench: plain streaming read of the same {ceiling['bytes']} bytes: {ceiling['us']} us, "
+        f"{ceiling['gbs']} GB/s ({ceiling['blocks']} workgroups)")
 
     # long enough runs (milliseconds) that the clocks have settled under MFMA load
     gemm, _ = run_workload("prefill_w4a16_m1024", max(200, args.steps), max(20, args.warmup), args.mode)
@@ -583,7 +615,10 @@ def bench(args):
                    "group": head["group"], "prec": "W4_A_BF16", "path": head["path"], "nsplit": head["nsplit"],
                    "weight_copies_rotated": head["copies"], "timing": args.mode},
         "roofline": {"bound": "hbm", "achieved": round(head["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "frac": round(head["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "stream_ceiling_gbs": ceiling["gbs"],
+                     "frac_of_stream_ceiling": round(head["gbs"] / ceiling["gbs"], 4)},
+        "stream_ceiling": ceiling,
         "per_call_us": head["per_call_us"],
         "gemm_m1024": {"workload": "prefill_w4a16_m1024", "us": round(gemm["ms"] * 1e3, 2),
                        "tflops": round(gemm["tflops"], 2), "peak_tflops": BF16_PEAK_TFLOPS,

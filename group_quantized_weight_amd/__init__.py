@@ -100,6 +100,8 @@ def lib():
             L.qgemm_dequantize.argtypes = [vp, vp, vp] + [c_int] * 5 + [vp, vp]
             L.qgemm_strerror.restype = ctypes.c_char_p
             L.qgemm_strerror.argtypes = [c_int]
+            L.qgemm_stream_read.restype = c_int
+            L.qgemm_stream_read.argtypes = [vp, c_size, vp, c_int, vp]
             _lib = L
     return _lib
 
@@ -203,6 +205,15 @@ def dequantize(w_packed, scales, K: int, N: int, G: int, prec: int = W4_A_BF16, 
     if st != OK:
         raise QGemmError(st, "qgemm_dequantize")
     return out
+
+
+def stream_read(buf, nbytes: int, out, blocks: int, stream=None):
+    """Plain streaming read of the first nbytes of buf (a measurement aid; see
+    include/qgemm.h); out (int32, at least 4 * blocks elements) is written."""
+    st = lib().qgemm_stream_read(_ptr(buf), int(nbytes), _ptr(out), int(blocks),
+                                 stream if stream is not None else _stream(buf.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_stream_read")
 
 
 def quantize_activations(A, G: int, Aq=None, a_scales=None, stream=None):

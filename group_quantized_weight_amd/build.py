@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemm.so")
 SOURCES = ["qgemm_api.hip", "pack.hip", "gemv.hip", "gemv_i8.hip", "gemm.hip", "gemm_small.hip",
            "reduce.hip", "quant.hip", "fp8.hip", "moe.hip", "dequant.hip",
-           "gemm_small_i8.hip"]
+           "gemm_small_i8.hip", "stream.hip"]
 ARCH = "gfx950"
 
 

@@ -131,6 +131,9 @@ hipError_t launch_gemm_small_i8(int wfmt, bool zp, int mb, const SmallI8Args &a,
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
                            const float *w_scale, uint16_t *out, float *partial, int M, int N, int K, int nsplit,
                            int Np, int cus, hipStream_t stream);
+// plain streaming read of `bytes` (a multiple of 16, below 2^31) by `blocks`
+// workgroups; out[4 * block + wave] receives an XOR of the data
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *out, int blocks, hipStream_t st);
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t stream);

@@ -1,7 +1,9 @@
 // GEMV path of the group-quantized GEMM: vector-ALU kernel for small M with
 // bf16 or float32 activations (int8 activations have their own kernel).
 //
-// Mapping (one workgroup = 4 waves = one 64-column tile of the packed layout):
+// Mapping (one workgroup = 4 waves = one 64-column tile of the packed layout;
+// blocks of 56 columns, which give N = 28672 two blocks per compute unit
+// instead of 1.75 tiles, measured 10% slower at M = 1 on MI355X):
 //   lane l       : columns 4 (l % 16) .. +3 of the tile and word-rows
 //                  r = l / 16 (mod 4) of its wave's K range; one 16-byte load
 //                  per lane per 4 rows, so each wave load reads 1 KiB of
@@ -20,20 +22,26 @@
 //                  the fixed order z = 0..nsplit-1.
 //
 // Per group, output element and lane the kernel forms the dot product of the
-// activations with a biased integer code and removes the bias with the sum
-// of the same activations:
-//   sum_k a_k (q_k - z) = sum_k a_k (b + q_k) - (b + z) * sum_k a_k
-// where b is the bias the dequant trick leaves in the code:
-//   bf16 activations: (b + q) is the bf16 value of pattern 0x4300 | q, i.e.
-//     128 + q (the bf16 magic number of the page "quantization-and-fused-kernels"
-//     (arganzheng.life), section 二.4); two codes are placed per 32-bit word by
-//     one and-or, then v_dot2_f32_bf16 multiplies two pairs and accumulates in
-//     float32.
-//   float32 activations: codes are split into bytes and converted with
-//     v_cvt_f32_ubyte (b = 0 for int4; b = 128 for int8 codes flipped to
-//     unsigned by xor 0x80).
-// Then acc += s[g,n] * dot in float32 (the per-group scale of the teaching
-// GEMV, arganzheng.life section 九.4).
+// activations with the exact integers q - z and then applies the group's
+// scale, acc += s[g,n] * sum_k a_k (q_k - z) in float32 (the per-group scale
+// of the teaching GEMV, arganzheng.life section 九.4). No biased sum is formed
+// and no bias is removed afterwards, so a column whose codes all equal its
+// zero-point gives exactly zero.
+//   bf16 activations: the workgroup stages its rows' activations into LDS as
+//     fp16, each row scaled by a power of two 2^e chosen from the row's
+//     largest magnitude over the workgroup's K-slice (its largest scaled
+//     magnitude lies in [2^14, 2^15): exact for every bf16 value down to
+//     2^-14 scaled, that is 2^28 below the row's maximum). Each packed word
+//     becomes four fp16 pairs q - z: the codes are placed into the mantissa
+//     of 1024.0 (0x6400 | q, or 0x6400 | 16 q for the codes one nibble
+//     higher; the fp16 magic number of the page "quantization-and-fused-kernels"
+//     (arganzheng.life), section 二.4) and one packed fp16 add or fma per pair
+//     subtracts 1024 + z (or scales by 1/16 and subtracts 64 + z), all exact.
+//     v_dot2_f32_f16 multiplies two pairs (exact products) and accumulates in
+//     float32; the row's result is multiplied by 2^-e at the end.
+//   float32 activations: codes are converted with v_cvt_f32_ubyte (int4) and
+//     z subtracted in float32, or sign-extended from their byte (int8 codes),
+//     both exact; then float32 FMAs.
 //
 // Reduction: the 4 lanes of a column and then the waves are added in a
 // fixed order (lane shuffles, then LDS), so results are reproducible.
@@ -44,9 +52,10 @@
 // the current one.
 //
 // Latency: each thread issues its activation loads first and its first batch
-// of weight loads next, then writes the activations to LDS; since vector
-// loads complete in order, waiting for the activations never waits for the
-// weights, and the weight stream starts at the top of the kernel.
+// of weight loads next, then finds the rows' largest magnitudes and writes
+// the activations to LDS; since vector loads complete in order, waiting for
+// the activations never waits for the weights, and the weight stream starts
+// at the top of the kernel.
 #include <type_traits>
 
 #include "common.h"
@@ -72,19 +81,69 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xFFFFu);
 }
 
-// The bf16 magic pattern 0x4300 in both halves, as an opaque VGPR value: with
-// one constant in a VGPR (the mask goes to an SGPR) the (w & mask) | magic
-// step compiles to a single v_and_or_b32 (a VOP3 encoding cannot hold two
-// literal constants).
-__device__ __forceinline__ uint32_t bf16_magic_pair() {
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+__device__ __forceinline__ f16x2_t h2(uint32_t x) { return __builtin_bit_cast(f16x2_t, x); }
+__device__ __forceinline__ uint32_t u32h(f16x2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// two exact products of fp16 pairs, accumulated in float32
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(h2(a), h2(b), c, false);
+}
+
+// The fp16 magic pattern 0x6400 (1024.0) in both halves as an opaque VGPR
+// value, so that (w & mask) | magic is one v_and_or_b32.
+__device__ __forceinline__ uint32_t f16_magic_pair() {
   uint32_t m;
-  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
   return m;
 }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+// Packed word (layout v2: the codes of k = 2i and 2i + 1 in bits 4i and
+// 4i + 16) -> four fp16 pairs q - z, k ascending. c0 = -(1024 + z) and
+// c1 = -(64 + z) in both halves.
+__device__ __forceinline__ void dequant_f16(uint32_t w, uint32_t magic, f16x2_t c0, f16x2_t c1, uint32_t (&x)[4]) {
+  const f16x2_t sixteenth = h2(0x2C002C00u);  // 1/16
+  const uint32_t t = w >> 8;
+  x[0] = u32h(h2((w & 0x000F000Fu) | magic) + c0);
+  x[1] = u32h(__builtin_elementwise_fma(h2((w & 0x00F000F0u) | magic), sixteenth, c1));
+  x[2] = u32h(h2((t & 0x000F000Fu) | magic) + c0);
+  x[3] = u32h(__builtin_elementwise_fma(h2((t & 0x00F000F0u) | magic), sixteenth, c1));
+}
+
+// fp16 constants -(1024 + z) and -(64 + z) in both halves, for a nibble z
+__device__ __forceinline__ void zp_consts(uint32_t z, f16x2_t &c0, f16x2_t &c1) {
+  const uint32_t zz = z | (z << 16);
+  c0 = h2(0xE400E400u | zz);
+  c1 = h2(0xD400D400u | (zz << 4));
+}
+
+// bf16 magnitude bits -> the exponent e that brings the value into
+// [2^14, 2^15) (141 - biased exponent; zero and subnormals get 141)
+__device__ __forceinline__ int scale_exponent(uint32_t mag_bits) { return 141 - (int)(mag_bits >> 7); }
+
+// the largest bf16 magnitude (as integer bits) among the 8 values of c0
+__device__ __forceinline__ uint32_t max_mag8(const u32x4_v &c0) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = c0[j] & 0x7FFFu, hi = (c0[j] >> 16) & 0x7FFFu;
+    r = r > lo ? r : lo;
+    r = r > hi ? r : hi;
+  }
+  return r;
+}
+
+// 8 bf16 values -> 8 fp16 values a * 2^e (round to nearest even)
+__device__ __forceinline__ u32x4_v to_f16_scaled(const u32x4_v &c0, int e) {
+  u32x4_v r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2_t f = {__builtin_amdgcn_ldexpf(__uint_as_float(c0[j] << 16), e),
+                 __builtin_amdgcn_ldexpf(__uint_as_float(c0[j] & 0xFFFF0000u), e)};
+    r[j] = u32h(__builtin_convertvector(f, f16x2_t));
+  }
+  return r;
 }
 
 // Staged activations: bytes per packed word-row per activation row.
@@ -119,33 +178,19 @@ __device__ __forceinline__ void mask_row(bool ok, u32x4_v &c0, u32x4_v &c1) {
   }
 }
 
-// Registers -> LDS in the order the dot products consume; returns the row's
-// activation sum (float bits), summed in k order.
+// Registers -> LDS in the order the dot products consume (bf16 activations:
+// as fp16 scaled by 2^e).
 template <int WF, int AF>
-__device__ __forceinline__ uint32_t store_row(unsigned char *dst, const u32x4_v &c0, const u32x4_v &c1) {
+__device__ __forceinline__ void store_row(unsigned char *dst, const u32x4_v &c0, const u32x4_v &c1, int e) {
   if constexpr (AF == A_BF16) {
-    *(u32x4_v *)dst = c0;
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s = s + bf16_lo(c0[j]) + bf16_hi(c0[j]);
-    return __float_as_uint(s);
+    *(u32x4_v *)dst = to_f16_scaled(c0, e);
   } else if constexpr (AF == A_F32 && WF == W4) {
     // byte conversions of an interleaved word give k + {0,4,1,5} (low nibbles)
     // and k + {2,6,3,7} (high nibbles)
     *(u32x4_v *)dst = (u32x4_v){c0[0], c1[0], c0[1], c1[1]};
     *(u32x4_v *)(dst + 16) = (u32x4_v){c0[2], c1[2], c0[3], c1[3]};
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += __uint_as_float(c0[j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += __uint_as_float(c1[j]);
-    return __float_as_uint(s);
   } else {
     *(u32x4_v *)dst = c0;
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += __uint_as_float(c0[j]);
-    return __float_as_uint(s);
   }
 }
 
@@ -178,13 +223,12 @@ void gemv_kernel(GemvArgs a) {
   constexpr int NB = kSmallBatches ? 2 : 1;           // batch slots in registers
   constexpr int SMAX = 2;                             // activation rows staged per thread up front
   static_assert(AF == A_BF16 || AF == A_F32, "int8 activations use gemv_i8_kernel");
-  constexpr int bias = AF == A_BF16 ? 128 : ((AF == A_F32 && WF == W8) ? 128 : 0);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lk = lane >> 4, c4 = lane & 15;
-  const int tile = blockIdx.x;
-  const int ncol = tile * kTileCols + 4 * c4;         // first of this lane's 4 columns
+  const int n0 = blockIdx.x * kTileCols;
+  const int ncol = n0 + 4 * c4;                       // first of this lane's 4 columns
   const bool col_ok = ncol < a.N;
   const int m0 = blockIdx.y * MB;
   const int z = blockIdx.z;
@@ -237,14 +281,21 @@ void gemv_kernel(GemvArgs a) {
   // write to, so the staging stores need no divergent branch
   const int nstage = MB * rows;
   unsigned char *s_act = lds;                                          // [nstage + 1][AB]
-  uint32_t *s_rsum = (uint32_t *)(lds + (size_t)(nstage + 1) * AB);   // [nstage + 1]
+  // bf16 activations: the largest magnitude (bf16 bits) of each row's slice
+  uint32_t *s_max = (uint32_t *)(lds + (size_t)(nstage + 1) * AB);    // [MB]
+  if constexpr (AF == A_BF16) {
+    if (threadIdx.x < MB) s_max[threadIdx.x] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
 
   // Weights, scales and zero-points are read through buffer resources: the
   // tile's base and the group's offset are wave-uniform (SGPRs) and each lane
   // adds one fixed byte offset, so issuing a load costs no vector arithmetic.
   // (A buffer load past num_records returns 0 instead of faulting.)
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(Wb + (size_t)tile * R * kTileCols), (short)0, R * kTileCols * 4, kBufferWord3);
+      (void *)(Wb + (size_t)blockIdx.x * R * kTileCols), (short)0, R * kTileCols * 4, kBufferWord3);
   const int w_voff = (lk * kTileCols + 4 * c4) * 4;
 
   // Scale and zero-point prefetch goes to registers with no divergent control
@@ -335,11 +386,43 @@ void gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int b = 0; b < (NB > 1 ? NB - 1 : 1); ++b) issue_batch(b * GPB, b);
 #pragma unroll
+  for (int s = 0; s < SMAX; ++s) mask_row(st_ok[s], st0[s], st1[s]);
+  // bf16: each row's largest magnitude over the slice (LDS atomic maxima),
+  // then the row's exponent; the staged rows past the register batch are
+  // loaded twice (the second time from the cache)
+  int rexp[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) rexp[m] = 0;
+  if constexpr (AF == A_BF16) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int idx = threadIdx.x + kGemvThreads * s;
+      if (st_ok[s]) __hip_atomic_fetch_max(&s_max[idx / rows], max_mag8(st0[s]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    for (int idx = threadIdx.x + kGemvThreads * SMAX; idx < nstage; idx += kGemvThreads) {
+      const int m = idx / rows, r = idx - (idx / rows) * rows;
+      if (out_row(m) >= a.M) continue;
+      u32x4_v c0, c1;
+      load_row<WF, AF>(a.A, (size_t)act_row(m) * a.K + (size_t)(gb * RPG + r) * KPW, c0, c1);
+      __hip_atomic_fetch_max(&s_max[m], max_mag8(c0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+    for (int m = 0; m < MB; ++m) rexp[m] = scale_exponent(s_max[m]);
+  }
+  auto row_exp = [&](int m) {
+    int e = rexp[0];
+#pragma unroll
+    for (int j = 1; j < MB; ++j) e = m == j ? rexp[j] : e;
+    return e;
+  };
+#pragma unroll
   for (int s = 0; s < SMAX; ++s) {
     const int idx = threadIdx.x + kGemvThreads * s;
-    mask_row(st_ok[s], st0[s], st1[s]);
     const int slot = idx < nstage ? idx : nstage;
-    s_rsum[slot] = store_row<WF, AF>(s_act + (size_t)slot * AB, st0[s], st1[s]);
+    store_row<WF, AF>(s_act + (size_t)slot * AB, st0[s], st1[s], row_exp(idx / rows));
   }
   for (int idx = threadIdx.x + kGemvThreads * SMAX; idx < nstage; idx += kGemvThreads) {
     const int m = idx / rows, r = idx - (idx / rows) * rows;
@@ -348,14 +431,14 @@ void gemv_kernel(GemvArgs a) {
     load_row<WF, AF>(a.A, ok ? (size_t)act_row(m) * a.K + (size_t)(gb * RPG + r) * KPW : (size_t)act_row0 * a.K,
                      c0, c1);
     mask_row(ok, c0, c1);
-    s_rsum[idx] = store_row<WF, AF>(s_act + (size_t)idx * AB, c0, c1);
+    store_row<WF, AF>(s_act + (size_t)idx * AB, c0, c1, row_exp(m));
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   // ---- main loop over this wave's groups, GPB groups per batch ----
-  const uint32_t magic = bf16_magic_pair();
+  const uint32_t magic = f16_magic_pair();
   float acc[MB][4];
 #pragma unroll
   for (int m = 0; m < MB; ++m)
@@ -377,43 +460,43 @@ void gemv_kernel(GemvArgs a) {
       for (int gi = 0; gi < GPB; ++gi) {
         if (gg + gi >= wgc) break;
         const int gl = wave_group(gg + gi);
-        float pf[MB][4];
-        float cs[MB];  // this lane's share of the group's activation sum
+        // the zero-point of each of the lane's 4 columns (8 without
+        // zero-points for int4, 0 for int8 codes)
+        uint32_t zn[4];
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          cs[m] = 0.f;
+        for (int c = 0; c < 4; ++c) {
+          zn[c] = WF == W8 ? 0u : 8u;
+          if constexpr (ZP) zn[c] = (zv[u][gi] >> (4 * ((ncol & 7) + c))) & 0xFu;
+        }
+        float pf[MB][4];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
 #pragma unroll
           for (int c = 0; c < 4; ++c) pf[m][c] = 0.f;
+        f16x2_t zc0[4], zc1[4];
+        if constexpr (AF == A_BF16) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) zp_consts(zn[c], zc0[c], zc1[c]);
         }
 #pragma unroll
         for (int i = 0; i < IPG; ++i) {
           const u32x4_v wq = wv[u][gi * IPG + i];
           const int lr = gl * RPG + 4 * i + lk;  // local word-row
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            cs[m] += __uint_as_float(s_rsum[m * rows + lr]);
-          }
           const unsigned char *arow = s_act + (size_t)lr * AB;
           if constexpr (AF == A_BF16) {
             uint32_t x[4][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const uint32_t w = wq[c];
-              x[c][0] = (w & 0x000F000Fu) | magic;
-              x[c][1] = ((w >> 4) & 0x000F000Fu) | magic;
-              x[c][2] = ((w >> 8) & 0x000F000Fu) | magic;
-              x[c][3] = ((w >> 12) & 0x000F000Fu) | magic;
-            }
+            for (int c = 0; c < 4; ++c) dequant_f16(wq[c], magic, zc0[c], zc1[c], x[c]);
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
               const u32x4_v av = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 float p = pf[m][c];
-                p = dot2_bf16(x[c][0], av[0], p);
-                p = dot2_bf16(x[c][1], av[1], p);
-                p = dot2_bf16(x[c][2], av[2], p);
-                p = dot2_bf16(x[c][3], av[3], p);
+                p = dot2_f16(x[c][0], av[0], p);
+                p = dot2_f16(x[c][1], av[1], p);
+                p = dot2_f16(x[c][2], av[2], p);
+                p = dot2_f16(x[c][3], av[3], p);
                 pf[m][c] = p;
               }
             }
@@ -422,10 +505,11 @@ void gemv_kernel(GemvArgs a) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const uint32_t lo = wq[c] & 0x0F0F0F0Fu, hi = (wq[c] >> 4) & 0x0F0F0F0Fu;
+              const float zf = (float)zn[c];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                q[c][j] = (float)((lo >> (8 * j)) & 0xFFu);
-                q[c][4 + j] = (float)((hi >> (8 * j)) & 0xFFu);
+              for (int j = 0; j < 4; ++j) {  // q - z, exact in float32
+                q[c][j] = (float)((lo >> (8 * j)) & 0xFFu) - zf;
+                q[c][4 + j] = (float)((hi >> (8 * j)) & 0xFFu) - zf;
               }
             }
 #pragma unroll
@@ -446,11 +530,9 @@ void gemv_kernel(GemvArgs a) {
           } else if constexpr (AF == A_F32 && WF == W8) {
             float q[4][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const uint32_t u = wq[c] ^ 0x80808080u;  // int8 code + 128 as an unsigned byte
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) q[c][j] = (float)((u >> (8 * j)) & 0xFFu);
-            }
+              for (int j = 0; j < 4; ++j) q[c][j] = (float)(int8_t)(wq[c] >> (8 * j));  // the signed code
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
               const u32x4_v a0 = *(const u32x4_v *)(arow + (size_t)m * rows * AB);
@@ -465,25 +547,22 @@ void gemv_kernel(GemvArgs a) {
           }
         }
 
-        // ---- group epilogue: remove the code bias, apply the group scale ----
+        // ---- group epilogue: apply the group scale ----
         float s[4];
         scales_of(u, gi, gl, s);
-        int zc[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          int zz = WF == W8 ? 0 : 8;
-          if constexpr (ZP) zz = (int)((zv[u][gi] >> (4 * ((ncol & 7) + c))) & 0xFu);
-          zc[c] = bias + zz;
-        }
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float d = pf[m][c] - (float)zc[c] * cs[m];
-            acc[m][c] = __builtin_fmaf(s[c], d, acc[m][c]);
-          }
+          for (int c = 0; c < 4; ++c) acc[m][c] = __builtin_fmaf(s[c], pf[m][c], acc[m][c]);
       }
     }
+  }
+  // bf16 activations were scaled by 2^e per row: undo it (exact)
+  if constexpr (AF == A_BF16) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[m][c] = __builtin_amdgcn_ldexpf(acc[m][c], -rexp[m]);
   }
 
   // ---- reduction: the 4 lanes of a column, then the waves (fixed order) ----
@@ -517,10 +596,11 @@ void gemv_kernel(GemvArgs a) {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kGemvWaves; ++w) v += s_red[((size_t)w * MB + m) * kTileCols + col];
-    const int n = tile * kTileCols + col;
+    const int n = n0 + col;
+    if (n >= a.N) continue;  // the last block may reach past column N (and Np)
     if (a.nsplit > 1) {
       a.partial[((size_t)z * a.M + orow) * a.Np + n] = v;
-    } else if (n < a.N) {
+    } else {
       const size_t o = (size_t)orow * a.N + n;
       if constexpr (OF == O_BF16)
         ((uint16_t *)a.out)[o] = f32_to_bf16(v);

@@ -681,6 +681,15 @@ int qgemm_fp8_gemm(int M, int N, int K, int scaling, const void *Aq, const void 
   return qgemm_fp8_gemm_ex(M, N, K, scaling, Aq, a_scales, Wq, w_scales, out, nullptr, 0, 1, stream);
 }
 
+int qgemm_stream_read(const void *src, size_t bytes, void *out, int blocks, void *stream) {
+  if (!src || !out || bytes == 0 || bytes % 16 != 0 || bytes >= (size_t)INT_MAX || blocks < 1 || blocks > 65535)
+    return QG_EINVAL;
+  if (!aligned16(src) || ((uintptr_t)out & 3u) != 0) return QG_EALIGN;
+  drop_pending_error();
+  return launch_stream_read(src, bytes, (uint32_t *)out, blocks, (hipStream_t)stream) == hipSuccess ? QG_OK
+                                                                                                    : QG_EHIP;
+}
+
 const char *qgemm_strerror(int status) {
   switch (status) {
     case QG_OK: return "ok";

@@ -332,6 +332,21 @@ int qgemm_fp8_gemm_ex(int M, int N, int K, int scaling, const void *Aq, const vo
                       const void *w_scales, void *out, void *workspace, size_t workspace_bytes, int force_nsplit,
                       void *stream);
 
+/* Measurement aid (not part of the product): a plain streaming read of
+ * `bytes` bytes at `src`, the reference point for the HBM rate the GEMV path
+ * reaches on the same byte count (the pages measure kernels against the
+ * memory roofline: "quantization-and-fused-kernels", section 三.2 and 十).
+ * Each of `blocks` workgroups reads a balanced contiguous range of 16-byte
+ * pieces with 8 loads in flight per lane.
+ *   src: device, 16-byte aligned; bytes: a multiple of 16, 0 < bytes < 2^31.
+ *   out: device, at least 4 * blocks uint32_t, written (an XOR of the data
+ *        each wave read, so the reads are not optimised away).
+ *   blocks: 1 .. 65535 (2 per compute unit is a good choice).
+ * QG_EINVAL for a null pointer or a size outside those limits, QG_EALIGN
+ * for a misaligned pointer, QG_EHIP if the launch fails. One kernel on
+ * `stream`, nothing allocated. */
+int qgemm_stream_read(const void *src, size_t bytes, void *out, int blocks, void *stream);
+
 /* Human-readable text of a status code. */
 const char *qgemm_strerror(int status);
 

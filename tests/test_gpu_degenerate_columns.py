@@ -43,6 +43,10 @@ def _problem(M, G, prec, zp, seed):
 
 # (path, M, G, prec, zp); path 0 = GEMV, 1 = tiled MFMA GEMM, 2 = small-M MFMA
 CASES = [
+    (0, 1, 128, 6, False), (0, 1, 128, 6, True), (0, 5, 128, 6, True), (0, 1, 32, 6, False),
+    (0, 8, 32, 6, True), (0, 1, 32, 2, False), (0, 3, 128, 2, True), (0, 1, 32, 3, False),
+    (0, 4, 128, 3, False), (0, 2, 128, 4, True), (0, 1, 32, 5, False), (0, 1, 32, 7, True),
+    (0, 1, 128, 1, False), (0, 1, 128, 1, True),
     (1, 150, 128, 6, False), (1, 150, 128, 6, True), (1, 130, 128, 1, True), (1, 300, 128, 6, True),
 ]
 

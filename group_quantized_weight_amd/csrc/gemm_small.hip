@@ -14,17 +14,19 @@
 //     each wave takes a contiguous share of the slice's groups;
 //   - per group, each lane loads 16 bytes of packed words per k-step (4
 //     adjacent columns x 8 k; a wave reads 1 KiB of contiguous memory) and
-//     turns each word into four bf16 pairs (128 + q) (bf16 magic number
-//     0x4300, section 二.4 of the first page); MFMA column j of tile f is
-//     physical column 4j + f of the 64-column tile;
-//   - activation fragments are read from global memory (rows past M read as
-//     zeros); the MFMAs accumulate P = sum_k a_k (128 + q_k), and one more
-//     MFMA per row block and k-step, against an all-ones operand, gives the
-//     group's row sums S = sum_k a_k, so no pre-pass is needed;
-//   - per group the bias and the scale are applied in float32:
-//     acc += s * (P - (128 + z) * S) (both products exact on integer
-//     inputs; one extra MFMA per row block instead of one per column tile:
-//     5 MB instead of 8 MB MFMAs per k-step);
+//     turns each word into four bf16 pairs of the exact integers q - z:
+//     each code goes into the mantissa of fp16 1024.0 (fp16 magic number,
+//     section 二.4 of the first page), v_fma_mix_f32 widens each half to
+//     float32 and subtracts 1024 + z (or, for the code one nibble higher,
+//     scales by 1/16 and subtracts 64 + z), and v_cvt_pk_bf16_f32 packs two
+//     results; every step is exact (|q - z| <= 15 needs 4 bits). MFMA column
+//     j of tile f is physical column 4j + f of the 64-column tile;
+//   - activation fragments are read from global memory as bf16, unchanged
+//     (rows past M read as zeros); each product a * (q - z) is exact in the
+//     MFMA's float32 accumulator, which sums the group's 128 of them;
+//   - per group the scale is applied in float32: acc += s * P. No biased sum
+//     is formed, so a column whose codes all equal its zero-point gives
+//     exactly zero;
 //   - the 4 waves' results are added in wave order (waves 1..3 through LDS),
 //     then written to the output (nsplit == 1) or to float32 partials that a
 //     second kernel adds in the order z = 0..nsplit-1.
@@ -45,24 +47,18 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4_s;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_s;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_s;
 typedef __attribute__((ext_vector_type(2))) float f32x2_s;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_s;
 
 constexpr int kWaves = 4;
 constexpr int kBufWord3s = 0x00020000;
 constexpr int kStreamPolicy = 2;    // non-temporal
+// groups of weights in registers: kDepth - 1 in flight while one is computed
+constexpr int kDepth = 2;
 
-__device__ __forceinline__ uint32_t magic_pair() {
+__device__ __forceinline__ uint32_t magic_pair() {  // fp16 1024.0 in both halves
   uint32_t m;
-  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
   return m;
-}
-
-__device__ __forceinline__ bf16x8_s dequant(uint32_t w, uint32_t magic) {
-  u32x4_s x;
-  x[0] = (w & 0x000F000Fu) | magic;
-  x[1] = ((w >> 4) & 0x000F000Fu) | magic;
-  x[2] = ((w >> 8) & 0x000F000Fu) | magic;
-  x[3] = ((w >> 12) & 0x000F000Fu) | magic;
-  return __builtin_bit_cast(bf16x8_s, x);
 }
 
 __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
@@ -70,10 +66,28 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_s));
 }
 
-// Eight bf16 ones: the operand whose product with an activation fragment is
-// the fragment rows' sums.
-__device__ __forceinline__ bf16x8_s ones_operand() {
-  const u32x4_s x = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+// float32 1.0 in a register the compiler cannot see through, so that x * 1 +
+// c stays one v_fma_mix_f32 instead of a conversion and an add
+__device__ __forceinline__ float opaque_one() {
+  float one;
+  asm volatile("v_mov_b32 %0, 1.0" : "=v"(one));
+  return one;
+}
+
+// The eight codes of a packed word (layout version 2: codes 2i and 2i + 1 at
+// bits 4i and 4i + 16) as bf16 q - z, in k order. c0 = -(1024 + z), c1 =
+// -(64 + z).
+__device__ __forceinline__ bf16x8_s dequant(uint32_t w, uint32_t magic, float one, float c0, float c1) {
+  const uint32_t t = w >> 8;
+  const f16x2_s h0 = __builtin_bit_cast(f16x2_s, (w & 0x000F000Fu) | magic);  // 1024 + q0, 1024 + q1
+  const f16x2_s h1 = __builtin_bit_cast(f16x2_s, (w & 0x00F000F0u) | magic);  // 1024 + 16 q2, 1024 + 16 q3
+  const f16x2_s h2 = __builtin_bit_cast(f16x2_s, (t & 0x000F000Fu) | magic);  // q4, q5
+  const f16x2_s h3 = __builtin_bit_cast(f16x2_s, (t & 0x00F000F0u) | magic);  // q6, q7
+  u32x4_s x;
+  x[0] = bf16x2_bits(__builtin_fmaf((float)h0[0], one, c0), __builtin_fmaf((float)h0[1], one, c0));
+  x[1] = bf16x2_bits(__builtin_fmaf((float)h1[0], 0.0625f, c1), __builtin_fmaf((float)h1[1], 0.0625f, c1));
+  x[2] = bf16x2_bits(__builtin_fmaf((float)h2[0], one, c0), __builtin_fmaf((float)h2[1], one, c0));
+  x[3] = bf16x2_bits(__builtin_fmaf((float)h3[0], 0.0625f, c1), __builtin_fmaf((float)h3[1], 0.0625f, c1));
   return __builtin_bit_cast(bf16x8_s, x);
 }
 
@@ -147,22 +161,29 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_s){0.f, 0.f, 0.f, 0.f};
 
-  // one group's loads; the next group's are issued before the current one is
-  // computed (a group past the wave's range re-reads the wave's last one, or
-  // the matrix's last one for a wave without groups: valid addresses,
-  // results unused)
-  struct GroupLoads {
+  // One group's loads. The weights (from HBM) are issued kDepth - 1 groups
+  // ahead of the computation, the activations, scales and zero-points (from
+  // L2) one group ahead. A group past the wave's range re-reads the wave's
+  // last one, or the matrix's last one for a wave without groups: valid
+  // addresses, results unused.
+  struct WeightLoads {
     u32x4_s w[4];
+  };
+  struct GroupLoads {
     bf16x8_s af[MB][4];
     u32x2_s sv;
     uint32_t zw;
   };
-  auto issue = [&](int gi, GroupLoads &L) {
-    const int g = min(gb + wg0 + (gi < wgc ? gi : (wgc > 0 ? wgc - 1 : 0)), a.ngroups - 1);
+  auto group_of = [&](int gi) { return min(gb + wg0 + (gi < wgc ? gi : (wgc > 0 ? wgc - 1 : 0)), a.ngroups - 1); };
+  auto issue_w = [&](int gi, WeightLoads &L) {
+    const int g = group_of(gi);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       L.w[s] = __builtin_bit_cast(u32x4_s, __builtin_amdgcn_raw_buffer_load_b128(
                                                w_rsrc, w_voff, (g * 16 + 4 * s) * kTileCols * 4, kStreamPolicy));
+  };
+  auto issue = [&](int gi, GroupLoads &L) {
+    const int g = group_of(gi);
 #pragma unroll
     for (int fm = 0; fm < MB; ++fm)
 #pragma unroll
@@ -176,51 +197,74 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
       L.zw = __builtin_amdgcn_raw_buffer_load_b32(z_rsrc, (scol >> 3) * 4, g * (a.N >> 3) * 4, 0) >>
              (4 * (scol & 7));
   };
-  const bf16x8_s ones = ones_operand();
-  auto compute = [&](const GroupLoads &L) {
-    f32x4_s P[MB][4], S[MB];
+  const float one = opaque_one();
+  auto compute = [&](const WeightLoads &W, const GroupLoads &L) {
+    // column 4 li + fn of the lane: zero-point nibble fn of zw, scale sc[fn]
+    float c0[4], c1[4];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      S[i] = (f32x4_s){0.f, 0.f, 0.f, 0.f};
+    for (int fn = 0; fn < 4; ++fn) {
+      const float zf = (float)((L.zw >> (4 * fn)) & 0xFu);
+      c0[fn] = -1024.f - zf;
+      c1[fn] = -64.f - zf;
+    }
+    f32x4_s P[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) P[i][j] = (f32x4_s){0.f, 0.f, 0.f, 0.f};
-    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_s bfr[4];
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant(L.w[s][fn], magic);
+      for (int fn = 0; fn < 4; ++fn) bfr[fn] = dequant(W.w[s][fn], magic, one, c0[fn], c1[fn]);
 #pragma unroll
-      for (int fm = 0; fm < MB; ++fm) {
-        S[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(L.af[fm][s], ones, S[fm], 0, 0, 0);
+      for (int fm = 0; fm < MB; ++fm)
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn)
           P[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(L.af[fm][s], bfr[fn], P[fm][fn], 0, 0, 0);
-      }
     }
-    // column 4 li + fn of the lane: scale sc[fn], zero-point nibble fn of zw
     const float sc[4] = {__uint_as_float(L.sv[0] << 16), __uint_as_float(L.sv[0] & 0xFFFF0000u),
                          __uint_as_float(L.sv[1] << 16), __uint_as_float(L.sv[1] & 0xFFFF0000u)};
-    float bias[4];
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn) bias[fn] = -(float)(128 + (int)((L.zw >> (4 * fn)) & 0xFu));
 #pragma unroll
     for (int fm = 0; fm < MB; ++fm)
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[fm][fn][r] =
-              __builtin_fmaf(sc[fn], __builtin_fmaf(bias[fn], S[fm][r], P[fm][fn][r]), acc[fm][fn][r]);
+        for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(sc[fn], P[fm][fn][r], acc[fm][fn][r]);
   };
 
-  GroupLoads cur, nxt;
-  issue(0, cur);
-  for (int gi = 0; gi < wgc; ++gi) {
-    issue(gi + 1, nxt);
-    compute(cur);
-    cur = nxt;
+  // group j sits in weight slot j % kDepth and activation slot j % 2; the
+  // loop is unrolled so that every slot index is a constant (no register
+  // copies, which would wait for loads in flight)
+  constexpr int kUnroll = kDepth % 2 == 0 ? kDepth : 2 * kDepth;
+  WeightLoads wr[kDepth];
+  GroupLoads ar[2];
+  // the loads in flight at the loop head are issued in the loop's own order
+  // (weights of group j, activations of group j, weights of group j + 1,
+  // ...), so the compiler's wait analysis sees the same state on both edges
+  issue_w(0, wr[0]);
+  issue(0, ar[0]);
+#pragma unroll
+  for (int d = 1; d < kDepth - 1; ++d) issue_w(d, wr[d]);
+  __builtin_amdgcn_sched_barrier(0);
+  // (the last group leaves both loops at once: a jump back to the loop head
+  // from there would merge different sets of loads in flight, and the
+  // compiler would then wait for all of them at the head)
+  for (int gi = 0; gi < wgc; gi += kUnroll) {
+#pragma unroll
+    for (int d = 0; d < kUnroll; ++d) {
+      if (gi + d >= wgc) goto groups_done;
+      // activations first: the wait for a group's activations (counted in
+      // issue order) then leaves the later groups' weights in flight
+      issue(gi + d + 1, ar[(d + 1) % 2]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(gi + d + kDepth - 1, wr[(d + kDepth - 1) % kDepth]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wr[d % kDepth], ar[d % 2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+groups_done:
 
   // ---- the 4 waves' results, added in wave order: waves 1..3 hand theirs
   // to wave 0 through LDS (element (16 fm + 4 lk + r, 4 li + fn) of wave w at

@@ -505,6 +505,8 @@ int check_moe(int T, int topk, int N, int K, int G, int prec, int has_zp, int E,
   if ((long long)T * topk > INT_MAX / 2) return QG_EUNSUPPORTED;
   const int numel = T * topk;
   if (qgemm_moe_max_tiles(numel, E, block) == 0) return QG_EUNSUPPORTED;
+  // the MFMA blocks address the T activation rows with 32-bit byte offsets
+  if (block >= 16 && (size_t)T * K * 2 > (size_t)INT_MAX) return QG_EUNSUPPORTED;
   return check_shape(numel > 0 ? numel : 1, N, K, G, prec, has_zp, f);
 }
 

@@ -48,6 +48,8 @@ CASES = [
     (0, 4, 128, 3, False), (0, 2, 128, 4, True), (0, 1, 32, 5, False), (0, 1, 32, 7, True),
     (0, 1, 128, 1, False), (0, 1, 128, 1, True),
     (1, 150, 128, 6, False), (1, 150, 128, 6, True), (1, 130, 128, 1, True), (1, 300, 128, 6, True),
+    (2, 2, 128, 6, False), (2, 16, 128, 6, True), (2, 37, 128, 6, True), (2, 64, 128, 1, True),
+    (2, 64, 128, 6, False), (2, 32, 32, 5, False), (2, 40, 128, 4, True), (2, 24, 32, 7, True),
 ]
 
 
@@ -62,5 +64,6 @@ def test_degenerate_columns(path, M, G, prec, zp):
     zero_err = float(np.max(np.abs(out[:, ZERO])))
     print(f"path={path} M={M} G={G} prec={prec} zp={zp}: max |out| on zero columns = {zero_err:.3e}",
           flush=True)
+    assert zero_err == 0.0, f"path={path} M={M} prec={prec}: {zero_err:.3e} on columns with w_hat = 0"
     check(out, ref, bound, f"degenerate columns path={path} M={M} G={G} prec={prec} zp={zp}",
           bf16_out=prec == 1)

@@ -262,6 +262,10 @@ def test_moe_validation():
     assert r(G=64) == qg.EUNSUPPORTED and r(K=200) == qg.EINVAL
     assert r(zp=1, N=250, Z=P) == qg.EUNSUPPORTED and r(zp=1, Z=None) == qg.EINVAL
     assert r(b=16, G=32) == qg.EUNSUPPORTED and r(b=16, N=250) == qg.EUNSUPPORTED   # MFMA blocks
+    # MFMA blocks address the T activation rows with 32-bit byte offsets:
+    # T * K * 2 = 2^32 is refused before any pointer is used
+    assert r(T=65536, K=32768, b=16) == qg.EUNSUPPORTED
+    assert L.qgemm_moe_workspace_bytes(65536, 2, 256, 32768, 128, 1, 8, 16) == 0
     for kw in ("A", "W", "S", "srt", "te", "npp", "out"):
         assert r(**{kw: None}) == qg.EINVAL, kw
         assert r(**{kw: MIS}) == qg.EALIGN, kw

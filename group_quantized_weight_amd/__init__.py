@@ -76,6 +76,8 @@ def lib():
             L.qgemm_run.argtypes = run_args
             L.qgemm_run_ex.restype = c_int
             L.qgemm_run_ex.argtypes = run_args + [c_int, c_int]
+            L.qgemm_run_noalloc.restype = c_int
+            L.qgemm_run_noalloc.argtypes = [c_int] * 6 + [vp] * 7
             L.qgemm_moe_max_tiles.restype = c_int
             L.qgemm_moe_max_tiles.argtypes = [c_int] * 3
             L.qgemm_moe_default_block.restype = c_int
@@ -214,6 +216,22 @@ def stream_read(buf, nbytes: int, out, blocks: int, stream=None):
                                  stream if stream is not None else _stream(buf.device))
     if st != OK:
         raise QGemmError(st, "qgemm_stream_read")
+
+
+def run_noalloc(A, w_packed, scales, *, N: int, G: int, prec: int, zeros=None, a_scales=None, out=None,
+                stream=None):
+    """run() through qgemm_run_noalloc: no workspace, the library's own
+    per-GPU array instead (calls that overlap on one GPU must not be made)."""
+    import torch
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype(prec), device=A.device)
+    st = lib().qgemm_run_noalloc(M, N, K, G, prec, int(zeros is not None), _ptr(A), _ptr(a_scales),
+                                 _ptr(w_packed), _ptr(scales), _ptr(zeros), _ptr(out),
+                                 stream if stream is not None else _stream(A.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_run_noalloc")
+    return out
 
 
 def quantize_activations(A, G: int, Aq=None, a_scales=None, stream=None):

@@ -403,6 +403,62 @@ int qgemm_run(int M, int N, int K, int group, int prec, int has_zp, const void *
                       workspace_bytes, stream, QG_PATH_AUTO, 0);
 }
 
+}  // extern "C"
+
+// Workspace of qgemm_run_noalloc: one copy of this array per GPU, placed in
+// the code object's global memory when the library's code is loaded on that
+// device and held until the process ends. Host code never uses the array's
+// name as an address (on the host it names a stand-in): each device's
+// address comes from hipGetSymbolAddress, taken once with that device
+// current.
+static __device__ __align__(256) unsigned char scratch[QG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// This device's copy of `scratch`, or null when its address cannot be had.
+void *scratch_address(int dev) {
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void *q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  // threads that race here all store the same address
+  g_scratch[dev].store(q, std::memory_order_release);
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemm_run_noalloc(int M, int N, int K, int group, int prec, int has_zp, const void *A, const void *a_scales,
+                      const void *w_packed, const void *scales, const void *zeros, void *out, void *stream) {
+  Formats f;
+  int st = check_shape(M, N, K, group, prec, has_zp, f);
+  if (st != QG_OK) return st;
+  if (M == 0) return QG_OK;
+  Plan p;
+  st = make_plan(M, N, K, group, f, QG_PATH_AUTO, 0, p);
+  if (st != QG_OK) return st;
+  if (p.ws > (size_t)QG_NOALLOC_SCRATCH_BYTES) return QG_EWORKSPACE;
+  void *ws = nullptr;
+  if (p.ws > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+      (void)hipGetLastError();
+      return QG_EHIP;
+    }
+    ws = scratch_address(dev);
+    if (!ws) return QG_EHIP;
+  }
+  return qgemm_run_ex(M, N, K, group, prec, has_zp, A, a_scales, w_packed, scales, zeros, out, ws,
+                      ws ? (size_t)QG_NOALLOC_SCRATCH_BYTES : 0, stream, QG_PATH_AUTO, 0);
+}
+
 int qgemm_quantize_activations(const void *A, int M, int K, int group, void *Aq, void *a_scales,
                                void *stream) {
   if (M < 0 || K <= 0) return QG_EINVAL;

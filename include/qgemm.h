@@ -158,6 +158,30 @@ int qgemm_run(int M, int N, int K, int group, int prec, int has_zp, const void *
               const void *a_scales, const void *w_packed, const void *scales, const void *zeros,
               void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the workspace that qgemm_run_noalloc owns on each GPU. */
+#define QG_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * qgemm_run for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine)
+ * and takes no workspace: it uses a library-owned array of
+ * QG_NOALLOC_SCRATCH_BYTES on the current device, which is placed when the
+ * library's code is loaded on that device and held until the process ends.
+ * Arguments, results and the plan are those of qgemm_run (same kernels, same
+ * bits). Returns QG_EWORKSPACE when the problem needs more than
+ * QG_NOALLOC_SCRATCH_BYTES (qgemm_workspace_bytes), before anything is
+ * enqueued; QG_EHIP when the array's address cannot be had.
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents (no call depends on them). Calls that may overlap on
+ * one GPU (concurrent streams, or host threads without an order between
+ * them) race on the array and must not be made; calls ordered on one stream
+ * are safe.
+ */
+int qgemm_run_noalloc(int M, int N, int K, int group, int prec, int has_zp, const void *A,
+                      const void *a_scales, const void *w_packed, const void *scales,
+                      const void *zeros, void *out, void *stream);
+
 /* qgemm_run with an explicit plan (see qgemm_plan); for tests and tuning. */
 int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const void *A,
                  const void *a_scales, const void *w_packed, const void *scales,

@@ -55,7 +55,7 @@ class Prepared:
     def __init__(self, qg, M, N, K, G, prec, A, a_scale, Ws, Ss, Z, out, stream, force_path=-1, force_nsplit=0):
         self.lib = qg.lib()
         _, _, ws_bytes = qg.plan(M, N, K, G, prec, force_path, force_nsplit)
-        self.ws = qg.workspace(ws_bytes, A.device)
+        self.ws = qg.workspace(ws_bytes, A.device, stream)
         vp = ctypes.c_void_p
         self.args = []
         for W, S in zip(Ws, Ss):
@@ -351,9 +351,9 @@ def run_moe(name, steps, warmup, mode, block=None):
     srt, tiles, npp = qg.moe_align(ids, p.E, block)
     out = torch.empty((numel, p.N), dtype=torch.bfloat16, device="cuda")
     need = int(qg.lib().qgemm_moe_workspace_bytes(p.T, p.topk, p.N, p.K, p.G, prec, p.E, block))
-    ws = qg.workspace(need, A.device)
     L = qg.lib()
     stream = vp(torch.cuda.current_stream().cuda_stream)
+    ws = qg.workspace(need, A.device, stream)
 
     def step(i):
         st = L.qgemm_moe_align(vp(ids.data_ptr()), numel, p.E, block, vp(srt.data_ptr()), vp(tiles.data_ptr()),

@@ -165,28 +165,51 @@ def pack(w_canonical, K: int, N: int, prec: int):
     return out
 
 
-_ws_cache = {}
+_ws_cache = {}     # (device, stream handle) -> [workspace, handed out during a graph capture]
+_ws_retired = []   # outgrown workspaces that a captured graph may still write to
 
 
-_ws_retired = []
+def _stream_handle(stream, device) -> int:
+    """The raw HIP stream handle of stream (a ctypes handle, an int or a
+    torch stream); the device's current stream when None."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, ctypes.c_void_p):
+        return stream.value or 0
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
 
 
-def workspace(nbytes: int, device):
-    """A workspace of at least nbytes on device (cached per device and grown;
-    its contents before a call do not matter to the library). A workspace
-    that is outgrown is kept alive, never freed: a HIP graph captured while
-    it was current still writes to it on every replay."""
+def workspace(nbytes: int, device, stream=None):
+    """A workspace of at least nbytes for calls on stream (default: the
+    device's current stream), cached per (device, stream) so that calls
+    enqueued on different streams never share one; its contents before a
+    call do not matter to the library. It is allocated with that stream
+    current, so torch's allocator orders its reuse after the stream's work.
+    An outgrown workspace is freed, unless it was handed out while a graph
+    capture was under way: the captured graph writes to it on every replay,
+    so it is then kept alive for the life of the process."""
     import torch
     if nbytes == 0:
         return None
-    key = str(device)
-    ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < nbytes:
-        if ws is not None:
-            _ws_retired.append(ws)
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _ws_cache[key] = ws
-    return ws
+    device = torch.device(device)
+    handle = _stream_handle(stream, device)
+    key = (str(device), handle)
+    entry = _ws_cache.get(key)
+    if entry is None or entry[0].numel() < nbytes:
+        if entry is not None and entry[1]:
+            _ws_retired.append(entry[0])
+        if handle == torch.cuda.current_stream(device).cuda_stream:
+            entry = [torch.empty(nbytes, dtype=torch.uint8, device=device), False]
+        else:
+            with torch.cuda.stream(torch.cuda.ExternalStream(handle, device=device)):
+                entry = [torch.empty(nbytes, dtype=torch.uint8, device=device), False]
+        _ws_cache[key] = entry
+    if torch.cuda.is_current_stream_capturing():
+        entry[1] = True
+    return entry[0]
 
 
 def out_dtype(prec: int):
@@ -290,7 +313,7 @@ def moe_run(A, w_packed, scales, routing, *, topk: int, N: int, G: int, E: int, 
     if out is None:
         out = torch.empty((T * topk, N), dtype=out_dtype(prec), device=A.device)
     need = int(lib().qgemm_moe_workspace_bytes(T, topk, N, K, G, prec, E, block))
-    ws = workspace(need, A.device)
+    ws = workspace(need, A.device, stream)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().qgemm_moe_run(T, topk, N, K, G, prec, int(zeros is not None), E, block, _ptr(A), _ptr(w_packed),
                              _ptr(scales), _ptr(zeros), _ptr(sorted_ids), _ptr(tile_experts), _ptr(npp), _ptr(out),
@@ -341,7 +364,7 @@ def fp8_gemm(Aq, a_scales, Wq, w_scales, scaling: int = FP8_PER_TOKEN, out=None,
     if force_nsplit > 0:
         need = max(need, force_nsplit * M * -(-N // 128) * 128 * 4)
     if ws is None:
-        ws = workspace(need, Aq.device)
+        ws = workspace(need, Aq.device, st_arg)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().qgemm_fp8_gemm_ex(M, N, K, scaling, _ptr(Aq), _ptr(a_scales), _ptr(Wq), _ptr(w_scales), _ptr(out),
                                  _ptr(ws) if ws is not None else None, ws_bytes, force_nsplit, st_arg)
@@ -370,7 +393,7 @@ def run(A, w_packed, scales, *, N: int, G: int, prec: int, zeros=None, a_scales=
         out = torch.empty((M, N), dtype=out_dtype(prec), device=A.device)
     _, _, need = plan(max(M, 1), N, K, G, prec, force_path, force_nsplit)
     if ws is None:
-        ws = workspace(need, A.device)
+        ws = workspace(need, A.device, stream)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().qgemm_run_ex(M, N, K, G, prec, int(zeros is not None), _ptr(A), _ptr(a_scales),
                             _ptr(w_packed), _ptr(scales), _ptr(zeros), _ptr(out), _ptr(ws), ws_bytes,

@@ -112,18 +112,23 @@ def test_graph_survives_workspace_growth():
     p = wl.make_problem(16, 1000, 1024, 128, 1, True, seed=2500)
     d = Dev(p)
     out = d.run(force_path=qg.PATH_SMALL, force_nsplit=4)
-    small = qg._ws_cache["cuda:0"].numel()
     side = torch.cuda.Stream()
+    key = ("cuda:0", side.cuda_stream)
     with torch.cuda.stream(side):
         d.run(force_path=qg.PATH_SMALL, force_nsplit=4, out=out)
         torch.cuda.synchronize()
         ref = out.clone()
+        small = qg._ws_cache[key][0].numel()
+        assert qg._ws_cache[key][0].data_ptr() != qg._ws_cache[("cuda:0", torch.cuda.default_stream().cuda_stream)][0].data_ptr()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             d.run(force_path=qg.PATH_SMALL, force_nsplit=4, out=out)
+        assert qg._ws_cache[key][1]           # handed out during the capture
+        retired = len(qg._ws_retired)
         big = wl.make_problem(64, 4096, 2048, 128, 1, False, seed=2501)
         Dev(big).run(force_path=qg.PATH_SMALL, force_nsplit=8)     # needs a larger workspace
-        assert qg._ws_cache["cuda:0"].numel() > small
+        assert qg._ws_cache[key][0].numel() > small
+        assert len(qg._ws_retired) == retired + 1 and not qg._ws_cache[key][1]
         junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
         torch.cuda.synchronize()
         for r in range(3):
@@ -133,3 +138,18 @@ def test_graph_survives_workspace_growth():
             torch.cuda.synchronize()
             assert bitwise_equal(out, ref), f"replay {r} differs after the workspace grew"
         del g, junk
+
+
+def test_workspace_per_stream_and_freed_when_never_captured():
+    """Calls on two streams get two workspaces; a workspace that no capture
+    ever used is freed when it is outgrown, not retired."""
+    import torch
+    qg._ws_cache.clear()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    w1 = qg.workspace(1 << 20, "cuda:0", s1)
+    w2 = qg.workspace(1 << 20, "cuda:0", s2)
+    assert w1.data_ptr() != w2.data_ptr()
+    assert qg.workspace(1 << 19, "cuda:0", s1).data_ptr() == w1.data_ptr()     # reused when large enough
+    retired = len(qg._ws_retired)
+    w1b = qg.workspace(1 << 22, "cuda:0", s1)
+    assert w1b.numel() >= 1 << 22 and len(qg._ws_retired) == retired

@@ -281,11 +281,3 @@ def set_threads(n: int, lib=None) -> int:
 
 def num_threads(lib=None) -> int:
     return int((lib or load()).oracle_num_threads())
-
-
-def gate(out, ref, bound, rel=2e-3, atol=1e-5):
-    """Per-element parity gate: |out - ref| <= rel * bound + atol. Returns (ok, worst_ratio)."""
-    err = np.abs(np.asarray(out, dtype=np.float64) - ref)
-    lim = rel * bound + atol
-    ratio = float(np.max(err / lim)) if err.size else 0.0
-    return bool(np.all(err <= lim)), ratio

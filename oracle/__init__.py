@@ -237,6 +237,43 @@ def moe(T, topk, N, K, G, wfmt, afmt, sfmt, has_zp, A, topk_ids, W, S, Z, slots=
     return ref, bound
 
 
+def silu(x):
+    """The SiLU (swish) activation x * sigmoid(x) = x / (1 + e^-x), in
+    float64, as the page "quantization-and-fused-kernels" defines it for
+    SwiGLU (section 五.2; the practice kernel of section 九.2). exp(-x)
+    overflows to inf for x below about -709, giving -0.0: the limit."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def silu_mul(y, d: int):
+    """SwiGLU's gate step on the output y [M, 2d] of a fused gate_up product
+    (section 五.2: the first d columns are the gate, the last d the up
+    projection): out[m, j] = silu(y[m, j]) * y[m, d + j], float64 [M, d]."""
+    y = np.asarray(y, dtype=np.float64)
+    if y.ndim != 2 or d < 1 or y.shape[1] != 2 * d:
+        raise ValueError("silu_mul: y must be [M, 2d]")
+    return silu(y[:, :d]) * y[:, d:]
+
+
+def gate_up(M, d, K, G, wfmt, afmt, sfmt, has_zp, A, a_scale, W, S, Z, rows=None, cols=None, lib=None):
+    """The fused gate_up product followed by its SwiGLU gate step: W, S, Z are
+    canonical over N = 2d columns (gate columns 0..d-1, up columns d..2d-1);
+    output column j (of d) combines product columns j and d + j. Returns
+    (out, gate, up, gate_bound, up_bound), each [rows, cols of d]: out from
+    silu_mul on the float64 product, and the product columns with their
+    sum_k |a_k w_k| bounds (qgemm)."""
+    cols = np.arange(d) if cols is None else np.asarray(cols)
+    if np.any(cols < 0) or np.any(cols >= d):
+        raise ValueError("gate_up: output column out of range")
+    both = np.concatenate([cols, cols + d])
+    r, b = qgemm(M, 2 * d, K, G, wfmt, afmt, sfmt, has_zp, A, a_scale, W, S, Z, rows=rows, cols=both, lib=lib)
+    n = len(cols)
+    out = silu_mul(r, n)
+    return out, r[:, :n], r[:, n:], b[:, :n], b[:, n:]
+
+
 def fp8_value(code: int, lib=None) -> float:
     """Value of an 8-bit E4M3 ("fn") code (NaN for 0x7F and 0xFF)."""
     return float((lib or load()).oracle_fp8_value(int(code)))

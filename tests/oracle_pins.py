@@ -19,6 +19,7 @@ None of these re-types the oracle's formula: the decodes take other routes
 integer matmuls.
 """
 import json
+import math
 import os
 import struct
 from fractions import Fraction
@@ -569,6 +570,75 @@ def check_moe_vs_brute(lib, orc=oracle):
         assert np.allclose(ref[i], exact, rtol=1e-12, atol=1e-15), (i, e, t)
 
 
+# --------------------------------------------------------------------------
+# SwiGLU gate step after a fused gate_up product (silu_mul, gate_up)
+# --------------------------------------------------------------------------
+_E, _LN3, _LN4 = math.e, math.log(3.0), math.log(4.0)
+# (x, silu(x)), each from a closed form of x / (1 + e^-x)
+SILU_HAND = [
+    (0.0, 0.0),                    # 0 / (1 + 1)
+    (1.0, _E / (_E + 1.0)),        # 1 / (1 + 1/e)
+    (-1.0, -1.0 / (_E + 1.0)),     # -1 / (1 + e)
+    (_LN3, 0.75 * _LN3),           # sigmoid(ln 3) = 1 / (1 + 1/3) = 3/4
+    (-_LN3, -0.25 * _LN3),         # sigmoid(-ln 3) = 1 / (1 + 3) = 1/4
+    (_LN4, 0.8 * _LN4),            # sigmoid(ln 4) = 1 / (1 + 1/4) = 4/5
+]
+
+
+def check_silu_hand(lib, orc=oracle):
+    got = orc.silu(np.array([c[0] for c in SILU_HAND]))
+    want = np.array([c[1] for c in SILU_HAND])
+    assert np.allclose(got, want, rtol=1e-15, atol=0), (got, want)
+
+
+def check_silu_mul_hand(lib, orc=oracle):
+    """Gate = the first half of each row, up = the second: gate (ln 3, -ln 3)
+    with up (4, -2) gives (3/4 ln 3) 4 = 3 ln 3 and (-1/4 ln 3)(-2) = ln 3 / 2;
+    a 2 x 6 case mixes 0, +-1, ln 3 and ln 4 gates with signed ups."""
+    y = np.array([[_LN3, -_LN3, 4.0, -2.0]])
+    got = orc.silu_mul(y, 2)
+    assert np.allclose(got, [[3.0 * _LN3, 0.5 * _LN3]], rtol=1e-15, atol=0), got
+    y = np.array([[0.0, 1.0, -1.0, 5.0, 2.0, 3.0], [_LN4, 0.0, _LN3, 1.0, -7.0, 2.0]])
+    want = [[0.0, 2.0 * _E / (_E + 1.0), -3.0 / (_E + 1.0)], [0.8 * _LN4, 0.0, 1.5 * _LN3]]
+    got = orc.silu_mul(y, 3)
+    assert np.allclose(got, want, rtol=1e-15, atol=0), got
+
+
+def check_silu_properties(lib, orc=oracle):
+    """silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x) = 1); silu(x) -> x as
+    x -> +inf and -> 0 as x -> -inf, with the exact tails x e^-x / (1 + e^-x)
+    and -|x| e^-|x| / (1 + e^-|x|) at |x| = 40; silu_mul of a row [x, 1] is
+    silu(x)."""
+    rng = np.random.Generator(np.random.PCG64(81))
+    x = rng.standard_normal(2000) * 8.0
+    assert np.allclose(orc.silu(x) - orc.silu(-x), x, rtol=1e-13, atol=1e-14)
+    t = math.exp(-40.0)
+    assert math.isclose(float(orc.silu(40.0)), 40.0 - 40.0 * t / (1.0 + t), rel_tol=1e-15)
+    assert math.isclose(float(orc.silu(-40.0)), -40.0 * t / (1.0 + t), rel_tol=1e-12)
+    assert float(orc.silu(-1000.0)) == 0.0
+    y = np.stack([x[:50], np.ones(50)], axis=1)
+    assert np.array_equal(orc.silu_mul(y, 1)[:, 0], orc.silu(x[:50]))
+
+
+def check_gate_up_vs_brute(lib, orc=oracle):
+    """The fused gate_up composition pairs output column j with product
+    columns j (gate) and d + j (up): its gate and up columns equal the exact
+    rational brute force of the product, and its output is silu_mul of that
+    product, for all columns and for a selection in another order."""
+    d = 4
+    p = arrays_any_format(2, 2 * d, 64, 32, "w4", "bf16", "bf16", True, seed=71)
+    exact, _ = brute_force(p)
+    y = np.array([[float(v) for v in row] for row in exact])
+    for cols in (None, [3, 0, 2]):
+        c = np.arange(d) if cols is None else np.array(cols)
+        out, g, u, bg, bu = orc.gate_up(p.M, d, p.K, p.G, p.wfmt, p.afmt, p.sfmt, p.has_zp, p.A, None, p.W, p.S,
+                                        p.Z, cols=cols, lib=lib)
+        assert np.allclose(g, y[:, c], rtol=1e-12, atol=1e-15) and np.allclose(u, y[:, d + c], rtol=1e-12, atol=1e-15)
+        assert np.allclose(out, orc.silu_mul(np.concatenate([y[:, c], y[:, d + c]], axis=1), len(c)),
+                           rtol=1e-12, atol=1e-15)
+        assert np.all(bg >= np.abs(g) * (1 - 1e-12)) and np.all(bu >= np.abs(u) * (1 - 1e-12))
+
+
 def check_round_bf16_hand(lib):
     """Worked cases of round to nearest even into bf16 (8 significant bits):
     exact values stay, a tie goes to the even neighbour, anything past the
@@ -637,6 +707,8 @@ def all_checks():
             ("fp8_gemm_brute_1", lambda lib: check_fp8_gemm_brute(lib, 1)),
             ("fp8_blockwise_uniform", check_fp8_blockwise_uniform)]
     out += [("moe_align_hand", check_moe_align_hand), ("moe_vs_brute", check_moe_vs_brute)]
+    out += [("silu_hand", check_silu_hand), ("silu_mul_hand", check_silu_mul_hand),
+            ("silu_properties", check_silu_properties), ("gate_up_vs_brute", check_gate_up_vs_brute)]
     out += [("round_bf16_hand", check_round_bf16_hand), ("round_bf16_vs_torch", check_round_bf16_vs_torch),
             ("dequant_bf16", check_dequant_bf16)]
     return out

@@ -87,20 +87,31 @@ def test_mutant_is_caught(tmp_path, source, name, orig, mut):
     assert caught, f"mutant {name} passed every pin"
 
 
-# Planted mistakes in the Python half of the oracle (the MoE composition in
-# oracle/__init__.py): a mutated copy of the module is loaded under another
-# name and run through the MoE pins.
+# Planted mistakes in the Python half of the oracle (the MoE composition and
+# the SwiGLU gate step in oracle/__init__.py): a mutated copy of the module is
+# loaded under another name and run through the pins of the function mutated.
+_MOE_PINS = (pins.check_moe_align_hand, pins.check_moe_vs_brute)
+_SILU_PINS = (pins.check_silu_hand, pins.check_silu_mul_hand, pins.check_silu_properties, pins.check_gate_up_vs_brute)
 PY_MUTANTS = [
-    ("moe_token_index", "tokens = slots[pick] // topk", "tokens = slots[pick] % topk"),
-    ("moe_pad_down", "total += -(-counts[e] // block) * block", "total += (counts[e] // block) * block"),
-    ("moe_tile_count", "tile_experts += [e] * (-(-counts[e] // block))", "tile_experts += [e] * (counts[e] // block + 1)"),
-    ("moe_sentinel", "sorted_ids = [numel] * total", "sorted_ids = [0] * total"),
-    ("moe_expert_shift", "pick = np.nonzero(ids[slots] == e)[0]", "pick = np.nonzero(ids[slots] == (e + 1) % W.shape[0])[0]"),
+    ("moe_token_index", "tokens = slots[pick] // topk", "tokens = slots[pick] % topk", _MOE_PINS),
+    ("moe_pad_down", "total += -(-counts[e] // block) * block", "total += (counts[e] // block) * block", _MOE_PINS),
+    ("moe_tile_count", "tile_experts += [e] * (-(-counts[e] // block))", "tile_experts += [e] * (counts[e] // block + 1)",
+     _MOE_PINS),
+    ("moe_sentinel", "sorted_ids = [numel] * total", "sorted_ids = [0] * total", _MOE_PINS),
+    ("moe_expert_shift", "pick = np.nonzero(ids[slots] == e)[0]", "pick = np.nonzero(ids[slots] == (e + 1) % W.shape[0])[0]",
+     _MOE_PINS),
+    ("silu_exp_sign", "return x / (1.0 + np.exp(-x))", "return x / (1.0 + np.exp(x))", _SILU_PINS),
+    ("silu_identity", "return x / (1.0 + np.exp(-x))", "return x + 0.0 * np.exp(-x)", _SILU_PINS),
+    ("silu_mul_halves_swapped", "return silu(y[:, :d]) * y[:, d:]", "return silu(y[:, d:]) * y[:, :d]", _SILU_PINS),
+    ("silu_mul_up_shifted", "return silu(y[:, :d]) * y[:, d:]", "return silu(y[:, :d]) * np.roll(y[:, d:], 1, axis=1)",
+     _SILU_PINS),
+    ("gate_up_pairing", "both = np.concatenate([cols, cols + d])", "both = np.concatenate([cols, (cols + 1) % d + d])",
+     _SILU_PINS),
 ]
 
 
-@pytest.mark.parametrize("name,orig,mut", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
-def test_python_mutant_is_caught(name, orig, mut):
+@pytest.mark.parametrize("name,orig,mut,checks", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_is_caught(name, orig, mut, checks):
     import importlib.util
     path = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
     with open(path) as f:
@@ -112,9 +123,9 @@ def test_python_mutant_is_caught(name, orig, mut):
     exec(compile(src.replace(orig, mut), path, "exec"), mod.__dict__)
     lib = oracle.load()
     caught = []
-    for check in (pins.check_moe_align_hand, pins.check_moe_vs_brute):
+    for check in checks:
         try:
             check(lib, orc=mod)
         except (AssertionError, ValueError, IndexError):
             caught.append(check.__name__)
-    assert caught, f"mutant {name} passed every MoE pin"
+    assert caught, f"mutant {name} passed every pin of its function"

@@ -78,6 +78,17 @@ def lib():
             L.qgemm_run_ex.argtypes = run_args + [c_int, c_int]
             L.qgemm_run_noalloc.restype = c_int
             L.qgemm_run_noalloc.argtypes = [c_int] * 6 + [vp] * 7
+            L.qgemm_pack_gate_up.restype = c_int
+            L.qgemm_pack_gate_up.argtypes = [vp, vp, c_int, c_int, c_int, vp]
+            L.qgemm_gate_up_plan.restype = c_int
+            L.qgemm_gate_up_plan.argtypes = [c_int] * 7 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                                           ctypes.POINTER(c_size)]
+            L.qgemm_gate_up_workspace_bytes.restype = c_size
+            L.qgemm_gate_up_workspace_bytes.argtypes = [c_int] * 5
+            L.qgemm_run_gate_up_silu.restype = c_int
+            L.qgemm_run_gate_up_silu.argtypes = [c_int] * 6 + [vp] * 6 + [c_size, vp]
+            L.qgemm_run_gate_up_silu_ex.restype = c_int
+            L.qgemm_run_gate_up_silu_ex.argtypes = [c_int] * 6 + [vp] * 6 + [c_size, vp, c_int, c_int]
             L.qgemm_moe_max_tiles.restype = c_int
             L.qgemm_moe_max_tiles.argtypes = [c_int] * 3
             L.qgemm_moe_default_block.restype = c_int
@@ -239,6 +250,51 @@ def stream_read(buf, nbytes: int, out, blocks: int, stream=None):
                                  stream if stream is not None else _stream(buf.device))
     if st != OK:
         raise QGemmError(st, "qgemm_stream_read")
+
+
+def pack_gate_up(w_canonical, K: int, d: int, prec: int = W4_A_BF16):
+    """Pack a fused gate_up weight (canonical int4 words [K/8, 2d], gate
+    columns first, on a GPU) in gate-up order for run_gate_up_silu."""
+    import torch
+    nbytes = packed_bytes(K, 2 * d, prec)
+    if nbytes == 0:
+        raise QGemmError(EINVAL, "qgemm_packed_bytes")
+    rows = nbytes // (4 * padded_cols(2 * d))
+    out = torch.empty((rows, padded_cols(2 * d)), dtype=torch.int32, device=w_canonical.device)
+    st = lib().qgemm_pack_gate_up(_ptr(w_canonical), _ptr(out), K, d, prec, _stream(w_canonical.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_pack_gate_up")
+    return out
+
+
+def gate_up_plan(M: int, d: int, K: int, G: int, prec: int, force_path: int = PATH_AUTO, force_nsplit: int = 0):
+    path, ns, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    st = lib().qgemm_gate_up_plan(M, d, K, G, prec, force_path, force_nsplit, ctypes.byref(path), ctypes.byref(ns),
+                                  ctypes.byref(ws))
+    if st != OK:
+        raise QGemmError(st, "qgemm_gate_up_plan")
+    return path.value, ns.value, ws.value
+
+
+def run_gate_up_silu(A, w_packed, scales, *, d: int, G: int, prec: int = W4_A_BF16, zeros=None, out=None, ws=None,
+                     force_path: int = PATH_AUTO, force_nsplit: int = 0, stream=None):
+    """out[M, d] = silu(gate) * up of the fused gate_up product of A [M, K]
+    (bf16) with a pack_gate_up weight (see include/qgemm.h)."""
+    import torch
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, d), dtype=out_dtype(prec), device=A.device)
+    _, _, need = gate_up_plan(max(M, 1), d, K, G, prec, force_path, force_nsplit)
+    if ws is None:
+        ws = workspace(need, A.device, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().qgemm_run_gate_up_silu_ex(M, d, K, G, prec, int(zeros is not None), _ptr(A), _ptr(w_packed),
+                                         _ptr(scales), _ptr(zeros), _ptr(out), _ptr(ws), ws_bytes,
+                                         stream if stream is not None else _stream(A.device), force_path,
+                                         force_nsplit)
+    if st != OK:
+        raise QGemmError(st, "qgemm_run_gate_up_silu")
+    return out
 
 
 def run_noalloc(A, w_packed, scales, *, N: int, G: int, prec: int, zeros=None, a_scales=None, out=None,

@@ -42,6 +42,7 @@ struct GemvArgs {
   float *partial;          // [nsplit][M][Np] (nsplit > 1)
   int M, N, K, G, Np;
   int ngroups, nsplit;
+  int gu_d;                // > 0: gate-up packed product of N = 2 gu_d columns, out [M][gu_d] = silu(g) * u
   // grouped (MoE) launches only: routed rows per row block, each block's
   // expert, the padded routed-row count, and each expert's weight stride
   const int *sorted_ids;   // [row blocks * MB] slot ids (>= M: padding)
@@ -87,6 +88,7 @@ struct SmallArgs {
   float *partial;          // [nsplit][M][Np] (nsplit > 1)
   int M, N, K, Np;
   int ngroups, nsplit;     // K / 128 groups split into nsplit slices
+  int gu_d;                // see GemvArgs
   // grouped (MoE) launches only (see GemvArgs)
   const int *sorted_ids, *tile_experts, *num_post_pad;
   int topk, arows;         // activation row = slot / topk, of arows rows
@@ -114,8 +116,15 @@ hipError_t launch_gemv_i8(int wfmt, bool zp, bool dq, int mb, const GemvArgs &a,
 hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStream_t stream);
 // mb = ceil(M / 16) row blocks; grid (Np / 64, nsplit)
 hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t stream);
-hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np,
+// gu_d > 0 (int4 only): gate-up column order for a fused gate_up product of
+// N = 2 gu_d columns (see gate_up_column)
+hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np, int gu_d,
                        hipStream_t stream);
+// fixed-order z-split reduce followed by the SwiGLU gate step: out[m][j]
+// (j < d, row stride d) = silu(g) * u of the summed partials of packed
+// columns 64 (j / 32) + j % 32 (g) and that + 32 (u)
+hipError_t launch_reduce_gate_up(int ofmt, const float *partial, void *out, int M, int d, int Np, int nsplit,
+                                 hipStream_t stream);
 // Aq[m][k], a_scale[m][k / G] = per-group int8 quantization of A[M][K]
 // (float32); G in {32, 128}, K % G == 0, A 16-byte and Aq 4-byte aligned.
 hipError_t launch_quant(const float *A, int8_t *Aq, float *a_scale, int M, int K, int G, hipStream_t stream);
@@ -137,6 +146,21 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *out, int 
 // out[m][n] = sum_{z = 0..nsplit-1} partial[z][m][n], in that order.
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t stream);
+
+// Gate-up column order of a packed fused gate_up product (d = gate columns,
+// N = 2d total, d % 32 == 0): packed column n (tile t = n / 64, j = n % 64)
+// holds canonical column 32t + j for j < 32 (a gate column) and d + 32t + j -
+// 32 for j >= 32 (its up column); N when 32t + j % 32 >= d (no column).
+__host__ __device__ inline int gate_up_column(int n, int d, int N) {
+  const int t = n / kTileCols, j = n % kTileCols;
+  const int c = 32 * t + (j & 31);
+  if (c >= d) return N;
+  return j < 32 ? c : d + c;
+}
+
+// SiLU (x * sigmoid(x)) in float32; exp(-x) overflows to inf for x below
+// about -88, giving -0 (the limit).
+__device__ inline float silu_f32(float x) { return x / (1.0f + expf(-x)); }
 
 // Balanced contiguous partition of `count` items into `parts`: part z gets
 // [begin, begin + size).

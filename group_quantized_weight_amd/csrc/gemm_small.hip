@@ -131,7 +131,10 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_small_kernel(SmallArgs a)
   // in or all out; a lane past N reads column 0's and its results are
   // dropped)
   const int ncol = tile * kTileCols + 4 * li;
-  const int scol = ncol < a.N ? ncol : 0;
+  // canonical column of the scales and zero-points (a gate-up packed
+  // product holds gate and up columns in the tile's halves)
+  const int lcol = a.gu_d > 0 ? gate_up_column(ncol, a.gu_d, a.N) : ncol;
+  const int scol = lcol < a.N ? lcol : 0;
   const __amdgpu_buffer_rsrc_t s_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void *)Sb, (short)0, a.ngroups * a.N * 2, kBufWord3s);
   const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -292,6 +295,25 @@ groups_done:
       f32x4_s v = (f32x4_s){acc[fm][0][r], acc[fm][1][r], acc[fm][2][r], acc[fm][3][r]};
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) v += *(const f32x4_s *)&red[(((w - 1) * MB + fm) * 16 + 4 * lk + r) * 64 + 4 * li];
+      if (a.gu_d > 0 && a.nsplit == 1) {
+        // gate-up packed product: lane li < 8 holds gate columns 4 li .. +3
+        // of the tile, lane li + 8 (same row) their up columns; SwiGLU's gate
+        // step gives output columns 32 tile + 4 li .. +3 of [M][gu_d]
+        f32x4_s u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u[c] = __shfl_xor(v[c], 8);
+        const int nout = 32 * tile + 4 * li;
+        if (row >= a.M || li >= 8 || nout >= a.gu_d) continue;
+        f32x4_s g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) g[c] = silu_f32(v[c]) * u[c];
+        const size_t o = (size_t)row * a.gu_d + nout;
+        if constexpr (OF == O_BF16)
+          *(u32x2_s *)((uint16_t *)a.out + o) = (u32x2_s){bf16x2_bits(g[0], g[1]), bf16x2_bits(g[2], g[3])};
+        else
+          *(f32x4_s *)((float *)a.out + o) = g;
+        continue;
+      }
       if (row >= a.M) continue;
       if (a.nsplit > 1) {
         *(f32x4_s *)&a.partial[((size_t)z * a.M + row) * a.Np + n] = v;

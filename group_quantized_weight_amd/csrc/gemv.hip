@@ -229,7 +229,11 @@ void gemv_kernel(GemvArgs a) {
   const int lk = lane >> 4, c4 = lane & 15;
   const int n0 = blockIdx.x * kTileCols;
   const int ncol = n0 + 4 * c4;                       // first of this lane's 4 columns
-  const bool col_ok = ncol < a.N;
+  // the canonical column of its scales and zero-points: the packed column,
+  // or, in a gate-up packed product, the gate or up column it holds (a.N:
+  // none; the lane's 4 columns lie in one half of the tile)
+  const int lcol = a.gu_d > 0 ? gate_up_column(ncol, a.gu_d, a.N) : ncol;
+  const bool col_ok = lcol < a.N;
   const int m0 = blockIdx.y * MB;
   const int z = blockIdx.z;
   const int R = a.K / KPW;                            // word-rows of the whole matrix
@@ -302,7 +306,7 @@ void gemv_kernel(GemvArgs a) {
   // flow (a lane past column N reads a clamped, valid address and masks the
   // value at use), so issuing it never waits on the weight loads in flight.
   const bool vec_s = (a.N & 3) == 0;                // 4 scales per lane in one load
-  const int scol = col_ok ? ncol : 0;
+  const int scol = col_ok ? lcol : 0;
   constexpr int SB = SF == S_BF16 ? 2 : 4;          // bytes per scale
   const __amdgpu_buffer_rsrc_t s_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void *)Sb, (short)0, a.ngroups * a.N * SB, kBufferWord3);
@@ -354,11 +358,11 @@ void gemv_kernel(GemvArgs a) {
         for (int c = 0; c < 4; ++c) s[c] = __uint_as_float(sv[slot][gi][c]);
       }
     } else {  // N not a multiple of 4: one scale at a time (not prefetched)
-      const size_t si = (size_t)(gb + gl) * a.N + ncol;
+      const size_t si = (size_t)(gb + gl) * a.N + lcol;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         s[c] = 0.f;
-        if (ncol + c < a.N) {
+        if (lcol + c < a.N) {
           if constexpr (SF == S_BF16)
             s[c] = __uint_as_float((uint32_t)((const uint16_t *)Sb)[si + c] << 16);
           else
@@ -466,7 +470,7 @@ void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           zn[c] = WF == W8 ? 0u : 8u;
-          if constexpr (ZP) zn[c] = (zv[u][gi] >> (4 * ((ncol & 7) + c))) & 0xFu;
+          if constexpr (ZP) zn[c] = (zv[u][gi] >> (4 * ((lcol & 7) + c))) & 0xFu;
         }
         float pf[MB][4];
 #pragma unroll
@@ -589,6 +593,31 @@ void gemv_kernel(GemvArgs a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
+  if (a.gu_d > 0 && a.nsplit == 1) {
+    // gate-up packed product: SwiGLU's gate step on the tile's packed
+    // columns j (gate) and 32 + j (up), written to output column 32 t + j of
+    // [M][gu_d] (with a K-split the partials below keep the packed columns
+    // and the reduce applies it)
+    for (int t = threadIdx.x; t < MB * 32; t += kGemvThreads) {
+      const int m = t / 32, j = t % 32;
+      const int orow = out_row(m);
+      const int n = 32 * (int)blockIdx.x + j;
+      if (orow >= a.M || n >= a.gu_d) continue;
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGemvWaves; ++w) {
+        g += s_red[((size_t)w * MB + m) * kTileCols + j];
+        u += s_red[((size_t)w * MB + m) * kTileCols + 32 + j];
+      }
+      const float v = silu_f32(g) * u;
+      const size_t o = (size_t)orow * a.gu_d + n;
+      if constexpr (OF == O_BF16)
+        ((uint16_t *)a.out)[o] = f32_to_bf16(v);
+      else
+        ((float *)a.out)[o] = v;
+    }
+    return;
+  }
   for (int t = threadIdx.x; t < MB * kTileCols; t += kGemvThreads) {
     const int m = t / kTileCols, col = t % kTileCols;
     const int orow = out_row(m);

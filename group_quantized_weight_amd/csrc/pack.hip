@@ -19,6 +19,13 @@
 //   int8: the codes of k = 4r..4r+3 (byte j = k offset j).
 //
 // Columns n in [N, Np) are written as zero words.
+//
+// Gate-up order (gu_d = d > 0, N = 2d, d % 32 == 0): the canonical matrix
+// holds a fused gate_up product's columns, gate columns 0..d-1 then up columns
+// d..2d-1 (the layout of the page "quantization-and-fused-kernels", section
+// 五.2). Packed tile t then holds gate columns 32t..32t+31 in its first 32
+// columns and up columns d+32t..d+32t+31 in its last 32 (gate_up_column), so
+// that one workgroup produces both inputs of its output columns 32t..32t+31.
 #include "common.h"
 
 namespace qg {
@@ -28,13 +35,14 @@ __device__ __forceinline__ size_t packed_index(int r, int n, int rows) {
 }
 
 __global__ void pack_w4_kernel(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst, int N,
-                               int Np, int rows) {
+                               int Np, int rows, int gu_d) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   const int r = blockIdx.y;
   if (n >= Np) return;
   uint32_t out = 0;
-  if (n < N) {
-    const uint32_t w = src[(size_t)r * N + n];
+  const int c = gu_d > 0 ? gate_up_column(n, gu_d, N) : n;  // canonical column (N: none)
+  if (c < N) {
+    const uint32_t w = src[(size_t)r * N + c];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t code = (w >> (4 * j)) & 0xFu;
@@ -59,12 +67,12 @@ __global__ void pack_w8_kernel(const int8_t *__restrict__ src, uint32_t *__restr
   dst[packed_index(r, n, rows)] = out;
 }
 
-hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np,
+hipError_t launch_pack(int wfmt, const void *src, uint32_t *dst, int K, int N, int Np, int gu_d,
                        hipStream_t stream) {
   const int rows = wfmt == W4 ? K / 8 : K / 4;
   dim3 block(256), grid((Np + 255) / 256, rows);
   if (wfmt == W4)
-    pack_w4_kernel<<<grid, block, 0, stream>>>((const uint32_t *)src, dst, N, Np, rows);
+    pack_w4_kernel<<<grid, block, 0, stream>>>((const uint32_t *)src, dst, N, Np, rows, gu_d);
   else
     pack_w8_kernel<<<grid, block, 0, stream>>>((const int8_t *)src, dst, N, Np, rows);
   return hipGetLastError();

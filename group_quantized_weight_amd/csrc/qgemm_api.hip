@@ -276,7 +276,7 @@ int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, 
   if ((f.w == W4 ? K / 8 : K / 4) > 65535 || padded_cols(N) > (size_t)INT_MAX) return QG_EUNSUPPORTED;
   if (!aligned16(w_canonical) || !aligned16(w_packed)) return QG_EALIGN;
   drop_pending_error();
-  const hipError_t e = launch_pack(f.w, w_canonical, (uint32_t *)w_packed, K, N, (int)padded_cols(N),
+  const hipError_t e = launch_pack(f.w, w_canonical, (uint32_t *)w_packed, K, N, (int)padded_cols(N), 0,
                                    (hipStream_t)stream);
   return e == hipSuccess ? QG_OK : QG_EHIP;
 }
@@ -301,10 +301,12 @@ size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec) {
   return ws;
 }
 
-int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const void *A,
-                 const void *a_scales, const void *w_packed, const void *scales, const void *zeros,
-                 void *out, void *workspace, size_t workspace_bytes, void *stream, int force_path,
-                 int force_nsplit) {
+// The product of qgemm_run_ex; gu_d > 0: a gate-up packed product of N =
+// 2 gu_d columns whose SwiGLU gate step is applied in the epilogue (out is
+// [M][gu_d]; bf16 activations on the GEMV or small-M path only).
+static int run_common(int M, int N, int K, int group, int prec, int has_zp, const void *A, const void *a_scales,
+                      const void *w_packed, const void *scales, const void *zeros, void *out, void *workspace,
+                      size_t workspace_bytes, void *stream, int force_path, int force_nsplit, int gu_d) {
   Formats f;
   int st = check_shape(M, N, K, group, prec, has_zp, f);
   if (st != QG_OK) return st;
@@ -319,6 +321,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
   Plan p;
   st = make_plan(M, N, K, group, f, force_path, force_nsplit, p);
   if (st != QG_OK) return st;
+  if (gu_d > 0 && (p.path == QG_PATH_GEMM || f.a != A_BF16)) return QG_EUNSUPPORTED;
   if (p.ws > 0) {
     if (!workspace || workspace_bytes < p.ws) return QG_EWORKSPACE;
     if (!aligned16(workspace)) return QG_EALIGN;
@@ -348,6 +351,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.M = M; a.N = N; a.K = K; a.G = group; a.Np = Np;
     a.ngroups = K / group;
     a.nsplit = p.nsplit;
+    a.gu_d = gu_d;
     const dim3 grid(p.tiles_x, p.mblocks, p.nsplit);
     e = f.a == A_I8 ? launch_gemv_i8(f.w, has_zp != 0, p.dq_fused, p.mb, a, grid, p.lds, s)
                     : launch_gemv(f.w, f.a, f.s, f.o, has_zp != 0, p.mb, a, grid, p.lds, s);
@@ -374,6 +378,7 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.M = M; a.N = N; a.K = K; a.Np = Np;
     a.ngroups = K / 128;
     a.nsplit = p.nsplit;
+    a.gu_d = gu_d;
     e = launch_gemm_small(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.nsplit), s);
   } else {
     GemmArgs a;
@@ -392,8 +397,71 @@ int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const voi
     a.nsplit = p.nsplit;
     e = launch_gemm(f.o, has_zp != 0, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), s);
   }
-  if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, partial, out, M, N, Np, p.nsplit, s);
+  if (e == hipSuccess && p.nsplit > 1)
+    e = gu_d > 0 ? launch_reduce_gate_up(f.o, partial, out, M, gu_d, Np, p.nsplit, s)
+                 : launch_reduce(f.o, partial, out, M, N, Np, p.nsplit, s);
   return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_run_ex(int M, int N, int K, int group, int prec, int has_zp, const void *A,
+                 const void *a_scales, const void *w_packed, const void *scales, const void *zeros,
+                 void *out, void *workspace, size_t workspace_bytes, void *stream, int force_path,
+                 int force_nsplit) {
+  return run_common(M, N, K, group, prec, has_zp, A, a_scales, w_packed, scales, zeros, out, workspace,
+                    workspace_bytes, stream, force_path, force_nsplit, 0);
+}
+
+// ---- fused gate_up product with SwiGLU's gate step ----
+
+static bool gate_up_prec(int prec) { return prec == QG_W4_A_BF16 || prec == QG_W4_A_BF16_OF32; }
+
+int qgemm_pack_gate_up(const void *w_canonical, void *w_packed, int K, int d, int prec, void *stream) {
+  if (!gate_up_prec(prec)) return QG_EUNSUPPORTED;
+  if (K <= 0 || d <= 0 || !w_canonical || !w_packed) return QG_EINVAL;
+  if (K % 8 != 0 || d % 32 != 0) return QG_EINVAL;
+  if (d > INT_MAX / 2 || K / 8 > 65535 || padded_cols(2 * d) > (size_t)INT_MAX) return QG_EUNSUPPORTED;
+  if (!aligned16(w_canonical) || !aligned16(w_packed)) return QG_EALIGN;
+  drop_pending_error();
+  const hipError_t e = launch_pack(W4, w_canonical, (uint32_t *)w_packed, K, 2 * d, (int)padded_cols(2 * d), d,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_gate_up_plan(int M, int d, int K, int group, int prec, int force_path, int force_nsplit, int *path,
+                       int *nsplit, size_t *workspace_bytes) {
+  if (!gate_up_prec(prec)) return QG_EUNSUPPORTED;
+  if (d <= 0 || d % 32 != 0) return QG_EINVAL;
+  if (d > INT_MAX / 2) return QG_EUNSUPPORTED;
+  int pth = 0;
+  const int st = qgemm_plan(M, 2 * d, K, group, prec, force_path, force_nsplit, &pth, nsplit, workspace_bytes);
+  if (st != QG_OK) return st;
+  if (pth == QG_PATH_GEMM) return QG_EUNSUPPORTED;
+  if (path) *path = pth;
+  return QG_OK;
+}
+
+size_t qgemm_gate_up_workspace_bytes(int M, int d, int K, int group, int prec) {
+  size_t ws = 0;
+  if (qgemm_gate_up_plan(M, d, K, group, prec, QG_PATH_AUTO, 0, nullptr, nullptr, &ws) != QG_OK) return 0;
+  return ws;
+}
+
+int qgemm_run_gate_up_silu_ex(int M, int d, int K, int group, int prec, int has_zp, const void *A,
+                              const void *w_packed, const void *scales, const void *zeros, void *out,
+                              void *workspace, size_t workspace_bytes, void *stream, int force_path,
+                              int force_nsplit) {
+  if (!gate_up_prec(prec)) return QG_EUNSUPPORTED;
+  if (d <= 0 || d % 32 != 0) return QG_EINVAL;
+  if (d > INT_MAX / 2) return QG_EUNSUPPORTED;
+  return run_common(M, 2 * d, K, group, prec, has_zp, A, nullptr, w_packed, scales, zeros, out, workspace,
+                    workspace_bytes, stream, force_path, force_nsplit, d);
+}
+
+int qgemm_run_gate_up_silu(int M, int d, int K, int group, int prec, int has_zp, const void *A,
+                           const void *w_packed, const void *scales, const void *zeros, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return qgemm_run_gate_up_silu_ex(M, d, K, group, prec, has_zp, A, w_packed, scales, zeros, out, workspace,
+                                   workspace_bytes, stream, QG_PATH_AUTO, 0);
 }
 
 int qgemm_run(int M, int N, int K, int group, int prec, int has_zp, const void *A,

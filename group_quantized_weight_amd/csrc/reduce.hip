@@ -52,6 +52,49 @@ __global__ __launch_bounds__(128) void reduce_kernel(const float *__restrict__ p
   }
 }
 
+// Gate-up packed product (d gate columns, d % 32 == 0): thread = 4 adjacent
+// output columns j .. j + 3 of one row; their gate sums are those of packed
+// columns p = 64 (j / 32) + j % 32 .. +3 and their up sums those of p + 32,
+// each added over z in order; out[m][j] = silu(gate) * up, row stride d
+// (SwiGLU's gate step, page "quantization-and-fused-kernels", section 五.2).
+template <int OF>
+__global__ __launch_bounds__(128) void reduce_gate_up_kernel(const float *__restrict__ part, void *__restrict__ out,
+                                                             int M, int d, int Np, int nsplit) {
+  const int j = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (j >= d) return;
+  const int pg = 64 * (j / 32) + j % 32;
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    const float *p = part + (size_t)m * Np + pg;
+    const size_t zstride = (size_t)M * Np;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < nsplit; ++z) {
+      const float4 a = *(const float4 *)(p + (size_t)z * zstride);
+      const float4 b = *(const float4 *)(p + (size_t)z * zstride + 32);
+      g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+      u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+    }
+    const float r[4] = {silu_f32(g.x) * u.x, silu_f32(g.y) * u.y, silu_f32(g.z) * u.z, silu_f32(g.w) * u.w};
+    const size_t o = (size_t)m * d + j;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (OF == O_BF16)
+        ((uint16_t *)out)[o + c] = to_bf16(r[c]);
+      else
+        ((float *)out)[o + c] = r[c];
+    }
+  }
+}
+
+hipError_t launch_reduce_gate_up(int ofmt, const float *partial, void *out, int M, int d, int Np, int nsplit,
+                                 hipStream_t st) {
+  dim3 grid((d + 4 * 128 - 1) / (4 * 128), M < 65535 ? M : 65535);
+  if (ofmt == O_BF16)
+    reduce_gate_up_kernel<O_BF16><<<grid, 128, 0, st>>>(partial, out, M, d, Np, nsplit);
+  else
+    reduce_gate_up_kernel<O_F32><<<grid, 128, 0, st>>>(partial, out, M, d, Np, nsplit);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t st) {
   dim3 grid((N + 4 * 128 - 1) / (4 * 128), M < 65535 ? M : 65535);

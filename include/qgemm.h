@@ -158,6 +158,45 @@ int qgemm_run(int M, int N, int K, int group, int prec, int has_zp, const void *
               const void *a_scales, const void *w_packed, const void *scales, const void *zeros,
               void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Fused gate_up product with SwiGLU's gate step, for a Llama-style FFN
+ * (page "quantization-and-fused-kernels" (arganzheng.life), section 五.2:
+ * the gate_up GEMM writes [M][2d], gate columns first, and
+ * out = silu(gate) * up with silu(x) = x * sigmoid(x) = x / (1 + e^-x); the
+ * MoE pipeline of section 六.1 has the same step between its two GEMMs).
+ * Here the step runs in the product's epilogue: out [M][d] is written once
+ * and the [M][2d] product never reaches memory.
+ *
+ * The weight is one canonical int4 matrix of N = 2d columns (gate columns
+ * 0..d-1, up columns d..2d-1), scales [K/G][2d] bf16 and zero-points
+ * [K/G][2d/8] in that canonical column order, as for qgemm_run.
+ *   d: output columns, d % 32 == 0; prec: QG_W4_A_BF16 (bf16 out) or
+ *   QG_W4_A_BF16_OF32 (float32 out); A: bf16 [M][K].
+ * qgemm_pack_gate_up packs it in gate-up order: packed tile t (64 columns)
+ * holds gate columns 32t..32t+31 and then up columns d+32t..d+32t+31, so
+ * that one workgroup makes both inputs of each of its outputs; the buffer
+ * has qgemm_packed_bytes(K, 2d, prec) bytes. The product runs on the GEMV or
+ * small-M path (the plan of qgemm_plan for N = 2d); a problem that would take
+ * the tiled GEMM (M > 64 with group 128) returns QG_EUNSUPPORTED.
+ * out[m][j] = silu(y[m][j]) * y[m][d + j] with y the float32 product of
+ * qgemm_run (the same sums in the same order), the step in float32 (expf),
+ * then one rounding to the output type. With a K-split the reduce kernel
+ * applies the step after its fixed-order sum. Workspace, errors, streams and
+ * reproducibility are those of qgemm_run.
+ */
+int qgemm_pack_gate_up(const void *w_canonical, void *w_packed, int K, int d, int prec, void *stream);
+int qgemm_gate_up_plan(int M, int d, int K, int group, int prec, int force_path, int force_nsplit, int *path,
+                       int *nsplit, size_t *workspace_bytes);
+size_t qgemm_gate_up_workspace_bytes(int M, int d, int K, int group, int prec);
+int qgemm_run_gate_up_silu(int M, int d, int K, int group, int prec, int has_zp, const void *A,
+                           const void *w_packed, const void *scales, const void *zeros, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+/* qgemm_run_gate_up_silu with an explicit plan; for tests and tuning. */
+int qgemm_run_gate_up_silu_ex(int M, int d, int K, int group, int prec, int has_zp, const void *A,
+                              const void *w_packed, const void *scales, const void *zeros, void *out,
+                              void *workspace, size_t workspace_bytes, void *stream, int force_path,
+                              int force_nsplit);
+
 /* Bytes of the workspace that qgemm_run_noalloc owns on each GPU. */
 #define QG_NOALLOC_SCRATCH_BYTES (64u << 20)
 

@@ -274,6 +274,25 @@ def test_moe_validation():
     assert r(K=1024, ws=None, wsb=0) == qg.EWORKSPACE and r(K=1024, ws=P, wsb=need - 1) == qg.EWORKSPACE
 
 
+def test_gate_up_validation():
+    L = qg.lib()
+    g = lambda M=1, d=512, K=1024, G=128, prec=1, zp=0, A=P, W=P, S=P, Z=None, out=P2, ws=None, wsb=0: \
+        L.qgemm_run_gate_up_silu(M, d, K, G, prec, zp, A, W, S, Z, out, ws, wsb, None)
+    assert g(M=0, A=None, W=None, S=None, out=None) == qg.OK
+    assert g(d=500) == qg.EINVAL and g(d=0) == qg.EINVAL and g(d=-32) == qg.EINVAL
+    for prec in (2, 3, 4, 5, 7, 8):
+        assert g(prec=prec) == qg.EUNSUPPORTED, prec
+    assert g(M=65) == qg.EUNSUPPORTED                       # the tiled GEMM's band
+    assert g(A=None) == qg.EINVAL and g(out=MIS) == qg.EALIGN and g(zp=1, Z=None) == qg.EINVAL
+    assert L.qgemm_gate_up_workspace_bytes(65, 512, 1024, 128, 1) == 0
+    assert L.qgemm_gate_up_workspace_bytes(1, 512, 4096, 128, 1) == L.qgemm_workspace_bytes(1, 1024, 4096, 128, 1)
+    assert L.qgemm_pack_gate_up(P, P2, 1024, 500, 1, None) == qg.EINVAL
+    assert L.qgemm_pack_gate_up(P, P2, 1020, 512, 1, None) == qg.EINVAL
+    assert L.qgemm_pack_gate_up(P, P2, 1024, 512, 3, None) == qg.EUNSUPPORTED
+    assert L.qgemm_pack_gate_up(None, P2, 1024, 512, 1, None) == qg.EINVAL
+    assert L.qgemm_pack_gate_up(MIS, P2, 1024, 512, 1, None) == qg.EALIGN
+
+
 def test_pack_validation():
     L = qg.lib()
     assert L.qgemm_pack(None, P, 64, 8, qg.W4_A_BF16, None) == qg.EINVAL

@@ -321,6 +321,68 @@ def run_fp8(name, steps, warmup, mode):
     return res
 
 
+def run_gate_up(M, steps, warmup, mode, d=14336, K=4096, G=128):
+    """The fused gate_up product with SwiGLU's gate step
+    (qgemm_run_gate_up_silu) on the FFN of an 8B-class layer (d = 14336, K =
+    4096, W4A16 g128), beside the same work unfused: qgemm_run writing the
+    [M][2d] product, then torch's silu and multiply. Algorithmic bytes of the
+    fused step: packed weights, scales, activations and the [M][d] output;
+    the unfused one also writes and reads back the [M][2d] product."""
+    import torch
+    import torch.nn.functional as F
+    import group_quantized_weight_amd as qg
+    import workloads as wl
+    from tests.gpu_util import to_dev
+    prec = qg.W4_A_BF16
+    p = wl.make_problem(M, 2 * d, K, G, prec, False, seed=1200 + M)
+    per_copy = qg.packed_bytes(K, 2 * d, prec) + (K // G) * 2 * d * 2
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / per_copy)))
+    A, _, Wc, S0, _ = to_dev(p)
+    Wg = [qg.pack_gate_up(Wc, K, d, prec)]
+    Wp = [qg.pack(Wc, K, 2 * d, prec)]
+    del Wc
+    Ss = [S0] + [S0.clone() for _ in range(copies - 1)]
+    Wg += [Wg[0].clone() for _ in range(copies - 1)]
+    Wp += [Wp[0].clone() for _ in range(copies - 1)]
+    out = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, 2 * d), dtype=torch.bfloat16, device="cuda")
+    vp = ctypes.c_void_p
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    need = max(qg.lib().qgemm_gate_up_workspace_bytes(M, d, K, G, prec),
+               qg.lib().qgemm_workspace_bytes(M, 2 * d, K, G, prec))
+    ws = qg.workspace(need, A.device, stream)
+    wsp, wsb = (vp(ws.data_ptr()) if ws is not None else None), need
+    L = qg.lib()
+
+    def fused(i):
+        st = L.qgemm_run_gate_up_silu(M, d, K, G, prec, 0, vp(A.data_ptr()), vp(Wg[i % copies].data_ptr()),
+                                      vp(Ss[i % copies].data_ptr()), None, vp(out.data_ptr()), wsp, wsb, stream)
+        if st != 0:
+            raise RuntimeError(f"qgemm_run_gate_up_silu failed: {st}")
+
+    def unfused(i):
+        st = L.qgemm_run(M, 2 * d, K, G, prec, 0, vp(A.data_ptr()), None, vp(Wp[i % copies].data_ptr()),
+                         vp(Ss[i % copies].data_ptr()), None, vp(y.data_ptr()), wsp, wsb, stream)
+        if st != 0:
+            raise RuntimeError(f"qgemm_run failed: {st}")
+        torch.mul(F.silu(y[:, :d]), y[:, d:], out=out2)
+
+    f_ms = time_steps(fused, steps, warmup, mode)
+    u_ms = time_steps(unfused, steps, warmup, mode)
+    path, ns, _ = qg.gate_up_plan(M, d, K, G, prec)
+    fused_bytes = K * 2 * d // 2 + (K // G) * 2 * d * 2 + M * K * 2 + M * d * 2
+    saved = 2 * (M * 2 * d * 2)
+    gbs = fused_bytes / (f_ms * 1e-3) / 1e9
+    del Wg, Wp, Ss, A, out, out2, y
+    torch.cuda.empty_cache()
+    return {"M": M, "d": d, "K": K, "group": G, "path": ["gemv", "gemm", "small"][path], "nsplit": ns,
+            "fused_us": round(f_ms * 1e3, 2), "unfused_us": round(u_ms * 1e3, 2),
+            "fused_bytes": fused_bytes, "bytes_saved": saved, "fused_gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "copies": copies,
+            "unfused": "qgemm_run to [M][2d] bf16, then torch silu and mul"}
+
+
 def run_moe(name, steps, warmup, mode, block=None):
     """Grouped (MoE) W4A16 layer: one step = the align step plus the grouped
     GEMV, over resident activations and routing ids; the expert stacks are
@@ -467,6 +529,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--no-gate-up", action="store_true")
     ap.add_argument("--only", default=None, help="run one named workload only (profiling)")
     ap.add_argument("--force-path", type=int, default=-1, help="with --only: QG_PATH_* to force")
     ap.add_argument("--force-nsplit", type=int, default=0, help="with --only: K-split to force")
@@ -532,6 +595,9 @@ def bench(args):
     if args.only and args.only.startswith("stream:"):
         log(json.dumps(stream_ceiling(int(args.only.split(":")[1]), args.steps, args.warmup, args.mode)))
         return
+    if args.only and args.only.startswith("gate_up:"):
+        log(json.dumps(run_gate_up(int(args.only.split(":")[1]), args.steps, args.warmup, args.mode)))
+        return
     if args.only:
         import workloads as wl
         if args.only in wl.FP8_CONFIGS:
@@ -591,6 +657,14 @@ def bench(args):
             moe.append(r)
             log(f"bench: {name}: {r['us']} us, {r['gbs']} GB/s over {r['experts_used']} experts")
 
+    gate_up = []
+    if not args.no_gate_up:
+        for M in (1, 16):
+            r = run_gate_up(M, 200, 20, args.mode)
+            gate_up.append(r)
+            log(f"bench: gate_up + SiLU-mul M={M}: fused {r['fused_us']} us ({r['fused_gbs']} GB/s), "
+                f"unfused {r['unfused_us']} us")
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(p)
@@ -627,6 +701,7 @@ def bench(args):
         "crossover": sweep,
         "fp8_w8a8": fp8,
         "moe_grouped_gemv": moe,
+        "gate_up_silu": gate_up,
         "hbm_context": context,
         "cpu_baseline": cpu,
     }

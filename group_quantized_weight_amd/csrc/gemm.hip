@@ -27,11 +27,14 @@
 //     acc += s(g, n) * P in float32 (the promotion), overlapped with the next
 //     group's MFMAs. The scale never rounds into an fp16 weight.
 //
-// Tiling: workgroup tile 128 x 128, 4 waves (one per SIMD), each wave all 128
-// rows and 32 columns as 4 tiles of v_mfma_f32_32x32x16_f16, so each
-// dequantized weight fragment feeds 4 MFMAs. The weights are the MFMA's first
-// operand: a lane holds output row 32 fm + (l % 32) and, by the choice of the
-// weight row-to-column map, the 16 adjacent columns 32 w + 16 (l / 32) .. +15.
+// Tiling: workgroup tile 128 x 128, 8 waves (two per SIMD). Waves w and w + 4
+// share all 128 rows and the 32 columns 32 (w % 4) .. +31, as 4 tiles of
+// v_mfma_f32_32x32x16_f16 (each dequantized weight fragment feeds 4 MFMAs);
+// wave w takes k-steps 0..3 of every chunk and wave w + 4 k-steps 4..7, and
+// the second adds its accumulators into the first's through LDS at the end.
+// The weights are the MFMA's first operand: a lane holds output row
+// 32 fm + (l % 32) and, by the choice of the weight row-to-column map, the 16
+// adjacent columns 32 (w % 4) + 16 (l / 32) .. +15.
 // K is processed in chunks of 128 (one group). A chunk's activations (fp16,
 // 32 KiB), packed weights (8 KiB), float32 scales and zero-points are copied
 // by buffer loads straight into LDS (buffer_load ... lds), 2 chunks ahead,

@@ -6,8 +6,9 @@
 // A call enqueues one kernel, or two when K is split: the split kernel writes
 // float32 partials to the workspace and a reduction kernel adds them in the
 // fixed order z = 0..nsplit-1 (the kernel boundary orders the two; no
-// device-wide fences or atomics are used). The MFMA path adds a pre-pass
-// that writes per-group activation sums to the workspace. Precisions 7 and 8
+// device-wide fences or atomics are used). The tiled MFMA path adds a
+// pre-pass that writes the activations as fp16 (scaled by a power of two per
+// row), the row exponents and float32 scales to the workspace. Precisions 7 and 8
 // quantize float32 activations to int8 codes and per-group scales inside the
 // int8 GEMV's prologue (into LDS, no extra launch) for M <= 4, and with a
 // pre-pass into the workspace above that.

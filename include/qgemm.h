@@ -120,9 +120,10 @@ int qgemm_pack(const void *w_canonical, void *w_packed, int K, int N, int prec, 
  * Device workspace bytes qgemm_run needs for this problem (0: none, and the
  * workspace pointer may be NULL). The workspace holds the int8 codes and
  * float32 scales of in-call activation quantization (precisions 7 and 8,
- * M > 4), on the MFMA path the float32 activation sums per (group, row) of
- * a pre-pass, and the float32 partial sums of a K-split; its contents before a call do not matter. Calls
- * that share a workspace must not run concurrently.
+ * M > 4), on the tiled MFMA path the pre-pass's fp16 activations, row
+ * exponents and float32 scales, and the float32 partial sums of a K-split;
+ * its contents before a call do not matter. Calls that share a workspace
+ * must not run concurrently.
  */
 size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec);
 
@@ -140,8 +141,10 @@ int qgemm_plan(int M, int N, int K, int group, int prec, int force_path, int for
 /*
  * out = the group-quantized product described at the top of this file.
  * Enqueues one kernel, or two when K is split (nsplit > 1: the partial sums
- * of the K-slices, then their fixed-order reduction); the MFMA path first
- * enqueues a pre-pass that sums each group of activations.
+ * of the K-slices, then their fixed-order reduction); the tiled MFMA path
+ * first enqueues a pre-pass that writes the activations as fp16 scaled by a
+ * power of two per row, the row exponents, and the scales as float32, into
+ * the workspace.
  *   M >= 0 (M == 0 is a no-op), N >= 1, K >= 1, K % group == 0, group in {32, 128}.
  *   A:         activations [M][K] (bf16 / float32 / int8 by prec)
  *   a_scales:  float32 [M][K/G] for *_A_I8, else NULL (unused)

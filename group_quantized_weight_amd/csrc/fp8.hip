@@ -160,31 +160,36 @@ hipError_t launch_fp8_quant(const uint16_t *A, uint8_t *Aq, float *a_scale, int 
 //                       block (section 四.3); a_scale [M][K/128],
 //                       w_scale [N/128][K/128].
 //
-// Workgroup tile 128 x 128, 4 waves (2 x 2), each 64 x 64 = 4 x 4 tiles of
-// v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3, float32 accumulate): one
-// instruction per tile per 128-wide K step, which is one scale block. The
-// K step's operand tiles (128 rows x 128 bytes each) are copied by buffer
+// Workgroup tile 128 x 128, 4 waves (2 x 2), each 64 x 64 = 2 x 2 tiles of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, float32 accumulate), two
+// instructions per tile per 128-wide K step (one scale block). Against the
+// 16x16x128 form (4 x 4 tiles, one instruction each) this issues half the
+// matrix instructions for the same work, with the same LDS fragment reads.
+// The K step's operand tiles (128 rows x 128 bytes each) are copied by buffer
 // loads straight into LDS, into a ring of STAGES stages: 3 (two steps in
 // flight) when the grid is about one workgroup per compute unit, 2 (67 KiB,
 // so two workgroups share a compute unit and hide each other's waits) when
 // there are at least two tiles per compute unit (measured on MI355X: M = 4096,
 // K = N = 4096 per token 116 -> 85 us; M = 1024 prefers 3 stages, 32 vs
-// 38 us). The 16-byte pieces of a
-// row are XOR-swizzled with the row index (mod 8), so the fragment reads of
-// 8 consecutive rows hit 8 different bank groups. A lane's fragment is 32
-// consecutive bytes of k (k = 32 (lane / 16) .. +31) of row lane % 16, the
-// same k for both operands, so the instruction's sum runs over all 128 k.
-// The weight fragment is the instruction's first operand and the activation
-// fragment its second, so each tile is computed transposed: a lane holds 4
-// adjacent output columns of one row, which the epilogue scales (one
-// activation scale per row) and writes with one 8-byte store (the other
-// order, 4 rows of one column per lane, took 3 us more at M = 1024, K = N =
-// 4096: 64 scale loads and 64 two-byte stores per lane).
+// 38 us). The 16-byte pieces of a row are XOR-swizzled with the row index
+// (mod 8), so the fragment reads of 8 consecutive rows hit 8 different bank
+// groups. A lane's fragment for half-step h (k = 64 h .. 64 h + 63) is the
+// 32 consecutive bytes k = 64 h + 32 (lane / 32) .. +31 of one row, the same
+// k for both operands. The weight fragment is the instruction's first
+// operand and the activation fragment its second, so each tile is computed
+// transposed: a lane holds one output row (activation row lane % 32) and 16
+// output columns. Instruction row i of a weight tile is weight row
+// 16 ((i / 4) % 2) + 4 (i / 8) + i % 4, which makes a lane's 16 columns the
+// adjacent 16 (lane / 32) .. +15 of the tile: the epilogue scales them (one
+// activation scale per row, 16 consecutive weight scales) and writes them
+// with two 16-byte stores.
 // ---------------------------------------------------------------------------
 constexpr int kF8Tile = 128;
 constexpr int kF8Row = 128;                       // bytes per operand row per K step
 constexpr int kF8OpBytes = kF8Tile * kF8Row;      // 16 KiB
 constexpr int kF8Stage = 2 * kF8OpBytes + 512;    // A, B, and the block's 128 activation scales
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 
 template <bool BLOCKWISE, int STAGES>
 __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict__ Aq, const float *__restrict__ a_scale,
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
   __shared__ __align__(16) unsigned char s_ring[STAGES * kF8Stage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = lane & 15, lk = lane >> 4;
+  const int l32 = lane & 31, hl = lane >> 5;
   const int wr = wave >> 1, wc = wave & 1;
   const int m0 = blockIdx.y * kF8Tile, n0 = blockIdx.x * kF8Tile;
   const int nsteps = K / 128;
@@ -246,55 +251,63 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
   // after them, which vmcnt(8) then also waits for); with 2 stages none.
   constexpr int kInFlight = STAGES == 3 ? 8 : 0;
 
-  auto frag = [&](const unsigned char *op, int row) {   // 32 bytes: pieces 2 lk, 2 lk + 1 of the row
-    const u32x4_v lo = *(const u32x4_v *)(op + row * kF8Row + 16 * ((2 * lk) ^ (row & 7)));
-    const u32x4_v hi = *(const u32x4_v *)(op + row * kF8Row + 16 * ((2 * lk + 1) ^ (row & 7)));
+  // 32 bytes of one row: pieces 4 h + 2 (lane / 32) and the next
+  auto frag = [&](const unsigned char *op, int row, int h) {
+    const int p = 4 * h + 2 * hl;
+    const u32x4_v lo = *(const u32x4_v *)(op + row * kF8Row + 16 * (p ^ (row & 7)));
+    const u32x4_v hi = *(const u32x4_v *)(op + row * kF8Row + 16 * ((p + 1) ^ (row & 7)));
     return (i32x8_v){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
+  // this lane's rows: activation row 64 wr + 32 fm + l32 of tile fm; weight
+  // row 64 wc + 32 fn + wperm of tile fn
+  const int wperm = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
 
-  f32x4_v acc[4][4];
+  f32x16_v acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  struct Frags {
+    i32x8_v a[2][2], b[2][2];   // [tile][half-step]
+  };
+  auto read_step = [&](int step, Frags &F) {
+    const unsigned char *sb = s_ring + (step % STAGES) * kF8Stage;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        F.a[f][h] = frag(sb, 64 * wr + 32 * f + l32, h);
+        F.b[f][h] = frag(sb + kF8OpBytes, 64 * wc + 32 * f + wperm, h);
+      }
+  };
 
   if constexpr (!BLOCKWISE) {
     // Per token: the fragments of step i + 1 are read from LDS while the
-    // MFMAs of step i run, alternating one MFMA and one LDS read (two
+    // MFMAs of step i run, alternating one MFMA and two LDS reads (two
     // register sets, so no copies between them). This needs step i + 1 in
     // LDS at the top of step i, so the ring takes step i + STAGES into the
-    // stage step i used (read into registers during step i - 1). Measured
-    // 2-17% faster than reading each step's fragments at its own top
-    // (M = 16..4096, K = N = 4096); the blockwise loop, whose MFMA results
-    // also feed float32 promotions, measured 4-7% slower this way and keeps
-    // the simpler order below.
-    struct Frags {
-      i32x8_v a[4], b[4];
-    };
-    auto read_step = [&](int step, Frags &F) {
-      const unsigned char *sb = s_ring + (step % STAGES) * kF8Stage;
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        F.a[f] = frag(sb, 64 * wr + 16 * f + li);
-        F.b[f] = frag(sb + kF8OpBytes, 64 * wc + 16 * f + li);
-      }
-    };
+    // stage step i used (read into registers during step i - 1).
     auto step = [&](int i, const Frags &C, Frags &Nx) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(8 * (STAGES - 2)) : "memory");
       const int nx = i + STAGES;
       copy_step(s0 + nx, i % STAGES, nx < cnt ? 0 : kDead);
       read_step(i + 1, Nx);
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(C.b[fn], C.a[fm], acc[fm][fn], 0, 0, 0, 127,
-                                                                         0, 127);
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 2; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(C.b[fn][h], C.a[fm][h], acc[fm][fn], 0, 0,
+                                                                          0, 127, 0, 127);
       __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < 8; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     };
 #pragma unroll
@@ -316,68 +329,66 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t *__restrict
       const int nx = i + STAGES - 1;
       copy_step(s0 + nx, nx % STAGES, nx < cnt ? 0 : kDead);
       const unsigned char *sb = s_ring + (i % STAGES) * kF8Stage;
-      i32x8_v af[4], bfr[4];
-  #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        af[f] = frag(sb, 64 * wr + 16 * f + li);
-        bfr[f] = frag(sb + kF8OpBytes, 64 * wc + 16 * f + li);
-      }
-      if constexpr (BLOCKWISE) {
-        const float sb_w = w_scale[(size_t)(n0 / 128) * nsteps + s0 + i];   // one per workgroup tile and block
-        const float *sa = (const float *)(sb + 2 * kF8OpBytes);
-  #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) {
-          const float s1 = sa[64 * wr + 16 * fm + li] * sb_w;
-  #pragma unroll
-          for (int fn = 0; fn < 4; ++fn) {
-            const f32x4_v p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bfr[fn], af[fm], (f32x4_v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[fm][fn][r] = __builtin_fmaf(s1, p[r], acc[fm][fn][r]);
-          }
+      Frags F;
+      read_step(i, F);
+      const float sb_w = w_scale[(size_t)(n0 / 128) * nsteps + s0 + i];   // one per workgroup tile and block
+      const float *sa = (const float *)(sb + 2 * kF8OpBytes);
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm) {
+        const float s1 = sa[64 * wr + 32 * fm + l32] * sb_w;
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+          f32x16_v pz;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) pz[e] = 0.f;
+          f32x16_v p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[fn][0], F.a[fm][0], pz, 0, 0, 0, 127, 0,
+                                                                       127);
+          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[fn][1], F.a[fm][1], p, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[fm][fn][e] = __builtin_fmaf(s1, p[e], acc[fm][fn][e]);
         }
-      } else {
-  #pragma unroll
-        for (int fm = 0; fm < 4; ++fm)
-  #pragma unroll
-          for (int fn = 0; fn < 4; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0, 127,
-                                                                           0, 127);
       }
     }
   }
 
-  // ---- epilogue: tile (fm, fn) element r is row 16 fm + li, column 16 fn + 4 lk + r ----
+  // ---- epilogue: tile (fm, fn) element e is row 64 wr + 32 fm + l32, column
+  // 64 wc + 32 fn + 16 (lane / 32) + e ----
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm) {
-    const int m = m0 + 64 * wr + 16 * fm + li;
+  for (int fm = 0; fm < 2; ++fm) {
+    const int m = m0 + 64 * wr + 32 * fm + l32;
     if (m >= M) continue;
     const float as = BLOCKWISE ? 1.f : a_scale[m];
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) {
-      const int n = n0 + 64 * wc + 16 * fn + 4 * lk;
+    for (int fn = 0; fn < 2; ++fn) {
+      const int n = n0 + 64 * wc + 32 * fn + 16 * hl;
       if (n >= N) continue;
-      float v[4];
+      float v[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        v[r] = BLOCKWISE ? acc[fm][fn][r] : as * ((n + r < N ? w_scale[n + r] : 0.f) * acc[fm][fn][r]);
+      for (int e = 0; e < 16; ++e)
+        v[e] = BLOCKWISE ? acc[fm][fn][e] : as * ((n + e < N ? w_scale[n + e] : 0.f) * acc[fm][fn][e]);
       if (nsplit > 1) {
-        // the slice's scaled float32 partial; the reduce adds slices z = 0..nsplit-1
-        *(f32x4_v *)&partial[((size_t)blockIdx.z * M + m) * Np + n] = (f32x4_v){v[0], v[1], v[2], v[3]};
+        // the slice's scaled float32 partial (columns up to Np, a multiple of
+        // 128); the reduce adds slices z = 0..nsplit-1
+        float *pp = &partial[((size_t)blockIdx.z * M + m) * Np + n];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          *(f32x4_v *)(pp + 4 * e4) = (f32x4_v){v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]};
         continue;
       }
-      const f32x2_v lo = {v[0], v[1]}, hi = {v[2], v[3]};
-      const uint32_t b01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_v));
-      const uint32_t b23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_v));
-      uint16_t *o = out + (size_t)m * N + n;
-      if (n + 4 <= N && ((((size_t)m * N + n) & 3) == 0)) {   // 8-byte aligned: one store
-        *(u32x2_v *)o = (u32x2_v){b01, b23};
-      } else {   // the ragged end of a row, or N % 4 != 0
-        const uint16_t e[4] = {(uint16_t)(b01 & 0xFFFFu), (uint16_t)(b01 >> 16), (uint16_t)(b23 & 0xFFFFu),
-                               (uint16_t)(b23 >> 16)};
+      uint32_t b[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) o[r] = e[r];
+      for (int e2 = 0; e2 < 8; ++e2) {
+        const f32x2_v pr = {v[2 * e2], v[2 * e2 + 1]};
+        b[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_v));
+      }
+      uint16_t *o = out + (size_t)m * N + n;
+      if (n + 16 <= N && ((((size_t)m * N + n) & 7) == 0)) {   // 16-byte aligned: two stores
+        *(u32x4_v *)o = (u32x4_v){b[0], b[1], b[2], b[3]};
+        *(u32x4_v *)(o + 8) = (u32x4_v){b[4], b[5], b[6], b[7]};
+      } else {   // the ragged end of a row, or N % 8 != 0
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (n + e < N) o[e] = (uint16_t)(b[e / 2] >> (16 * (e & 1)));
       }
     }
   }

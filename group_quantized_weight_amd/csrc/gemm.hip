@@ -436,19 +436,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pre-pass. Blocks [0, ceil(M / 4)): one wave per row m: e(m) = 141 - E,
+// Pre-pass. Blocks [0, M): one workgroup (4 waves) per row m: e(m) = 141 - E,
 // with E the biased exponent of the row's largest |a| (so that the largest
 // scaled magnitude lies in [2^14, 2^15)), and A16[m][k] = fp16(a * 2^e(m))
 // (round to nearest even; exact unless the scaled value is below 2^-14).
 // Blocks past those: scales S32[g][n] = float(S[g][n]) for n < N, 0 for
-// N <= n < Np (8 per thread).
+// N <= n < Np (8 per thread). A workgroup per row (rather than a wave) puts
+// every compute unit to work from M = 256 on and keeps the row in registers.
 // ---------------------------------------------------------------------------
-template <int PPL>  // 16-byte pieces per lane held in registers (K <= 512 PPL); 0: two passes
+template <int PPT>  // 16-byte pieces per thread held in registers (K <= 2048 PPT); 0: two passes
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ A, uint16_t *__restrict__ A16,
                                                    int *__restrict__ rexp, const uint16_t *__restrict__ S,
                                                    float *__restrict__ S32, int M, int K, int N, int Np,
                                                    int ngroups, int row_blocks) {
-  const int lane = threadIdx.x & 63;
+  __shared__ uint32_t s_wmax[4];
   if ((int)blockIdx.x >= row_blocks) {
     const long long idx = ((long long)(blockIdx.x - row_blocks) * 256 + threadIdx.x) * 8;
     if (idx >= (long long)ngroups * Np) return;
@@ -463,8 +464,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ 
     *(f32x4_t *)(S32 + idx + 4) = hi;
     return;
   }
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pieces = K / 8;  // 16-byte pieces of the row
   const u32x4_t *src = (const u32x4_t *)(A + (size_t)m * K);
   u32x4_t *dst = (u32x4_t *)(A16 + (size_t)m * K);
@@ -479,23 +480,23 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ 
     }
     return r;
   };
-  u32x4_t v[PPL > 0 ? PPL : 1];
+  u32x4_t v[PPT > 0 ? PPT : 1];
   uint32_t mb = 0;
-  if constexpr (PPL > 0) {
+  if constexpr (PPT > 0) {
     // pieces past the row re-read the row's last piece (in bounds; the
     // maximum is unchanged and nothing is stored for them)
 #pragma unroll
-    for (int u = 0; u < PPL; ++u) {
-      const int p = lane + 64 * u;
+    for (int u = 0; u < PPT; ++u) {
+      const int p = threadIdx.x + 256 * u;
       v[u] = src[p < pieces ? p : pieces - 1];
     }
 #pragma unroll
-    for (int u = 0; u < PPL; ++u) {
+    for (int u = 0; u < PPT; ++u) {
       const uint32_t x = mag(v[u]);
       mb = mb > x ? mb : x;
     }
   } else {
-    for (int p = lane; p < pieces; p += 64) {
+    for (int p = threadIdx.x; p < pieces; p += 256) {
       const uint32_t x = mag(src[p]);
       mb = mb > x ? mb : x;
     }
@@ -505,8 +506,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ 
     const uint32_t y = (uint32_t)__shfl_xor((int)mb, o);
     mb = mb > y ? mb : y;
   }
+  if (lane == 0) s_wmax[wave] = mb;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) mb = mb > s_wmax[w] ? mb : s_wmax[w];
   const int e = 141 - (int)(mb >> 7);  // bf16 exponent field: bits 14..7 of the magnitude
-  if (lane == 0) rexp[m] = e;
+  if (threadIdx.x == 0) rexp[m] = e;
   auto convert = [&](const u32x4_t &x) {
     u32x4_t r;
 #pragma unroll
@@ -517,14 +522,14 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ 
     }
     return r;
   };
-  if constexpr (PPL > 0) {
+  if constexpr (PPT > 0) {
 #pragma unroll
-    for (int u = 0; u < PPL; ++u) {
-      const int p = lane + 64 * u;
+    for (int u = 0; u < PPT; ++u) {
+      const int p = threadIdx.x + 256 * u;
       if (p < pieces) dst[p] = convert(v[u]);
     }
   } else {
-    for (int p = lane; p < pieces; p += 64) dst[p] = convert(src[p]);
+    for (int p = threadIdx.x; p < pieces; p += 256) dst[p] = convert(src[p]);
   }
 }
 
@@ -538,20 +543,20 @@ static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
 // M * K * 2 <= INT_MAX and (K / 128) * Np * 4 <= INT_MAX.
 hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStream_t st) {
   if (a.K % kGemmKC != 0 || a.N % 8 != 0) return hipErrorInvalidValue;
-  const int row_blocks = (a.M + 3) / 4;
+  const int row_blocks = a.M;
   const long long sblocks = ((long long)a.nchunks * a.Np / 8 + 255) / 256;
   const dim3 pgrid((unsigned)(row_blocks + sblocks));
-  const int ppl = (a.K / 8 + 63) / 64;  // pieces per lane
+  const int ppl = (a.K / 8 + 255) / 256;  // pieces per thread
 #define QG_PREP(P) \
   prep_kernel<P><<<pgrid, 256, 0, st>>>(a.A, a.A16, a.rexp, a.S, a.S32, a.M, a.K, a.N, a.Np, a.nchunks, row_blocks)
-  if (ppl <= 2)
+  if (ppl <= 1)
+    QG_PREP(1);
+  else if (ppl <= 2)
     QG_PREP(2);
   else if (ppl <= 4)
     QG_PREP(4);
   else if (ppl <= 8)
     QG_PREP(8);
-  else if (ppl <= 16)
-    QG_PREP(16);
   else
     QG_PREP(0);
 #undef QG_PREP

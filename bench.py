@@ -438,6 +438,80 @@ def run_moe(name, steps, warmup, mode, block=None):
     return res
 
 
+def run_moe_gate_up(name, steps, warmup, mode, block=None):
+    """The grouped gate_up product with SwiGLU's gate step fused
+    (qgemm_moe_run_gate_up_silu: GEMM #1 and the SiLU-and-mul of the MoE
+    pipeline) on an MoE layer whose N is the gate_up width 2d, beside the
+    unfused sequence (qgemm_moe_run writing [T*topk][2d], then torch's silu
+    and mul). One step includes the align step in both."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    import group_quantized_weight_amd as qg
+    import workloads as wl
+    vp = ctypes.c_void_p
+    p = wl.make_moe_config(name)
+    prec = qg.W4_A_BF16
+    d = p.N // 2
+    if block is None:
+        block = qg.moe_default_block(p.T, p.topk, p.E, p.G, p.N)
+    per_expert = qg.packed_bytes(p.K, p.N, prec) + (p.K // p.G) * p.N * 2
+    copies = max(1, min(16, math.ceil(ROTATE_BYTES / (p.E * per_expert))))
+    A = torch.from_numpy(p.A.view("int16")).view(torch.bfloat16).cuda()
+    Wc = [torch.from_numpy(np.ascontiguousarray(p.W[e]).view(np.int32)).cuda() for e in range(p.E)]
+    Wg0 = torch.stack([qg.pack_gate_up(w, p.K, d, prec) for w in Wc]).contiguous()
+    Wp0 = torch.stack([qg.pack(w, p.K, p.N, prec) for w in Wc]).contiguous()
+    del Wc
+    S0 = torch.from_numpy(np.ascontiguousarray(p.S).view(np.int16)).view(torch.bfloat16).cuda()
+    Wgs = [Wg0] + [Wg0.clone() for _ in range(copies - 1)]
+    Wps = [Wp0] + [Wp0.clone() for _ in range(copies - 1)]
+    Ss = [S0] + [S0.clone() for _ in range(copies - 1)]
+    ids = torch.from_numpy(p.topk_ids.reshape(-1).astype(np.int32)).cuda()
+    numel = p.T * p.topk
+    srt, tiles, npp = qg.moe_align(ids, p.E, block)
+    out = torch.empty((numel, d), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty((numel, d), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((numel, p.N), dtype=torch.bfloat16, device="cuda")
+    need = int(qg.lib().qgemm_moe_workspace_bytes(p.T, p.topk, p.N, p.K, p.G, prec, p.E, block))
+    L = qg.lib()
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    ws = qg.workspace(need, A.device, stream)
+    wsp = vp(ws.data_ptr()) if ws is not None else None
+    routing = (vp(srt.data_ptr()), vp(tiles.data_ptr()), vp(npp.data_ptr()))
+
+    def align():
+        st = L.qgemm_moe_align(vp(ids.data_ptr()), numel, p.E, block, *routing, stream)
+        assert st == 0, st
+
+    def fused(i):
+        align()
+        st = L.qgemm_moe_run_gate_up_silu(p.T, p.topk, d, p.K, p.G, prec, 0, p.E, block, vp(A.data_ptr()),
+                                          vp(Wgs[i % copies].data_ptr()), vp(Ss[i % copies].data_ptr()), None,
+                                          *routing, vp(out.data_ptr()), wsp, need, stream)
+        assert st == 0, st
+
+    def unfused(i):
+        align()
+        st = L.qgemm_moe_run(p.T, p.topk, p.N, p.K, p.G, prec, 0, p.E, block, vp(A.data_ptr()),
+                             vp(Wps[i % copies].data_ptr()), vp(Ss[i % copies].data_ptr()), None, *routing,
+                             vp(y.data_ptr()), wsp, need, stream)
+        assert st == 0, st
+        torch.mul(F.silu(y[:, :d]), y[:, d:], out=out2)
+
+    f_ms = time_steps(fused, steps, warmup, mode)
+    u_ms = time_steps(unfused, steps, warmup, mode)
+    used = len(np.unique(p.topk_ids))
+    nbytes = used * per_expert + p.T * p.K * 2 + numel * d * 2
+    res = dict(workload=name, T=p.T, topk=p.topk, E=p.E, experts_used=used, d=d, K=p.K, group=p.G, block=block,
+               fused_us=round(f_ms * 1e3, 2), unfused_us=round(u_ms * 1e3, 2), fused_bytes=nbytes,
+               fused_gbs=round(nbytes / (f_ms * 1e-3) / 1e9, 1),
+               frac_hbm=round(nbytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_saved=2 * numel * p.N * 2,
+               copies=copies, unfused="qgemm_moe_run to [T*topk][2d] bf16, then torch silu and mul")
+    del A, Wg0, Wp0, S0, Wgs, Wps, Ss, ids, srt, tiles, npp, out, out2, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def stream_read_context(steps=20, warmup=5):
     """Context only, not the product: a plain streaming read over rotated
     buffers of the decode weight size (torch's float32 sum of bf16 data), as
@@ -595,6 +669,9 @@ def bench(args):
     if args.only and args.only.startswith("stream:"):
         log(json.dumps(stream_ceiling(int(args.only.split(":")[1]), args.steps, args.warmup, args.mode)))
         return
+    if args.only and args.only.startswith("moe_gate_up:"):
+        log(json.dumps(run_moe_gate_up(args.only.split(":")[1], args.steps, args.warmup, args.mode)))
+        return
     if args.only and args.only.startswith("gate_up:"):
         log(json.dumps(run_gate_up(int(args.only.split(":")[1]), args.steps, args.warmup, args.mode)))
         return
@@ -663,6 +740,12 @@ def bench(args):
             r = run_gate_up(M, 200, 20, args.mode)
             gate_up.append(r)
             log(f"bench: gate_up + SiLU-mul M={M}: fused {r['fused_us']} us ({r['fused_gbs']} GB/s), "
+                f"unfused {r['unfused_us']} us")
+        for name in ("moe_e8_top2_t1", "moe_e8_top2_t16"):
+            r = run_moe_gate_up(name, 100, 20, args.mode)
+            r["moe"] = True
+            gate_up.append(r)
+            log(f"bench: {name} gate_up + SiLU-mul: fused {r['fused_us']} us ({r['fused_gbs']} GB/s), "
                 f"unfused {r['unfused_us']} us")
 
     cpu = None

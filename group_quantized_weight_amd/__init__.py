@@ -89,6 +89,8 @@ def lib():
             L.qgemm_run_gate_up_silu.argtypes = [c_int] * 6 + [vp] * 6 + [c_size, vp]
             L.qgemm_run_gate_up_silu_ex.restype = c_int
             L.qgemm_run_gate_up_silu_ex.argtypes = [c_int] * 6 + [vp] * 6 + [c_size, vp, c_int, c_int]
+            L.qgemm_moe_run_gate_up_silu.restype = c_int
+            L.qgemm_moe_run_gate_up_silu.argtypes = [c_int] * 9 + [vp] * 9 + [c_size, vp]
             L.qgemm_moe_max_tiles.restype = c_int
             L.qgemm_moe_max_tiles.argtypes = [c_int] * 3
             L.qgemm_moe_default_block.restype = c_int
@@ -376,6 +378,28 @@ def moe_run(A, w_packed, scales, routing, *, topk: int, N: int, G: int, E: int, 
                              _ptr(ws), ws_bytes, stream if stream is not None else _stream(A.device))
     if st != OK:
         raise QGemmError(st, "qgemm_moe_run")
+    return out
+
+
+def moe_run_gate_up_silu(A, w_packed, scales, routing, *, topk: int, d: int, G: int, E: int, block: int,
+                         prec: int = W4_A_BF16, zeros=None, out=None, stream=None):
+    """Grouped gate_up product with SwiGLU's gate step: out [T*topk, d], row i
+    = silu(gate) * up of A[i // topk] times slot i's expert's gate_up weight
+    (each expert packed with pack_gate_up, stacked; see include/qgemm.h)."""
+    import torch
+    T, K = A.shape
+    sorted_ids, tile_experts, npp = routing
+    if out is None:
+        out = torch.empty((T * topk, d), dtype=out_dtype(prec), device=A.device)
+    need = int(lib().qgemm_moe_workspace_bytes(T, topk, 2 * d, K, G, prec, E, block))
+    ws = workspace(need, A.device, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().qgemm_moe_run_gate_up_silu(T, topk, d, K, G, prec, int(zeros is not None), E, block, _ptr(A),
+                                          _ptr(w_packed), _ptr(scales), _ptr(zeros), _ptr(sorted_ids),
+                                          _ptr(tile_experts), _ptr(npp), _ptr(out), _ptr(ws), ws_bytes,
+                                          stream if stream is not None else _stream(A.device))
+    if st != OK:
+        raise QGemmError(st, "qgemm_moe_run_gate_up_silu")
     return out
 
 

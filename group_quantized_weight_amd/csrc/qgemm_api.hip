@@ -656,10 +656,13 @@ size_t qgemm_moe_workspace_bytes(int T, int topk, int N, int K, int group, int p
   return p.ws;
 }
 
-int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp, int E, int block, const void *A,
-                  const void *w_packed, const void *scales, const void *zeros, const int *sorted_ids,
-                  const int *tile_experts, const int *num_post_pad, void *out, void *workspace,
-                  size_t workspace_bytes, void *stream) {
+// The grouped product of qgemm_moe_run; gu_d > 0: each expert's weight is a
+// gate-up packed product of N = 2 gu_d columns whose SwiGLU gate step is
+// applied in the epilogue (out is [T * topk][gu_d]).
+static int moe_run_common(int T, int topk, int N, int K, int group, int prec, int has_zp, int E, int block,
+                          const void *A, const void *w_packed, const void *scales, const void *zeros,
+                          const int *sorted_ids, const int *tile_experts, const int *num_post_pad, void *out,
+                          void *workspace, size_t workspace_bytes, void *stream, int gu_d) {
   Formats f;
   int st = check_moe(T, topk, N, K, group, prec, has_zp, E, block, f);
   if (st != QG_OK) return st;
@@ -701,6 +704,7 @@ int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp
     a.w_expert_words = qgemm_packed_bytes(K, N, prec) / 4;
     a.s_expert_elems = (size_t)(K / 128) * N;
     a.z_expert_words = (size_t)(K / 128) * (N / 8);
+    a.gu_d = gu_d;
     e = launch_gemm_small_grouped(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.nsplit, p.mblocks), s);
   } else {
     GemvArgs a = {};
@@ -720,10 +724,31 @@ int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp
     a.w_expert_words = qgemm_packed_bytes(K, N, prec) / 4;
     a.s_expert_bytes = (size_t)(K / group) * N * 2;
     a.z_expert_words = (size_t)(K / group) * (N / 8);
+    a.gu_d = gu_d;
     e = launch_gemv_grouped(f.o, has_zp != 0, p.mb, a, dim3(p.tiles_x, p.mblocks, p.nsplit), p.lds, s);
   }
-  if (e == hipSuccess && p.nsplit > 1) e = launch_reduce(f.o, partial, out, numel, N, Np, p.nsplit, s);
+  if (e == hipSuccess && p.nsplit > 1)
+    e = gu_d > 0 ? launch_reduce_gate_up(f.o, partial, out, numel, gu_d, Np, p.nsplit, s)
+                 : launch_reduce(f.o, partial, out, numel, N, Np, p.nsplit, s);
   return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp, int E, int block, const void *A,
+                  const void *w_packed, const void *scales, const void *zeros, const int *sorted_ids,
+                  const int *tile_experts, const int *num_post_pad, void *out, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  return moe_run_common(T, topk, N, K, group, prec, has_zp, E, block, A, w_packed, scales, zeros, sorted_ids,
+                        tile_experts, num_post_pad, out, workspace, workspace_bytes, stream, 0);
+}
+
+int qgemm_moe_run_gate_up_silu(int T, int topk, int d, int K, int group, int prec, int has_zp, int E, int block,
+                               const void *A, const void *w_packed, const void *scales, const void *zeros,
+                               const int *sorted_ids, const int *tile_experts, const int *num_post_pad, void *out,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (d <= 0 || d % 32 != 0) return QG_EINVAL;
+  if (d > INT_MAX / 2) return QG_EUNSUPPORTED;
+  return moe_run_common(T, topk, 2 * d, K, group, prec, has_zp, E, block, A, w_packed, scales, zeros, sorted_ids,
+                        tile_experts, num_post_pad, out, workspace, workspace_bytes, stream, d);
 }
 
 int qgemm_fp8_quantize(const void *A, int M, int K, int block, void *Aq, void *a_scales, void *stream) {

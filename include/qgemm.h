@@ -329,6 +329,24 @@ int qgemm_moe_run(int T, int topk, int N, int K, int group, int prec, int has_zp
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The grouped product with SwiGLU's gate step in its epilogue: GEMM #1 of
+ * the MoE pipeline and the SiLU-and-mul after it (page
+ * "quantization-and-fused-kernels", sections 五.2 and 六.1), fused. Each of
+ * the E experts' weights is a [K][2d] gate_up matrix (gate columns first)
+ * packed with qgemm_pack_gate_up, the experts' packed buffers
+ * qgemm_packed_bytes(K, 2d, prec) bytes apart; scales [E][K/G][2d] and
+ * zero-points [E][K/G][2d/8] in canonical column order. Row i of out
+ * [T * topk][d] is silu(y_i[:d]) * y_i[d:] with y_i the row qgemm_moe_run
+ * would give for N = 2d. d % 32 == 0; every other argument, the workspace
+ * (qgemm_moe_workspace_bytes with N = 2d) and the errors are those of
+ * qgemm_moe_run.
+ */
+int qgemm_moe_run_gate_up_silu(int T, int topk, int d, int K, int group, int prec, int has_zp, int E, int block,
+                               const void *A, const void *w_packed, const void *scales, const void *zeros,
+                               const int *sorted_ids, const int *tile_experts, const int *num_post_pad,
+                               void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * FP8 (E4M3) W8A8 -- the variant the page "quantization-and-fused-kernels"
  * (arganzheng.life) contrasts with W4A16 in section 四: weights and
  * activations both in FP8, products accumulated in float32 on the matrix

@@ -158,3 +158,55 @@ def test_moe_gemv_and_mfma_blocks_agree(block):
     p = wl.make_moe_problem(12, 2, 6, 1024, 1024, 128, True, seed=1950)
     o, ref, bound = _run_case(p, block, 6)
     check(o, ref, bound, f"moe block={block}")
+
+
+# ---------------------------------------------------------------------------
+# grouped gate_up product with SwiGLU's gate step (qgemm_moe_run_gate_up_silu)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("prec", [1, 6])
+@pytest.mark.parametrize("T,topk,E,block,G,zp,d,K,split", [
+    # few tiles: a K-split, the step applied by the reduce
+    (1, 2, 8, 1, 128, True, 256, 1024, True),      # grouped GEMV (1-row blocks)
+    (5, 2, 3, 4, 32, False, 512, 512, True),
+    (16, 2, 8, 16, 128, True, 384, 1024, True),    # grouped small-M MFMA (16-row blocks)
+    (40, 3, 4, 32, 128, False, 256, 512, True),
+    # the E = 8 layer at full size (d = 14336): no split, the step in the epilogue
+    (1, 2, 8, 1, 128, False, 14336, 4096, False),
+    (16, 2, 8, 16, 128, True, 14336, 4096, False),
+])
+def test_moe_gate_up_silu(prec, T, topk, E, block, G, zp, d, K, split):
+    """Against the oracle's grouped product on the 2d gate_up columns followed
+    by silu_mul, under the gate derived from the product's (as for the dense
+    fused step); and, with float32 output, equal to the float64 gate step of
+    qgemm_moe_run's own output on the canonically packed weights up to the
+    float32 evaluation."""
+    import torch
+    from tests.test_gpu_gate_up import S1
+    from tests.gpu_util import ATOL, REL, bf16_half_ulp
+    p = wl.make_moe_problem(T, topk, E, 2 * d, K, G, zp, seed=2100 + T + E + d + prec)
+    A, Wp, S, Z = _moe_dev(p, prec)
+    Wg = torch.stack([qg.pack_gate_up(torch.from_numpy(np.ascontiguousarray(p.W[e]).view(np.int32)).cuda(), K, d,
+                                      prec) for e in range(E)]).contiguous()
+    routing = _check_align(p.topk_ids, E, block)
+    ws = qg.lib().qgemm_moe_workspace_bytes(T, topk, 2 * d, K, G, prec, E, block)
+    assert (ws > 0) == split, ws
+    out = qg.moe_run_gate_up_silu(A, Wg, S, routing, topk=topk, d=d, G=G, E=E, block=block, prec=prec, zeros=Z)
+    torch.cuda.synchronize()
+    assert out.shape == (T * topk, d)
+    cols = np.arange(d) if d <= 1024 else sample_indices(d, 256, 9)
+    ref2, bound2 = oracle.moe(T, topk, 2 * d, K, G, "w4", "bf16", "bf16", zp, p.A, p.topk_ids, p.W, p.S, p.Z,
+                              cols=np.concatenate([cols, cols + d]))
+    n = len(cols)
+    g, u, bg, bu = ref2[:, :n], ref2[:, n:], bound2[:, :n], bound2[:, n:]
+    ref = oracle.silu_mul(ref2, n)
+    o = out.float().cpu().numpy().astype(np.float64)[:, cols]
+    lg, lu = REL * bg + ATOL, REL * bu + ATOL
+    lim = S1 * lg * (np.abs(u) + lu) + np.abs(oracle.silu(g)) * lu + 1e-6 * np.abs(ref) + 1e-30
+    if prec == 1:
+        lim = lim + bf16_half_ulp(np.maximum(np.abs(o), np.abs(ref)))
+    bad = np.abs(o - ref) > lim
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[0])
+    if prec == 6:
+        y = qg.moe_run(A, Wp, S, routing, topk=topk, N=2 * d, G=G, E=E, block=block, prec=prec, zeros=Z)
+        want = oracle.silu_mul(y.float().cpu().numpy().astype(np.float64), d)[:, cols]
+        assert np.all(np.abs(o - want) <= 1e-6 * np.abs(want) + 1e-30)

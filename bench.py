@@ -690,11 +690,16 @@ def bench(args):
 
     log(f"bench: {args.workload} steps={args.steps} warmup={args.warmup} mode={args.mode}")
     # the first measurement of a fresh process meets an idle device: settle longer
+    # The streaming-read ceiling first: it also brings the memory clocks up
+    # from idle before the headline is timed (measured first in a fresh
+    # process, the decode step read up to 1.8 us slower than the same kernel
+    # timed later in that process).
+    import workloads as wl
+    ceiling = stream_ceiling(algorithmic_bytes(wl.make_config(args.workload)), args.steps, args.warmup, args.mode)
+    log(f"bench: plain streaming read of the {args.workload} bytes ({ceiling['bytes']}): {ceiling['us']} us, "
+        f"{ceiling['gbs']} GB/s ({ceiling['blocks']} workgroups)")
     head, p = run_workload(args.workload, args.steps, args.warmup, args.mode, settle=HEAD_SETTLE_S)
     log(f"bench: {args.workload}: {head['ms'] * 1e3:.2f} us/step, {head['gbs']:.0f} GB/s")
-    ceiling = stream_ceiling(head["bytes"], args.steps, args.warmup, args.mode)
-    log(f"bench: plain streaming read of the same {ceiling['bytes']} bytes: {ceiling['us']} us, "
-        f"{ceiling['gbs']} GB/s ({ceiling['blocks']} workgroups)")
 
     # long enough runs (milliseconds) that the clocks have settled under MFMA load
     gemm, _ = run_workload("prefill_w4a16_m1024", max(200, args.steps), max(20, args.warmup), args.mode)

@@ -689,7 +689,6 @@ def bench(args):
         return
 
     log(f"bench: {args.workload} steps={args.steps} warmup={args.warmup} mode={args.mode}")
-    # the first measurement of a fresh process meets an idle device: settle longer
     # The streaming-read ceiling first: it also brings the memory clocks up
     # from idle before the headline is timed (measured first in a fresh
     # process, the decode step read up to 1.8 us slower than the same kernel

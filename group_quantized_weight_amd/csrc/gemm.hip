@@ -50,6 +50,8 @@
 // (developer.aliyun.com), section 3.3).
 #include "common.h"
 
+#include <type_traits>
+
 namespace qg {
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
@@ -377,62 +379,80 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
       }
   }
   // The two waves of a column group hold partial sums over complementary
-  // k-steps: the second writes its accumulators to LDS (the ring is free
-  // now), the first adds them (first + second, a fixed order).
-  __syncthreads();
-  float *s_red = (float *)s_lds + (size_t)cg * (FM * 16 * 64);
-  if (kh == 1) {
+  // k-steps. Each finishes two of the four row tiles: the first wave (kh 0)
+  // row tiles 0 and 1, the second 2 and 3; each hands the other's two to it
+  // through LDS (the ring is free now) and adds the two in the fixed order
+  // first + second. The row exponents are read before the exchange, so that
+  // their latency is spent on it.
+  int rex[2];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        *(f32x4_t *)(s_red + ((fm * 4 + e4) * 64 + lane) * 4) =
-            (f32x4_t){acc[fm][4 * e4], acc[fm][4 * e4 + 1], acc[fm][4 * e4 + 2], acc[fm][4 * e4 + 3]};
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + 32 * (2 * kh + i) + j;
+    rex[i] = a.rexp[row < a.M ? row : a.M - 1];
   }
   __syncthreads();
-  if (kh == 1) return;
+  float *s_mine = (float *)s_lds + (size_t)(2 * cg + kh) * (2 * 16 * 64);     // what this wave hands over
+  const float *s_other = (float *)s_lds + (size_t)(2 * cg + 1 - kh) * (2 * 16 * 64);
+  auto put = [&](int i, const f32x16_t &x) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+    for (int e4 = 0; e4 < 4; ++e4)
+      *(f32x4_t *)(s_mine + ((i * 4 + e4) * 64 + lane) * 4) = (f32x4_t){x[4 * e4], x[4 * e4 + 1], x[4 * e4 + 2], x[4 * e4 + 3]};
+  };
+  auto take = [&](int i, f32x16_t &x, bool first) {  // x = first ? x + other : other + x
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
-      const f32x4_t o = *(const f32x4_t *)(s_red + ((fm * 4 + e4) * 64 + lane) * 4);
+      const f32x4_t o = *(const f32x4_t *)(s_other + ((i * 4 + e4) * 64 + lane) * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[fm][4 * e4 + e] = acc[fm][4 * e4 + e] + o[e];
+      for (int e = 0; e < 4; ++e) x[4 * e4 + e] = first ? x[4 * e4 + e] + o[e] : o[e] + x[4 * e4 + e];
     }
-
-  // ---- epilogue: row m0 + 32 fm + j, columns n0 + 32 cg + 16 h .. +15 ----
+  };
   const int n16 = n0 + 32 * cg + 16 * h;
+  // row m0 + 32 fm + j, columns n16 .. n16 + 15 (register indices stay
+  // compile-time constants: a runtime index would put acc in memory)
+  auto finish = [&](auto kh_c) __attribute__((always_inline)) {
+    constexpr int KH = decltype(kh_c)::value;
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int row = m0 + 32 * fm + j;
-    if (row >= a.M) continue;
-    const int e = a.rexp[row];
-    float v[16];
+    for (int i = 0; i < 2; ++i) put(i, acc[2 * (1 - KH) + i]);
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = __builtin_amdgcn_ldexpf(acc[fm][q], -e);
-    if (a.nsplit > 1) {
-      // K-slice partials; a second kernel adds them in the order z = 0..nsplit-1
-      float *p = &a.partial[((size_t)blockIdx.z * a.M + row) * a.Np + n16];
+    for (int i = 0; i < 2; ++i) take(i, acc[2 * KH + i], KH == 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) *(f32x4_t *)(p + 4 * q) = (f32x4_t){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-      continue;
-    }
-    // N % 8 == 0: each half of the lane's 16 columns is all in or all out
+    for (int i = 0; i < 2; ++i) {
+      const int fm = 2 * KH + i;
+      const int row = m0 + 32 * fm + j;
+      if (row >= a.M) continue;
+      float v[16];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int n = n16 + 8 * half;
-      if (n >= a.N) continue;
-      const size_t o = (size_t)row * a.N + n;
-      const float *x = v + 8 * half;
-      if constexpr (OF == O_BF16) {
-        *(u32x4_t *)((uint16_t *)a.out + o) = (u32x4_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                                        pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-      } else {
-        *(f32x4_t *)((float *)a.out + o) = (f32x4_t){x[0], x[1], x[2], x[3]};
-        *(f32x4_t *)((float *)a.out + o + 4) = (f32x4_t){x[4], x[5], x[6], x[7]};
+      for (int q = 0; q < 16; ++q) v[q] = __builtin_amdgcn_ldexpf(acc[fm][q], -rex[i]);
+      if (a.nsplit > 1) {
+        // K-slice partials; a second kernel adds them in the order z = 0..nsplit-1
+        float *p = &a.partial[((size_t)blockIdx.z * a.M + row) * a.Np + n16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(f32x4_t *)(p + 4 * q) = (f32x4_t){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        continue;
+      }
+      // N % 8 == 0: each half of the lane's 16 columns is all in or all out
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int n = n16 + 8 * half;
+        if (n >= a.N) continue;
+        const size_t o = (size_t)row * a.N + n;
+        const float *x = v + 8 * half;
+        if constexpr (OF == O_BF16) {
+          *(u32x4_t *)((uint16_t *)a.out + o) = (u32x4_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                          pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        } else {
+          *(f32x4_t *)((float *)a.out + o) = (f32x4_t){x[0], x[1], x[2], x[3]};
+          *(f32x4_t *)((float *)a.out + o + 4) = (f32x4_t){x[4], x[5], x[6], x[7]};
+        }
       }
     }
-  }
+  };
+  if (kh == 0)
+    finish(std::integral_constant<int, 0>{});
+  else
+    finish(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------------------

@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -37,11 +38,33 @@ def flags():
             "-I", os.path.join(ROOT, "include"), "-Wall"]
 
 
+def _scratch_kernels(remarks: str):
+    """(kernel, bytes per lane) of every kernel whose resource-usage remark
+    reports scratch memory."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str, obj: str):
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    # the resource-usage remarks are read back: a kernel that uses scratch
+    # memory (a register array indexed at run time, or spills past the
+    # register file) fails the build, since it runs several times slower
+    cmd = [hipcc()] + flags() + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    bad = _scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels using scratch memory: " +
+                           ", ".join(f"{n} ({b} bytes/lane)" for n, b in bad))
     return obj
 
 

@@ -246,7 +246,6 @@ void gemv_kernel(GemvArgs a) {
   const uint32_t *Wb = a.W;
   const char *Sb = (const char *)a.S;
   const uint32_t *Zb = a.Z;
-  int slot[MB];
   if constexpr (GR) {
     if (m0 >= *a.num_post_pad) return;
     const int e = a.tile_experts[blockIdx.y];
@@ -254,22 +253,16 @@ void gemv_kernel(GemvArgs a) {
     Wb += (size_t)e * a.w_expert_words;
     Sb += (size_t)e * a.s_expert_bytes;
     if constexpr (ZP) Zb += (size_t)e * a.z_expert_words;
-#pragma unroll
-    for (int m = 0; m < MB; ++m) slot[m] = a.sorted_ids[m0 + m];
-  } else {
-#pragma unroll
-    for (int m = 0; m < MB; ++m) slot[m] = m0 + m;
   }
-  // output row of block row m (valid when < M) and its activation row
+  // output row of block row m (valid when < M) and its activation row (a
+  // grouped block reads its slot from memory at each use: the rows are
+  // used at runtime indices, and a register array behind a select was
+  // turned back into an indexed stack array)
   auto out_row = [&](int m) {
-    if constexpr (GR) {
-      int r = slot[0];
-#pragma unroll
-      for (int j = 1; j < MB; ++j) r = m == j ? slot[j] : r;
-      return r;
-    } else {
+    if constexpr (GR)
+      return a.sorted_ids[m0 + (m < MB ? m : MB - 1)];
+    else
       return m0 + m;
-    }
   };
   auto act_row = [&](int m) { return GR ? out_row(m) / a.topk : m0 + m; };
   const int act_row0 = GR ? 0 : m0;                   // a valid row for lanes without one
@@ -416,11 +409,13 @@ void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) rexp[m] = scale_exponent(s_max[m]);
   }
+  // a row's exponent at a runtime row index, from LDS (a select over rexp[]
+  // was turned back into an indexed load of a stack array)
   auto row_exp = [&](int m) {
-    int e = rexp[0];
-#pragma unroll
-    for (int j = 1; j < MB; ++j) e = m == j ? rexp[j] : e;
-    return e;
+    if constexpr (AF == A_BF16)
+      return scale_exponent(s_max[m < MB ? m : MB - 1]);
+    else
+      return 0;
   };
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {

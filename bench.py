@@ -368,8 +368,12 @@ def run_gate_up(M, steps, warmup, mode, d=14336, K=4096, G=128):
             raise RuntimeError(f"qgemm_run failed: {st}")
         torch.mul(F.silu(y[:, :d]), y[:, d:], out=out2)
 
-    f_ms = time_steps(fused, steps, warmup, mode)
-    u_ms = time_steps(unfused, steps, warmup, mode)
+    # alternated, the better of two runs each: the first timing after the
+    # set-up runs on a device that has not settled yet
+    f_ms, u_ms = math.inf, math.inf
+    for _ in range(2):
+        f_ms = min(f_ms, time_steps(fused, steps, warmup, mode))
+        u_ms = min(u_ms, time_steps(unfused, steps, warmup, mode))
     path, ns, _ = qg.gate_up_plan(M, d, K, G, prec)
     fused_bytes = K * 2 * d // 2 + (K // G) * 2 * d * 2 + M * K * 2 + M * d * 2
     saved = 2 * (M * 2 * d * 2)
@@ -498,8 +502,12 @@ def run_moe_gate_up(name, steps, warmup, mode, block=None):
         assert st == 0, st
         torch.mul(F.silu(y[:, :d]), y[:, d:], out=out2)
 
-    f_ms = time_steps(fused, steps, warmup, mode)
-    u_ms = time_steps(unfused, steps, warmup, mode)
+    # alternated, the better of two runs each: the first timing after the
+    # set-up runs on a device that has not settled yet
+    f_ms, u_ms = math.inf, math.inf
+    for _ in range(2):
+        f_ms = min(f_ms, time_steps(fused, steps, warmup, mode))
+        u_ms = min(u_ms, time_steps(unfused, steps, warmup, mode))
     used = len(np.unique(p.topk_ids))
     nbytes = used * per_expert + p.T * p.K * 2 + numel * d * 2
     res = dict(workload=name, T=p.T, topk=p.topk, E=p.E, experts_used=used, d=d, K=p.K, group=p.G, block=block,

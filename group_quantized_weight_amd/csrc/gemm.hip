@@ -30,8 +30,9 @@
 // Tiling: workgroup tile 128 x 128, 8 waves (two per SIMD). Waves w and w + 4
 // share all 128 rows and the 32 columns 32 (w % 4) .. +31, as 4 tiles of
 // v_mfma_f32_32x32x16_f16 (each dequantized weight fragment feeds 4 MFMAs);
-// wave w takes k-steps 0..3 of every chunk and wave w + 4 k-steps 4..7, and
-// the second adds its accumulators into the first's through LDS at the end.
+// wave w takes k-steps 0..3 of every chunk and wave w + 4 k-steps 4..7; at
+// the end each of the two hands the other two of its four row tiles through
+// LDS and finishes the other two (the sum always first + second).
 // The weights are the MFMA's first operand: a lane holds output row
 // 32 fm + (l % 32) and, by the choice of the weight row-to-column map, the 16
 // adjacent columns 32 (w % 4) + 16 (l / 32) .. +15.

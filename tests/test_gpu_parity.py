@@ -305,13 +305,13 @@ def test_workspace_contents_do_not_matter():
 
 
 @pytest.mark.parametrize("prec,zp", [(1, False), (1, True), (6, False)])
-def test_gemm_two_stage_ring(prec, zp):
-    """At least two 128 x 128 tiles per compute unit select the tiled GEMM's
-    2-stage LDS ring (two workgroups per compute unit): M = 4096, N = 4096 is
-    1024 tiles, K = 384 three chunks (the ring wraps). The first 128 rows
-    must equal, bit for bit, the same rows computed alone (32 tiles: the
-    3-stage ring, no K-split forced); sampled columns of every row meet the
-    gate against the oracle."""
+def test_gemm_many_tiles_per_unit(prec, zp):
+    """Many 128 x 128 tiles per compute unit: M = 4096, N = 4096 is 1024
+    tiles, run in four rounds of workgroups; K = 384 is three chunks, so the
+    3-stage LDS ring wraps exactly once. The first 128 rows must equal, bit
+    for bit, the same rows computed alone (32 tiles, one round, no K-split
+    forced); sampled columns of every row meet the gate against the
+    oracle."""
     import torch
     M, N, K = 4096, 4096, 384
     p = wl.make_problem(M, N, K, 128, prec, zp, seed=2500 + 10 * prec + zp)
@@ -321,10 +321,10 @@ def test_gemm_two_stage_ring(prec, zp):
     part = qg.run(d.A[:128].contiguous(), d.Wp, d.S, N=N, G=128, prec=prec, zeros=d.Z,
                   force_path=qg.PATH_GEMM, force_nsplit=1)
     torch.cuda.synchronize()
-    assert bitwise_equal(out[:128].contiguous(), part), "2-stage and 3-stage rings differ"
+    assert bitwise_equal(out[:128].contiguous(), part), "rows differ from the same rows computed alone"
     cols = sample_indices(N, 192, 6)
     ref, bound = oracle.for_problem(p, cols=cols)
-    check(to_f64(out)[:, cols], ref, bound, f"two-stage ring prec={prec} zp={zp}", bf16_out=p.ofmt == "bf16")
+    check(to_f64(out)[:, cols], ref, bound, f"many tiles per unit prec={prec} zp={zp}", bf16_out=p.ofmt == "bf16")
 
 
 # ---------------------------------------------------------------------------

@@ -17,7 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemm.so")
 SOURCES = ["qgemm_api.hip", "pack.hip", "gemv.hip", "gemv_i8.hip", "gemm.hip", "gemm_small.hip",
            "reduce.hip", "quant.hip", "fp8.hip", "moe.hip", "dequant.hip",
-           "gemm_small_i8.hip", "stream.hip"]
+           "gemm_small_i8.hip", "stream.hip", "fp8_big.hip"]
+# kernels whose matrix results stay in the accumulation registers (256 float32
+# accumulators per lane do not fit the ordinary VGPRs)
+AGPR_FORM = {"fp8_big.hip"}
 ARCH = "gfx950"
 
 
@@ -28,14 +31,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libqgemm.so")
 
 
-def flags():
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-            # packed fp32 instructions are kept out of every kernel
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA operands and results in ordinary VGPRs: the per-group fp32
-            # promotion then reads them without accumulator-register moves
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", os.path.join(ROOT, "include"), "-Wall"]
+def flags(src: str = ""):
+    f = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         # packed fp32 instructions are kept out of every kernel
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include"), "-Wall"]
+    if src not in AGPR_FORM:
+        # MFMA operands and results in ordinary VGPRs: the per-group fp32
+        # promotion then reads them without accumulator-register moves
+        f += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return f
 
 
 def _scratch_kernels(remarks: str):
@@ -57,7 +62,7 @@ def _compile(src: str, obj: str):
     # the resource-usage remarks are read back: a kernel that uses scratch
     # memory (a register array indexed at run time, or spills past the
     # register file) fails the build, since it runs several times slower
-    cmd = [hipcc()] + flags() + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags(src) + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -137,6 +137,11 @@ hipError_t launch_dequant_w4(const uint32_t *W, const uint16_t *S, const uint32_
                              int G, hipStream_t st);
 // small-M integer MFMA path for int8 activations (gemm_small_i8.hip)
 hipError_t launch_gemm_small_i8(int wfmt, bool zp, int mb, const SmallI8Args &a, dim3 grid, hipStream_t st);
+// per-token FP8 GEMM in 256 x 256 tiles (fp8_big.hip), for products with at
+// least `cus` such tiles and 256 K below 2^31
+bool fp8_big_tiles(int M, int N, int K, int cus);
+hipError_t launch_fp8_gemm_big(const uint8_t *Aq, const float *a_scale, const uint8_t *Wq, const float *w_scale,
+                               uint16_t *out, int M, int N, int K, hipStream_t stream);
 hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale, const uint8_t *Wq,
                            const float *w_scale, uint16_t *out, float *partial, int M, int N, int K, int nsplit,
                            int Np, int cus, hipStream_t stream);

@@ -411,6 +411,8 @@ hipError_t launch_fp8_gemm(int scaling, const uint8_t *Aq, const float *a_scale,
                            const float *w_scale, uint16_t *out, float *partial, int M, int N, int K, int nsplit,
                            int Np, int cus, hipStream_t st) {
   if (M == 0) return hipSuccess;
+  if (scaling == 0 && nsplit == 1 && fp8_big_tiles(M, N, K, cus))
+    return launch_fp8_gemm_big(Aq, a_scale, Wq, w_scale, out, M, N, K, st);
   const dim3 grid((N + kF8Tile - 1) / kF8Tile, (M + kF8Tile - 1) / kF8Tile, nsplit);
   const int stages = (long long)grid.x * grid.y * nsplit >= 2LL * cus ? 2 : 3;
   if (scaling == 1)

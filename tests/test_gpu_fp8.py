@@ -171,6 +171,35 @@ def test_gemm_two_stage_ring(scaling):
           bf16_out=True)
 
 
+@pytest.mark.parametrize("M,N,K", [(4000, 4100, 256), (4096, 4096, 128), (4352, 4000, 384)])
+def test_gemm_big_tiles_per_token(M, N, K):
+    """Per-token products with at least one 256 x 256 tile per compute unit
+    take the 256 x 256 kernel (ragged M and N, odd rows of N = 4100 not
+    16-byte aligned, K = 128 with copies past the last step): sampled
+    columns of every row against the oracle, and two 128-row slices bitwise
+    equal to the same rows computed by the 128 x 128 kernel (the same
+    instruction sequence over K)."""
+    import torch
+    p = wl.make_fp8_problem(M, N, K, 0, seed=1700 + M + N + K, outlier_frac=0.01)
+    Aq, sc = _quant_same(p.A, 0, f"big-tile inputs M={M} K={K}")
+    Wq, ws = _u8_dev(p.Wq), _f32_dev(p.w_scale)
+    flat = torch.full((M * N + 64,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = flat[:M * N].view(M, N)
+    qg.fp8_gemm(Aq, sc, Wq, ws, 0, out=out)
+    out2 = qg.fp8_gemm(Aq, sc, Wq, ws, 0)
+    parts = [(r0, qg.fp8_gemm(Aq[r0:r0 + 128].contiguous(), sc[r0:r0 + 128].contiguous(), Wq, ws, 0, split=False))
+             for r0 in (0, M - 128)]
+    torch.cuda.synchronize()
+    assert bool((flat[M * N:] == 7.0).all()), "write past the output"
+    assert bitwise_equal(out, out2), "rerun not bitwise equal"
+    for r0, part in parts:
+        assert bitwise_equal(out[r0:r0 + 128].contiguous(), part), f"rows {r0}.. differ from the 128 x 128 kernel"
+    cols = sample_indices(N, 96, 7)
+    ref, bound = oracle.fp8_gemm(M, N, K, 0, Aq.cpu().numpy(), sc.cpu().numpy(), p.Wq, p.w_scale, cols=cols)
+    check(out.float().cpu().numpy().astype(np.float64)[:, cols], ref, bound, f"big tiles M={M} N={N} K={K}",
+          bf16_out=True)
+
+
 @pytest.mark.parametrize("M,N", [(3, 300), (130, 1000), (64, 8)])
 def test_gemm_ragged_n_per_token(M, N):
     """Per-token scaling allows any N: the weight rows past N read zeros and

@@ -298,7 +298,7 @@ def run_fp8(name, steps, warmup, mode):
     ms_step = time_steps(step, steps, warmup, mode)
     flops = 2 * p.M * p.N * p.K
     res = dict(workload=name, M=p.M, N=p.N, K=p.K, scaling=["per_token", "blockwise"][p.scaling],
-               gemm_us=round(ms_gemm * 1e3, 2), step_us=round(ms_step * 1e3, 2),
+               gemm_us=round(ms_gemm * 1e3, 2), step_us=round(ms_step * 1e3, 2), timing=mode,
                gemm_tflops=round(flops / (ms_gemm * 1e-3) / 1e12, 1),
                frac_fp8_peak=round(flops / (ms_gemm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4), scaled_mm_us=None,
                nsplit=qg.fp8_nsplit(p.M, p.N, p.K, p.scaling))
@@ -605,7 +605,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    # eager: the steps launched one after another on one stream. Graph replays
+    # of the same steps (--mode graph) measured slower on these devices
+    # (ROCm 7: 0.6-2.7 us more per 12.5 us decode step, 4-6 us more per
+    # prefill step), so they are the option, not the default.
+    ap.add_argument("--mode", choices=["graph", "eager"], default="eager")
     ap.add_argument("--workload", default="decode_w4a16_g128")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")

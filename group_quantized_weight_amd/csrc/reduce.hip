@@ -18,31 +18,51 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 }
 
 template <int OF>
-__global__ __launch_bounds__(128) void reduce_kernel(const float *__restrict__ part, void *__restrict__ out,
+__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ part, void *__restrict__ out,
                                                      int M, int N, int Np, int nsplit) {
-  // thread: 4 adjacent columns of one row; the slices' partials are loaded 8
-  // at a time (all loads issued before the adds) and added in z order
-  const int n = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  // thread: 8 adjacent columns of one row (within the partials' padded row
+  // of Np % 8 == 0 columns); the slices' partials are loaded 4 slices at a
+  // time (all loads issued before the adds) and added in z order
+  const int n = 8 * (blockIdx.x * blockDim.x + threadIdx.x);
   if (n >= N) return;
+  const size_t zstride = (size_t)M * Np;
   for (int m = blockIdx.y; m < M; m += gridDim.y) {
     const float *p = part + (size_t)m * Np + n;
-    const size_t zstride = (size_t)M * Np;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int z0 = 0; z0 < nsplit; z0 += 8) {
-      float4 v[8];
+    float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+    for (int z0 = 0; z0 < nsplit; z0 += 4) {
+      float4 v[4][2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = z0 + u < nsplit ? *(const float4 *)(p + (size_t)(z0 + u) * zstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+        for (int h = 0; h < 2; ++h)
+          v[u][h] = z0 + u < nsplit ? *(const float4 *)(p + (size_t)(z0 + u) * zstride + 4 * h)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
         if (z0 + u < nsplit) {
-          s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+          s0.x += v[u][0].x; s0.y += v[u][0].y; s0.z += v[u][0].z; s0.w += v[u][0].w;
+          s1.x += v[u][1].x; s1.y += v[u][1].y; s1.z += v[u][1].z; s1.w += v[u][1].w;
         }
     }
-    const float r[4] = {s.x, s.y, s.z, s.w};
+    const float r[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     const size_t o = (size_t)m * N + n;
+    if constexpr (OF == O_BF16) {
+      if (n + 8 <= N && (o & 7) == 0) {   // 16-byte aligned: one store
+        uint32_t w[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c) w[c] = (uint32_t)to_bf16(r[2 * c]) | ((uint32_t)to_bf16(r[2 * c + 1]) << 16);
+        *(uint4 *)((uint16_t *)out + o) = make_uint4(w[0], w[1], w[2], w[3]);
+        continue;
+      }
+    } else {
+      if (n + 8 <= N && (o & 3) == 0) {
+        *(float4 *)((float *)out + o) = s0;
+        *(float4 *)((float *)out + o + 4) = s1;
+        continue;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
       if (n + c < N) {
         if constexpr (OF == O_BF16)
           ((uint16_t *)out)[o + c] = to_bf16(r[c]);
@@ -97,11 +117,11 @@ hipError_t launch_reduce_gate_up(int ofmt, const float *partial, void *out, int 
 
 hipError_t launch_reduce(int ofmt, const float *partial, void *out, int M, int N, int Np, int nsplit,
                          hipStream_t st) {
-  dim3 grid((N + 4 * 128 - 1) / (4 * 128), M < 65535 ? M : 65535);
+  dim3 grid((N + 8 * 256 - 1) / (8 * 256), M < 65535 ? M : 65535);
   if (ofmt == O_BF16)
-    reduce_kernel<O_BF16><<<grid, 128, 0, st>>>(partial, out, M, N, Np, nsplit);
+    reduce_kernel<O_BF16><<<grid, 256, 0, st>>>(partial, out, M, N, Np, nsplit);
   else
-    reduce_kernel<O_F32><<<grid, 128, 0, st>>>(partial, out, M, N, Np, nsplit);
+    reduce_kernel<O_F32><<<grid, 256, 0, st>>>(partial, out, M, N, Np, nsplit);
   return hipGetLastError();
 }
 

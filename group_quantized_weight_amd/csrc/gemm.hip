@@ -554,6 +554,77 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ 
   }
 }
 
+// from this many rows (256 workgroups of 4 rows) the pre-pass takes a wave per
+// row
+constexpr int kPrepWaveMinRows = 1024;
+
+// The same pre-pass with one wave per row (4 rows per workgroup), the row
+// held in registers (NCH 16-byte pieces per lane, K <= 512 NCH) and its
+// maximum found by lane exchanges alone; used when the rows alone give every
+// compute unit a workgroup. Blocks past ceil(M / 4) convert the scales.
+template <int NCH>
+__global__ __launch_bounds__(256) void prep_wave_kernel(const uint16_t *__restrict__ A, uint16_t *__restrict__ A16,
+                                                        int *__restrict__ rexp, const uint16_t *__restrict__ S,
+                                                        float *__restrict__ S32, int M, int K, int N, int Np,
+                                                        int ngroups, int row_blocks) {
+  if ((int)blockIdx.x >= row_blocks) {
+    const long long idx = ((long long)(blockIdx.x - row_blocks) * 256 + threadIdx.x) * 8;
+    if (idx >= (long long)ngroups * Np) return;
+    const int g = (int)(idx / Np), n = (int)(idx % Np);
+    u32x4_t v = {0, 0, 0, 0};
+    if (n < N) v = *(const u32x4_t *)(S + (size_t)g * N + n);
+    f32x4_t lo = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                  __uint_as_float(v[1] & 0xFFFF0000u)};
+    f32x4_t hi = {__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xFFFF0000u), __uint_as_float(v[3] << 16),
+                  __uint_as_float(v[3] & 0xFFFF0000u)};
+    *(f32x4_t *)(S32 + idx) = lo;
+    *(f32x4_t *)(S32 + idx + 4) = hi;
+    return;
+  }
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (m >= M) return;   // whole waves
+  const int pieces = K / 8;
+  const u32x4_t *src = (const u32x4_t *)(A + (size_t)m * K);
+  u32x4_t *dst = (u32x4_t *)(A16 + (size_t)m * K);
+  u32x4_t v[NCH];
+  // pieces past the row re-read its last piece (in bounds; not stored)
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int p = lane + 64 * u;
+    v[u] = src[p < pieces ? p : pieces - 1];
+  }
+  uint32_t mb = 0;
+#pragma unroll
+  for (int u = 0; u < NCH; ++u)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t lo = v[u][c] & 0x7FFFu, hi = (v[u][c] >> 16) & 0x7FFFu;
+      mb = mb > lo ? mb : lo;
+      mb = mb > hi ? mb : hi;
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = (uint32_t)__shfl_xor((int)mb, o);
+    mb = mb > y ? mb : y;
+  }
+  const int e = 141 - (int)(mb >> 7);  // as in prep_kernel
+  if (lane == 0) rexp[m] = e;
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int p = lane + 64 * u;
+    if (p >= pieces) continue;
+    u32x4_t r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f32x2_t f = {__builtin_amdgcn_ldexpf(__uint_as_float(v[u][c] << 16), e),
+                   __builtin_amdgcn_ldexpf(__uint_as_float(v[u][c] & 0xFFFF0000u), e)};
+      r[c] = u32(__builtin_convertvector(f, f16x2_t));
+    }
+    dst[p] = r;
+  }
+}
+
 template <int OF, bool ZP>
 static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
   gemm_kernel<OF, ZP><<<grid, kGemmThreads, 0, st>>>(a);
@@ -564,8 +635,22 @@ static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
 // M * K * 2 <= INT_MAX and (K / 128) * Np * 4 <= INT_MAX.
 hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStream_t st) {
   if (a.K % kGemmKC != 0 || a.N % 8 != 0) return hipErrorInvalidValue;
-  const int row_blocks = a.M;
   const long long sblocks = ((long long)a.nchunks * a.Np / 8 + 255) / 256;
+  const int nch = (a.K / 8 + 63) / 64;    // pieces per lane with a wave per row
+  if (a.M >= kPrepWaveMinRows && nch <= 16) {
+    const int row_blocks = (a.M + 3) / 4;
+    const dim3 pgrid((unsigned)(row_blocks + sblocks));
+#define QG_PREPW(P) \
+  prep_wave_kernel<P><<<pgrid, 256, 0, st>>>(a.A, a.A16, a.rexp, a.S, a.S32, a.M, a.K, a.N, a.Np, a.nchunks, row_blocks)
+    if (nch <= 4)
+      QG_PREPW(4);
+    else if (nch <= 8)
+      QG_PREPW(8);
+    else
+      QG_PREPW(16);
+#undef QG_PREPW
+  } else {
+  const int row_blocks = a.M;
   const dim3 pgrid((unsigned)(row_blocks + sblocks));
   const int ppl = (a.K / 8 + 255) / 256;  // pieces per thread
 #define QG_PREP(P) \
@@ -581,6 +666,7 @@ hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStrea
   else
     QG_PREP(0);
 #undef QG_PREP
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ofmt == O_BF16) return zp ? go<O_BF16, true>(a, grid, st) : go<O_BF16, false>(a, grid, st);

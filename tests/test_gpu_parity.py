@@ -327,6 +327,28 @@ def test_gemm_many_tiles_per_unit(prec, zp):
     check(to_f64(out)[:, cols], ref, bound, f"many tiles per unit prec={prec} zp={zp}", bf16_out=p.ofmt == "bf16")
 
 
+@pytest.mark.parametrize("K", [1152, 8192])
+def test_gemm_prep_wave_per_row(K):
+    """From 1024 rows the pre-pass takes one wave per row (a ragged last
+    workgroup at M = 1030; K = 1152 leaves lanes without a piece, K = 8192
+    holds 16 pieces per lane): the last 6 rows equal, bit for bit, the same
+    rows computed alone (a workgroup per row), and sampled columns of every
+    row meet the gate against the oracle."""
+    import torch
+    M, N = 1030, 256
+    p = wl.make_problem(M, N, K, 128, 1, False, seed=2600 + K, outlier_frac=0.01)
+    d = Dev(p)
+    assert qg.plan(M, N, K, 128, 1)[0] == qg.PATH_GEMM
+    out = d.run(force_path=qg.PATH_GEMM, force_nsplit=1)
+    part = qg.run(d.A[M - 6:].contiguous(), d.Wp, d.S, N=N, G=128, prec=1, force_path=qg.PATH_GEMM,
+                  force_nsplit=1)
+    torch.cuda.synchronize()
+    assert bitwise_equal(out[M - 6:].contiguous(), part), "rows differ from the same rows computed alone"
+    cols = sample_indices(N, 64, 7)
+    ref, bound = oracle.for_problem(p, cols=cols)
+    check(to_f64(out)[:, cols], ref, bound, f"prep wave per row K={K}", bf16_out=True)
+
+
 # ---------------------------------------------------------------------------
 # the named workloads at full size, in the launch configuration of bench.py
 # (automatic plan); sampled outputs against the oracle

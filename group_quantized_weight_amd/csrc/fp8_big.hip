@@ -142,11 +142,14 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_big_kernel(const uint8_t *__r
       for (int e = 0; e < 16; ++e) acc[fm][fn][e] = 0.f;
 
   // One half-step: 16 slots, each one matrix instruction on C (tile q / 4,
-  // q % 4), then what the tables place there: the next half-step's fragment
-  // reads from stage `sbn`, half `en`, early (they have landed by the next
-  // wait), and, when `copies`, copy kCopyAt[q] of chunk `cn` into stage
-  // `stc`. With one wave per SIMD the order is kept as written, so that no
-  // wait or queue stall sits between two matrix instructions.
+  // q % 4), then the next half-step's fragment reads from stage `sbn`, half
+  // `en`, in the slots kReadAt names (early: they have landed by the next
+  // wait), and, when `copies`, one copy of chunk `cn` into stage `stc` per
+  // slot: the weights' 8 first, then the activations' (the weights stream
+  // from HBM, the activations are mostly served by the caches; weights
+  // first measured about 2% faster at M = N = K = 4096). With one wave per
+  // SIMD the order is kept as written, so that no wait or queue stall sits
+  // between two matrix instructions.
   constexpr int kReadAt[16] = {0, 4, 1, 5, 2, 6, 3, 7, -1, -1, -1, -1, -1, -1, -1, -1};   // fragment (b: + 4)
   auto half = [&](const Frags &C, Frags &Nx, const unsigned char *sbn, auto en_c, bool copies, int cn, int stc,
                   int dead) __attribute__((always_inline)) {
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_big_kernel(const uint8_t *__r
       const int f = kReadAt[q];
       if (f >= 4) Nx.b[f - 4] = frag(sbn, b_off[en][0], b_off[en][1], f - 4);
       else if (f >= 0) Nx.a[f] = frag(sbn, a_off[en][0], a_off[en][1], f);
-      if (copies) copy_one(cn, stc, (q & 1) ? 8 + (q >> 1) : (q >> 1), dead);
+      if (copies) copy_one(cn, stc, q < 8 ? 8 + q : q - 8, dead);
       __builtin_amdgcn_sched_barrier(0);
     }
   };

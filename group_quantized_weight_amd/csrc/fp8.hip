@@ -38,11 +38,31 @@ __device__ __forceinline__ uint32_t to_fp8x2(float x0, float x1) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
 }
 
+// Division of bf16 values by one scale, as the E4M3 conversion needs it.
+// For a finite scale sc >= 2^-100 it takes r = RN(1 / sc) once and, per
+// value, q = RN(x r) and RN(q + RN(x - sc q) r) (Markstein's correction
+// step, the residual exact by fma): 3 instructions instead of the ~10 of a
+// correctly rounded division. That quotient can differ from RN(x / sc) in
+// the last place, but only for quotients far below E4M3's smallest
+// subnormal, so the codes are those of the correctly rounded quotient
+// (checked over every bf16 x and every scale amax / 448 >= 2^-100, amax a
+// bf16 magnitude: tests/test_fp8_division.py). Other scales divide.
+struct ScaleDiv {
+  float sc, r;
+  bool fast;
+  __device__ explicit ScaleDiv(float s) : sc(s), r(1.0f / s), fast(s >= 0x1p-100f && s < __builtin_inff()) {}
+  __device__ float operator()(float x) const {
+    if (!fast) return x / sc;
+    const float q = x * r;
+    return __builtin_fmaf(__builtin_fmaf(-sc, q, x), r, q);
+  }
+};
+
 // 8 bf16 values (one 16-byte load) divided by the scale -> 8 codes (8 bytes).
-__device__ __forceinline__ uint2 quant8(u32x4_v v, float sc) {
+__device__ __forceinline__ uint2 quant8(u32x4_v v, const ScaleDiv &d) {
   uint32_t w[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = to_fp8x2(bf16_lo(v[j]) / sc, bf16_hi(v[j]) / sc);
+  for (int j = 0; j < 4; ++j) w[j] = to_fp8x2(d(bf16_lo(v[j])), d(bf16_hi(v[j])));
   return make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
 }
 
@@ -72,7 +92,7 @@ __global__ __launch_bounds__(256) void fp8_quant_block_kernel(const uint16_t *__
 #pragma unroll
   for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
   const float sc = amax > 0.f ? amax / 448.f : 1.f;
-  *(uint2 *)(Aq + e) = quant8(v, sc);
+  *(uint2 *)(Aq + e) = quant8(v, ScaleDiv(sc));
   if ((threadIdx.x & 15) == 0) a_scale[e / 128] = sc;
 }
 
@@ -92,7 +112,8 @@ __global__ __launch_bounds__(256) void fp8_quant_row_kernel(const uint16_t *__re
   __syncthreads();
   amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
   const float sc = amax > 0.f ? amax / 448.f : 1.f;
-  for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) *(uint2 *)(qrow + k) = quant8(*(const u32x4_v *)(row + k), sc);
+  const ScaleDiv d(sc);
+  for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) *(uint2 *)(qrow + k) = quant8(*(const u32x4_v *)(row + k), d);
   if (threadIdx.x == 0) a_scale[blockIdx.x] = sc;
 }
 
@@ -120,10 +141,11 @@ __global__ __launch_bounds__(256) void fp8_quant_row_wave_kernel(const uint16_t 
   for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
   const float sc = amax > 0.f ? amax / 448.f : 1.f;
   uint8_t *dst = Aq + (size_t)row * K;
+  const ScaleDiv d(sc);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int k = 8 * (lane + 64 * c);
-    if (k < K) *(uint2 *)(dst + k) = quant8(v[c], sc);
+    if (k < K) *(uint2 *)(dst + k) = quant8(v[c], d);
   }
   if (lane == 0) a_scale[row] = sc;
 }

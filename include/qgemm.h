@@ -367,8 +367,10 @@ enum {
  * elements of a row (block == 128, a_scales float32 [M][K/128]), in float32:
  *     a_scale = max |a| / 448, or 1 when that max is 0
  *     code    = E4M3(clamp(a / a_scale, -448, 448)), rounded to nearest even
- * with the division correctly rounded. The page's optional upper bound on the
- * scale is not applied.
+ * with the division correctly rounded (the codes are those of the correctly
+ * rounded quotient; the kernel may reach them through a reciprocal and a
+ * correction step). The page's optional upper bound on the scale is not
+ * applied.
  *   A:  bf16 [M][K] (device, read); Aq: E4M3 codes [M][K] (device, written).
  * M >= 0 (0 is a no-op), K >= 1 with K % 8 == 0 (K % 128 == 0 for block 128);
  * all pointers 16-byte aligned. One kernel on `stream`; nothing allocated.

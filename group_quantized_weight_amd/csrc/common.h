@@ -113,7 +113,9 @@ hipError_t launch_gemv_i8(int wfmt, bool zp, bool dq, int mb, const GemvArgs &a,
                           hipStream_t stream);
 // pre-pass (fp16 activations, exponents, float32 scales), then the MFMA
 // kernel on grid (Np / 128, ceil(M / 128), nsplit)
-hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStream_t stream);
+// wide: 128 x 256 tiles (grid.x counts 128-column tiles; nsplit 1 and
+// Np % 256 == 0 required)
+hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, bool wide, hipStream_t stream);
 // mb = ceil(M / 16) row blocks; grid (Np / 64, nsplit)
 hipError_t launch_gemm_small(int ofmt, bool zp, int mb, const SmallArgs &a, dim3 grid, hipStream_t stream);
 // gu_d > 0 (int4 only): gate-up column order for a fused gate_up product of

@@ -457,6 +457,269 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 128 x 256 tiles, for products whose tiles of that size fill the device
+// (no K-split): the same operands, chunks, copies and promotion as
+// gemm_kernel, but wave w takes the 32 columns 32 w .. +31 and all 8 k-steps
+// of every chunk. Against a 128 x 128 tile this halves the activation bytes
+// copied per product and the float32 promotions per MFMA (one per group of 8
+// k-steps instead of 4), and the waves hand nothing to each other at the
+// end. A chunk's stage holds the activations (32 KiB) and 16 word-rows x 256
+// columns of weights (16 KiB); the small ring holds 256 scales and 32
+// zero-point words per stage, and the waves without a small copy write into
+// one shared dead slot.
+// ---------------------------------------------------------------------------
+constexpr int kWideBN = 256;
+constexpr int kWideWOff = 128 * kARow;                      // 32 KiB
+constexpr int kWideStage = kWideWOff + 16 * kWideBN * 4;    // 48 KiB
+constexpr int kWideSmall = 2048;                            // [256 scales][32 zero-point words]
+constexpr int kWideZOff = 1024;
+
+template <int OF, bool ZP>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_wide_kernel(GemmArgs a) {
+  __shared__ __align__(16) unsigned char s_lds[kST * kWideStage + kSR * kWideSmall + 1024];
+  unsigned char *const s_ring = s_lds;
+  unsigned char *const s_small = s_lds + kST * kWideStage;
+  unsigned char *const s_dead = s_small + kSR * kWideSmall;   // the dead copies' slot, never read
+  constexpr int FM = 4;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // 0..7: columns 32 wave .. +31
+  const int j = lane & 31, h = lane >> 5;
+  // tile order: compact blocks of tiles per die, as in gemm_kernel
+  int tx = blockIdx.x, ty = blockIdx.y;
+  {
+    const int TX = gridDim.x, TY = gridDim.y, T = TX * TY;
+    if (T % 8 == 0) {
+      const int L = blockIdx.x + TX * blockIdx.y;
+      const int Lx = (L & 7) * (T >> 3) + (L >> 3);
+      const int GM = TY < 4 ? TY : 4;
+      const int per = GM * TX;
+      const int g = Lx / per, first = g * GM;
+      const int gs = TY - first < GM ? TY - first : GM;
+      const int r = Lx - g * per;
+      ty = first + r % gs;
+      tx = r / gs;
+    }
+  }
+  const int m0 = ty * kGemmBM;
+  const int n0 = tx * kWideBN;
+  const int nch = a.nchunks;
+
+  const int R = a.K / 8;
+  // weight row j of the MFMA is column fj of the wave's 32 (as in gemm_kernel)
+  const int fj = 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
+  const int cw = 32 * wave + fj;                         // within the workgroup's 256 columns
+
+  const int a_rows = a.M - m0 < kGemmBM ? a.M - m0 : kGemmBM;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.A16 + (size_t)m0 * a.K), (short)0, a_rows * a.K * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.W + (size_t)(n0 / kTileCols) * R * kTileCols), (short)0, 4 * R * kTileCols * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.S32, (short)0, a.nchunks * a.Np * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.Z, (short)0, ZP ? a.nchunks * (a.N >> 3) * 4 : 0, kBufWord3);
+  const __amdgpu_buffer_rsrc_t none_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, kBufWord3);
+
+  // activation copies: as in gemm_kernel (copy c = wave + 8 tt, 1 KiB each)
+  const int ar0 = 4 * wave + (lane >> 4);
+  const int a_voff0 = ar0 * (a.K * 2) + (((lane & 15) ^ (ar0 & 15)) << 4);
+  const int a_vstep = 32 * a.K * 2;
+  // weight copy i (0, 1) of wave w: word-row 2 w + i of the chunk, all 256
+  // columns: lane -> 64-column tile lane / 16, columns 4 (lane % 16) .. +3
+  // of it (LDS row-major [word-row][256 columns])
+  const int w_voff0 = ((lane >> 4) * R + 2 * wave) * 256 + (lane & 15) * 16;
+
+  auto copy_a = [&](int chunk, int stage, int tt, const __amdgpu_buffer_rsrc_t &rs) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(s_ring + stage * kWideStage + kAOff + (wave + 8 * tt) * 1024),
+                                             16, a_voff0 + tt * a_vstep, chunk * 256, 0, 0);
+  };
+  auto copy_w = [&](int chunk, int stage, int i, const __amdgpu_buffer_rsrc_t &rs) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(s_ring + stage * kWideStage + kWideWOff + (2 * wave + i) * 1024),
+                                             16, w_voff0 + i * 256, chunk * 4096, 0, 0);
+  };
+  // scales (wave 0: 256 floats) and zero-points (wave 1, with zero-points:
+  // 32 words; lanes past them fill the slot's tail); the other waves issue
+  // a copy with an out-of-range offset into the shared dead slot
+  constexpr int kDead = (int)0x80000000u;
+  const __amdgpu_buffer_rsrc_t small_rsrc = wave == 0 ? s_rsrc : z_rsrc;
+  const int small_voff = wave == 0 ? n0 * 4 + lane * 16 : ((ZP && wave == 1) ? (n0 >> 3) * 4 + lane * 16 : kDead);
+  const int small_cstride = wave == 0 ? a.Np * 4 : (ZP && wave == 1 ? (a.N >> 3) * 4 : 0);
+  const bool small_real = wave == 0 || (ZP && wave == 1);
+  auto copy_small = [&](int chunk, int sstage, const __amdgpu_buffer_rsrc_t &rs) {
+    unsigned char *dst = small_real ? s_small + sstage * kWideSmall + (wave == 0 ? 0 : kWideZOff) : s_dead;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, chunk * small_cstride + small_voff, 0, 0, 0);
+  };
+
+  const uint32_t magic = f16_magic_pair();
+  f16x2_t c0 = h2(0xE408E408u), c1 = h2(0xD480D480u);  // -(1024 + 8), -(64 + 8)
+
+  f32x16_t acc[FM], P[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = P[i][e] = 0.f;
+
+  const int s_rd = (32 * wave + 16 * h) * 4;            // the lane's 16 scales in a small stage
+  const int w_rd = kWideWOff + (h * kWideBN + cw) * 4;  // + s * 2048: word-row 2 s + h
+  int a_rd[8];                                          // k-step s, row tile 0; + fm * 32 rows
+#pragma unroll
+  for (int s = 0; s < 8; ++s) a_rd[s] = kAOff + j * kARow + (((2 * s + h) ^ (j & 15)) << 4);
+
+  f32x4_t scA[4], scB[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) scA[u] = scB[u] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+  typedef __attribute__((address_space(3))) const f16x8_t lds_f16x8;
+  typedef __attribute__((address_space(3))) const f32x4_t lds_f32x4;
+
+  // One chunk = 32 MFMA slots: slots 0..15 row tiles 0 and 1 (k-step
+  // s = slot / 2, each weight word dequantized just before its first use and
+  // kept for the second half), slots 16..31 tiles 2 and 3. Each slot also
+  // promotes 2 elements: slots 0..15 tiles 2 and 3 of the previous chunk,
+  // slots 16..31 tiles 0 and 1 of this chunk. Activation fragments are read
+  // three slots ahead; the copies of chunk i + 2 (small first) are issued
+  // between the MFMAs.
+  auto run_chunk = [&](int i, f32x4_t(&scp)[4], f32x4_t(&scc)[4]) __attribute__((always_inline)) {
+    const int sbase = (i % kST) * kWideStage;
+    const unsigned char *sm = s_small + (i % kSR) * kWideSmall;
+    const bool live = i + 2 < nch;
+    const __amdgpu_buffer_rsrc_t ar = live ? a_rsrc : none_rsrc, wr = live ? w_rsrc : none_rsrc,
+                                 sr = live ? small_rsrc : none_rsrc;
+    const int cn = i + 2, stn = (i + 2) % kST;
+    if constexpr (ZP) {
+      const uint32_t zw = *(const uint32_t *)(sm + kWideZOff + (cw >> 3) * 4);
+      const uint32_t z = (zw >> (4 * (cw & 7))) & 0xFu;
+      const uint32_t zz = z | (z << 16);
+      c0 = h2(0xE400E400u | zz);
+      c1 = h2(0xD400D400u | (zz << 4));
+    }
+    uint32_t ab[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      ab[s] = (uint32_t)(uintptr_t)(s_ring + sbase) + a_rd[s];
+      asm volatile("" : "+v"(ab[s]));
+    }
+    uint32_t wb = (uint32_t)(uintptr_t)(s_ring + sbase) + w_rd;
+    uint32_t qm = (uint32_t)(uintptr_t)sm + s_rd;
+    asm volatile("" : "+v"(wb), "+v"(qm));
+    auto frag = [&](int q) {
+      const int half = q >> 4, s = (q & 15) >> 1, fm = 2 * half + (q & 1);
+      return *(lds_f16x8 *)(ab[s] + fm * 32 * kARow);
+    };
+    f16x8_t af[4];
+    af[0] = frag(0);
+    af[1] = frag(1);
+    af[2] = frag(2);
+    uint32_t wraw[2];
+    wraw[0] = *(lds_u32 *)(wb);
+    f16x8_t wq[8];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const int half = q >> 4, r = q & 15, s = r >> 1, fm = 2 * half + (q & 1);
+      if (q + 3 < 32) af[(q + 3) & 3] = frag(q + 3);
+      if (q == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) scc[u] = *(lds_f32x4 *)(qm + u * 16);
+      }
+      if (half == 0 && (q & 1) == 0) {
+        // the word of k-step s + 1 is read one k-step ahead
+        if (s + 1 < 8) wraw[(s + 1) & 1] = *(lds_u32 *)(wb + (s + 1) * 2048);
+        wq[s] = dequant_f16(wraw[s & 1], magic, c0, c1);
+      }
+      if (s == 0)
+        P[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wq[s], af[q & 3], (f32x16_t){}, 0, 0, 0);
+      else
+        P[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wq[s], af[q & 3], P[fm], 0, 0, 0);
+      {
+        const int tt = half == 0 ? 2 + (r >> 3) : (r >> 3);
+        const int e0 = 2 * (r & 7);
+        const f32x4_t sc = half == 0 ? scp[e0 >> 2] : scc[e0 >> 2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          acc[tt][e0 + e] = __builtin_fmaf(sc[(e0 & 3) + e], P[tt][e0 + e], acc[tt][e0 + e]);
+      }
+      if (q == 1) copy_small(cn, (i + 2) % kSR, sr);
+      if (q == 5 || q == 11 || q == 17 || q == 23) copy_a(cn, stn, (q - 5) / 6, ar);
+      if (q == 27 || q == 30) copy_w(cn, stn, q == 27 ? 0 : 1, wr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  {
+    const __amdgpu_buffer_rsrc_t r0a = nch > 0 ? a_rsrc : none_rsrc, r0w = nch > 0 ? w_rsrc : none_rsrc,
+                                 r0s = nch > 0 ? small_rsrc : none_rsrc;
+    const __amdgpu_buffer_rsrc_t r1a = nch > 1 ? a_rsrc : none_rsrc, r1w = nch > 1 ? w_rsrc : none_rsrc,
+                                 r1s = nch > 1 ? small_rsrc : none_rsrc;
+    copy_small(0, 0, r0s);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) copy_a(0, 0, tt, r0a);
+    copy_w(0, 0, 0, r0w);
+    copy_w(0, 0, 1, r0w);
+    copy_small(1, 1, r1s);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) copy_a(1, 1, tt, r1a);
+    copy_w(1, 1, 0, r1w);
+    copy_w(1, 1, 1, r1w);
+  }
+  // at the top of chunk i at most the 6 main copies of chunk i + 1 are in
+  // flight (its small copy, issued first, has landed)
+  int i = 0;
+  for (; i + 1 < nch; i += 2) {
+    wait_then_barrier<6>();
+    run_chunk(i, scB, scA);
+    wait_then_barrier<6>();
+    run_chunk(i + 1, scA, scB);
+  }
+  if (i < nch) {
+    wait_then_barrier<6>();
+    run_chunk(i, scB, scA);
+  }
+  {
+    const bool odd = (nch & 1) != 0;
+#pragma unroll
+    for (int fm = 2; fm < FM; ++fm)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4_t sc = odd ? scA[e4] : scB[e4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[fm][4 * e4 + e] = __builtin_fmaf(sc[e], P[fm][4 * e4 + e], acc[fm][4 * e4 + e]);
+      }
+  }
+  // the copies past the last chunk (zeros into stages no one reads) land
+  // before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // row m0 + 32 fm + j, columns n16 .. n16 + 15
+  const int n16 = n0 + 32 * wave + 16 * h;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int row = m0 + 32 * fm + j;
+    if (row >= a.M) continue;
+    const int rex = a.rexp[row];
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = __builtin_amdgcn_ldexpf(acc[fm][q], -rex);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int n = n16 + 8 * half;
+      if (n >= a.N) continue;
+      const size_t o = (size_t)row * a.N + n;
+      const float *x = v + 8 * half;
+      if constexpr (OF == O_BF16) {
+        *(u32x4_t *)((uint16_t *)a.out + o) = (u32x4_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                        pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+      } else {
+        *(f32x4_t *)((float *)a.out + o) = (f32x4_t){x[0], x[1], x[2], x[3]};
+        *(f32x4_t *)((float *)a.out + o + 4) = (f32x4_t){x[4], x[5], x[6], x[7]};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pre-pass. Blocks [0, M): one workgroup (4 waves) per row m: e(m) = 141 - E,
 // with E the biased exponent of the row's largest |a| (so that the largest
 // scaled magnitude lies in [2^14, 2^15)), and A16[m][k] = fp16(a * 2^e(m))
@@ -626,15 +889,19 @@ __global__ __launch_bounds__(256) void prep_wave_kernel(const uint16_t *__restri
 }
 
 template <int OF, bool ZP>
-static hipError_t go(const GemmArgs &a, dim3 grid, hipStream_t st) {
-  gemm_kernel<OF, ZP><<<grid, kGemmThreads, 0, st>>>(a);
+static hipError_t go(const GemmArgs &a, dim3 grid, bool wide, hipStream_t st) {
+  if (wide)
+    gemm_wide_kernel<OF, ZP><<<dim3(grid.x / 2, grid.y), kGemmThreads, 0, st>>>(a);
+  else
+    gemm_kernel<OF, ZP><<<grid, kGemmThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
 // The dispatcher sends only K % 128 == 0, N % 8 == 0 here, with
 // M * K * 2 <= INT_MAX and (K / 128) * Np * 4 <= INT_MAX.
-hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStream_t st) {
+hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, bool wide, hipStream_t st) {
   if (a.K % kGemmKC != 0 || a.N % 8 != 0) return hipErrorInvalidValue;
+  if (wide && (a.nsplit != 1 || a.Np % kWideBN != 0 || grid.x % 2 != 0)) return hipErrorInvalidValue;
   const long long sblocks = ((long long)a.nchunks * a.Np / 8 + 255) / 256;
   const int nch = (a.K / 8 + 63) / 64;    // pieces per lane with a wave per row
   if (a.M >= kPrepWaveMinRows && nch <= 16) {
@@ -669,8 +936,8 @@ hipError_t launch_gemm(int ofmt, bool zp, const GemmArgs &a, dim3 grid, hipStrea
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ofmt == O_BF16) return zp ? go<O_BF16, true>(a, grid, st) : go<O_BF16, false>(a, grid, st);
-  return zp ? go<O_F32, true>(a, grid, st) : go<O_F32, false>(a, grid, st);
+  if (ofmt == O_BF16) return zp ? go<O_BF16, true>(a, grid, wide, st) : go<O_BF16, false>(a, grid, wide, st);
+  return zp ? go<O_F32, true>(a, grid, wide, st) : go<O_F32, false>(a, grid, wide, st);
 }
 
 }  // namespace qg

@@ -396,7 +396,9 @@ static int run_common(int M, int N, int K, int group, int prec, int has_zp, cons
     a.M = M; a.N = N; a.K = K; a.Np = Np;
     a.nchunks = K / kGemmKC;
     a.nsplit = p.nsplit;
-    e = launch_gemm(f.o, has_zp != 0, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), s);
+    // 128 x 256 tiles when those alone fill the device
+    const bool wide = p.nsplit == 1 && Np % 256 == 0 && (long long)(Np / 256) * p.tiles_y >= device_cus();
+    e = launch_gemm(f.o, has_zp != 0, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), wide, s);
   }
   if (e == hipSuccess && p.nsplit > 1)
     e = gu_d > 0 ? launch_reduce_gate_up(f.o, partial, out, M, gu_d, Np, p.nsplit, s)

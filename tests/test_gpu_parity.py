@@ -304,27 +304,42 @@ def test_workspace_contents_do_not_matter():
     check(to_f64(o1), ref, bound, "split call", bf16_out=True)
 
 
-@pytest.mark.parametrize("prec,zp", [(1, False), (1, True), (6, False)])
-def test_gemm_many_tiles_per_unit(prec, zp):
-    """Many 128 x 128 tiles per compute unit: M = 4096, N = 4096 is 1024
-    tiles, run in four rounds of workgroups; K = 384 is three chunks, so the
-    3-stage LDS ring wraps exactly once. The first 128 rows must equal, bit
-    for bit, the same rows computed alone (32 tiles, one round, no K-split
-    forced); sampled columns of every row meet the gate against the
-    oracle."""
+def _wide_tiles(M, N):
+    """Whether the tiled GEMM takes 128 x 256 tiles: unsplit, and those tiles
+    alone fill the device (N padded to 256 columns)."""
     import torch
-    M, N, K = 4096, 4096, 384
-    p = wl.make_problem(M, N, K, 128, prec, zp, seed=2500 + 10 * prec + zp)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return -(-N // 256) * -(-M // 128) >= cus
+
+
+@pytest.mark.parametrize("prec,zp,M,N", [(1, False, 4096, 4096), (1, True, 4100, 2040), (6, False, 4096, 4096),
+                                         (6, True, 4100, 2040)])
+def test_gemm_wide_tiles(prec, zp, M, N):
+    """Products whose 128 x 256 tiles fill the device take them (here M = 4096
+    and 4100, a ragged last row tile; N = 2040 leaves the last tile's columns
+    partly past N). K = 384 is three chunks, so the 3-stage LDS ring wraps
+    exactly once. Every row is computed on its own: the rows reversed give
+    the reversed result bit for bit; nothing is written past the output; and
+    sampled columns of every row meet the gate against the oracle."""
+    import torch
+    K = 384
+    p = wl.make_problem(M, N, K, 128, prec, zp, seed=2500 + 10 * prec + zp + M)
     d = Dev(p)
     assert qg.plan(M, N, K, 128, prec)[:2] == (qg.PATH_GEMM, 1)
-    out = d.run()
-    part = qg.run(d.A[:128].contiguous(), d.Wp, d.S, N=N, G=128, prec=prec, zeros=d.Z,
-                  force_path=qg.PATH_GEMM, force_nsplit=1)
+    assert _wide_tiles(M, N), "the shape no longer selects 128 x 256 tiles on this device"
+    esz = 2 if p.ofmt == "bf16" else 4
+    dt = torch.int16 if esz == 2 else torch.int32
+    canary = torch.full((M * N + 256,), 12345, dtype=dt, device="cuda")
+    out_view = canary[:M * N].view(torch.bfloat16 if esz == 2 else torch.float32).view(M, N)
+    out = qg.run(d.A, d.Wp, d.S, N=N, G=128, prec=prec, zeros=d.Z, out=out_view)
+    rev = qg.run(d.A.flip(0).contiguous(), d.Wp, d.S, N=N, G=128, prec=prec, zeros=d.Z)
     torch.cuda.synchronize()
-    assert bitwise_equal(out[:128].contiguous(), part), "rows differ from the same rows computed alone"
+    assert bool((canary[M * N:] == 12345).all()), "write past the output"
+    assert bitwise_equal(rev.flip(0).contiguous(), out.contiguous()), "a row's result depends on its tile"
     cols = sample_indices(N, 192, 6)
     ref, bound = oracle.for_problem(p, cols=cols)
-    check(to_f64(out)[:, cols], ref, bound, f"many tiles per unit prec={prec} zp={zp}", bf16_out=p.ofmt == "bf16")
+    check(to_f64(out)[:, cols], ref, bound, f"wide tiles prec={prec} zp={zp} M={M} N={N}",
+          bf16_out=p.ofmt == "bf16")
 
 
 @pytest.mark.parametrize("K", [1152, 8192])

@@ -2,8 +2,8 @@
 // enough to give every compute unit a 256 x 256 tile: the same computation
 // as the 128 x 128 kernel (page "quantization-and-fused-kernels"
 // (arganzheng.life), section 四.2: float32 sum over K of a w, then the weight
-// scale, then the activation scale), with four times the products per byte
-// staged through LDS.
+// scale, then the activation scale), with twice the products per byte
+// copied into LDS.
 //
 //   - Workgroup tile 256 x 256, 4 waves (one per SIMD) of 128 x 128 = 4 x 4
 //     tiles of v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales), 256 float32
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_big_kernel(const uint8_t *__r
     half(fy, fx, s_ring + (st ^ 1) * kBStage, std::integral_constant<int, 0>{}, true, c + 2, st,
          c + 2 < nchunks ? 0 : kDead);
   }
-  // the copies past the last step (zeros into stages no one reads) land
+  // the copies past the last chunk (zeros into stages no one reads) land
   // before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 128 x 256 tiles, for products whose tiles of that size fill the device
+// 128 x 256 tiles, for unsplit products that finish sooner on them
 // (no K-split): the same operands, chunks, copies and promotion as
 // gemm_kernel, but wave w takes the 32 columns 32 w .. +31 and all 8 k-steps
 // of every chunk. Against a 128 x 128 tile this halves the activation bytes

@@ -302,6 +302,15 @@ size_t qgemm_workspace_bytes(int M, int N, int K, int group, int prec) {
   return ws;
 }
 
+// Whether t256 tiles of 128 x 256 finish sooner than t128 tiles of 128 x 128,
+// each kernel taking one tile per compute unit at a time: a round of the wide
+// tiles costs about 1.6 rounds of the narrow ones (256 tiles of each at K =
+// N = 4096: 71.6 against 44.8 us), so ties go to the narrow tiles.
+static bool wide_rounds_cheaper(long long t128, long long t256, int cus) {
+  const long long r128 = (t128 + cus - 1) / cus, r256 = (t256 + cus - 1) / cus;
+  return 8 * r256 < 5 * r128;
+}
+
 // The product of qgemm_run_ex; gu_d > 0: a gate-up packed product of N =
 // 2 gu_d columns whose SwiGLU gate step is applied in the epilogue (out is
 // [M][gu_d]; bf16 activations on the GEMV or small-M path only).
@@ -396,8 +405,9 @@ static int run_common(int M, int N, int K, int group, int prec, int has_zp, cons
     a.M = M; a.N = N; a.K = K; a.Np = Np;
     a.nchunks = K / kGemmKC;
     a.nsplit = p.nsplit;
-    // 128 x 256 tiles when those alone fill the device
-    const bool wide = p.nsplit == 1 && Np % 256 == 0 && (long long)(Np / 256) * p.tiles_y >= device_cus();
+    const bool wide = p.nsplit == 1 && Np % 256 == 0 &&
+                      wide_rounds_cheaper((long long)p.tiles_x * p.tiles_y, (long long)(Np / 256) * p.tiles_y,
+                                          device_cus());
     e = launch_gemm(f.o, has_zp != 0, a, dim3(p.tiles_x, p.tiles_y, p.nsplit), wide, s);
   }
   if (e == hipSuccess && p.nsplit > 1)

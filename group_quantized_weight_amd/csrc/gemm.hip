@@ -64,7 +64,6 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBufWord3 = 0x00020000;
-constexpr int kPolicyStream = 2;  // non-temporal
 
 // Main ring stage: [activations 128 rows x 256 B][weights 16 word-rows x 128 columns x 4 B].
 constexpr int kARow = 256;

@@ -625,8 +625,8 @@ def main():
                     help="time a plain device copy of this many MiB instead (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, sharding). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (a sharded layer runs it "
+              "once per GPU on that GPU's columns). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

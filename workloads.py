@@ -204,7 +204,8 @@ def make_problem(M, N, K, G, prec, has_zp=False, seed=0, *, scale_lo=1e-3, scale
 
 
 # ----------------------------------------------------------------------------
-# named workloads (the shapes of the pages' layers; see the design doc for sources)
+# named workloads: the shapes of the pages' layers (decode gate+up of an 8B-class
+# layer, Q8_0 / Q4_0 group GEMMs, the prefill sweep, zero-point and lm_head shapes)
 # ----------------------------------------------------------------------------
 def _cfg(name, M, N, K, G, prec, has_zp, seed, **kw):
     return dict(name=name, M=M, N=N, K=K, G=G, prec=prec, has_zp=has_zp, seed=seed, **kw)

@@ -368,6 +368,26 @@ def test_gemm_prep_wave_per_row(K):
     check(to_f64(out)[:, cols], ref, bound, f"prep wave per row K={K}", bf16_out=True)
 
 
+@pytest.mark.parametrize("M,wide", [(1280, True), (2560, False), (3584, True)])
+def test_gemm_tile_choice_full_k(M, wide):
+    """Between M = 1024 and 4096 (K = N = 4096, float32 output, so the gate
+    has no output-rounding allowance) the GEMM takes the tiling with fewer
+    weighted rounds over the compute units: 128 x 256 tiles at M = 1280 and
+    3584, 128 x 128 at M = 2560. Either way a rerun is bitwise equal and
+    sampled rows and columns meet the gate against the oracle."""
+    p = wl.make_problem(M, 4096, 4096, 128, 6, False, seed=2900 + M)
+    assert qg.plan(M, 4096, 4096, 128, 6)[:2] == (qg.PATH_GEMM, 1)
+    assert _wide_tiles(M, 4096) == wide, "the tiling choice changed for this shape"
+    d = Dev(p)
+    out = d.run()
+    out2 = d.run()
+    assert bitwise_equal(out, out2), "rerun not bitwise equal"
+    rows = sample_indices(M, 48, 3)
+    cols = sample_indices(4096, 256, 4)
+    ref, bound = oracle.for_problem(p, rows=rows, cols=cols)
+    check(to_f64(out)[np.ix_(rows, cols)], ref, bound, f"tile choice M={M} wide={wide}")
+
+
 # ---------------------------------------------------------------------------
 # the named workloads at full size, in the launch configuration of bench.py
 # (automatic plan); sampled outputs against the oracle
